@@ -1,0 +1,266 @@
+/*
+ * lwo.h - C ABI of the layerwise weight-offload library for one MI355X GPU.
+ *
+ * A diffusion transformer's blocks keep their weights in host memory, one
+ * flat extent per block, and are streamed into exactly two device slots by
+ * hipMemcpyAsync on a dedicated copy stream; the copy of block i+1 overlaps
+ * the forward of block i, and the last streamed block prefetches the first
+ * one again.  Sources (pages of the offloader documentation of a diffusion
+ * serving engine):
+ *   [LW]  "CPU Offloading for Diffusion Models", section "Layerwise
+ *         (Blockwise) Offloading / How It Works" and its execution-flow
+ *         table (prefetch next block on a copy stream, last block prefetches
+ *         block 0, flattened pinned host tensors).
+ *   [DLO] "Distributed Layerwise Offload": "Components and ownership",
+ *         "Startup and runtime sequence" (two shared device slots sized for
+ *         the largest streamed block, readiness events, prime the first
+ *         block), "Registered runtime-cache transfer" (page-align, coalesce,
+ *         budget check before mutation, read-only registration, all-or-
+ *         nothing rollback, unregister before unmap), "Failure and lifecycle
+ *         boundaries", "Feature compatibility" (resident leading layers,
+ *         per-tensor fp8 linears).
+ *   [ARCH] "CPU Offloading": "Shared lifecycle" (a failed enable leaves no
+ *         partial state) and "Cross-strategy invariants" (device storage is
+ *         not reused until dependent work completes).
+ *
+ * Conventions for every call:
+ *   - returns lwo_status; LWO_OK is 0; no C++ exception crosses the ABI;
+ *   - on failure nothing is left half-built, and lwo_last_error() returns a
+ *     thread-local message describing the last failure on this thread;
+ *   - pointers documented as "device" are HIP device pointers on the
+ *     store's device; "host" pointers are ordinary process memory;
+ *   - a store is used from one host thread at a time.
+ *
+ * Block layout (shared with the flat extents the caller may provide): every
+ * tensor starts at a multiple of 256 bytes, the extent is a multiple of 4096
+ * bytes, gaps are zero.  Weight matrices ("*.w", row-major [out, in]) are in
+ * the linear dtype; biases, norm gains and modulation tables in the
+ * activation dtype; with fp8 linears ten float32 per-tensor scales follow
+ * every other tensor, in weight-matrix order.  lwo_block_layout() lists the
+ * tensors and offsets.
+ *
+ * Block math (the workload's transformer block; LN is LayerNorm with eps
+ * 1e-6 and no affine, GELU is the tanh form):
+ *   DiT kind:   m = Lin_ada(SiLU(cond)) -> shift1 scale1 gate1 shift2 scale2 gate2
+ *               x += gate1 * Lin_o(Attn(Lin_qkv(LN(x)(1+scale1)+shift1)))
+ *               x += gate2 * Lin_fc2(GELU(Lin_fc1(LN(x)(1+scale2)+shift2)))
+ *   video kind: m = cond + M_block (same six chunks); q and k pass through
+ *               RMSNorm (eps 1e-6, gain) over the hidden width; after the
+ *               self-attention branch an ungated cross-attention branch
+ *               x += Lin_co(Attn(Lin_cq(LN(x)), Lin_ck(ctx), Lin_cv(ctx)));
+ *               then the FFN branch as above.
+ */
+#ifndef LWO_H
+#define LWO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lwo_status {
+    LWO_OK = 0,
+    LWO_EINVAL = 1,      /* bad argument, descriptor, alignment or size */
+    LWO_ENOMEM = 2,      /* host or device allocation failed */
+    LWO_EHIP = 3,        /* a HIP runtime call failed (message names it) */
+    LWO_EBUDGET = 4,     /* registration needs more than the budget; nothing was registered */
+    LWO_EREGISTER = 5,   /* a range failed to register; earlier ranges were rolled back */
+    LWO_EROLLBACK = 6,   /* a rollback unregister failed: the process must not unmap the range */
+    LWO_ESTATE = 7,      /* call not valid in the store's current state */
+    LWO_ECHECKSUM = 8    /* slot bytes differ from the host extent */
+} lwo_status;
+
+typedef enum lwo_dtype { LWO_F32 = 0, LWO_BF16 = 1, LWO_FP8_E4M3 = 2 } lwo_dtype;
+typedef enum lwo_block_kind { LWO_KIND_DIT = 0, LWO_KIND_VIDEO = 1 } lwo_block_kind;
+typedef enum lwo_host_mode { LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1 } lwo_host_mode;
+
+/* Shape of the block stack and of one denoise step's activations.
+ * Constraints (LWO_EINVAL otherwise): n_blocks >= 1; hidden = heads * head
+ * dim with head dim in {64, 72, 128}; batch, tokens >= 1; video kind needs
+ * ctx_tokens >= 1, DiT kind ctx_tokens = 0; act_dtype F32 or BF16;
+ * linear_dtype equal to act_dtype, or FP8_E4M3 with act BF16 and the video
+ * kind; hidden and ffn are multiples of 64 (of 128 with FP8 linears). */
+typedef struct lwo_model_desc {
+    int32_t kind;          /* lwo_block_kind */
+    int32_t n_blocks;
+    int32_t hidden;        /* D */
+    int32_t heads;         /* H */
+    int32_t ffn;           /* F */
+    int32_t batch;         /* B */
+    int32_t tokens;        /* T */
+    int32_t ctx_tokens;    /* Tc (video kind) */
+    int32_t act_dtype;     /* lwo_dtype */
+    int32_t linear_dtype;  /* lwo_dtype */
+} lwo_model_desc;
+
+typedef struct lwo_tensor_info {
+    char name[32];         /* e.g. "attn.q.w" */
+    uint64_t offset;       /* byte offset inside the block extent */
+    uint64_t bytes;
+    int32_t rank;          /* 1 or 2 */
+    int32_t shape[2];
+    int32_t dtype;         /* lwo_dtype */
+} lwo_tensor_info;
+
+/* Where build takes each block's flat extent from.
+ *   extents != NULL: extents[b] points to extent_bytes of host memory in the
+ *     layout above.  PIN_COPY reads them during the call only.  REGISTER
+ *     borrows them until destroy (they must be page-aligned, immutable and
+ *     stay mapped until lwo_destroy_block_store returns).
+ *   extents == NULL (PIN_COPY only): fill(user, b, dst, extent_bytes) is
+ *     called once per block, in order, to write block b's extent into the
+ *     store's pinned host memory dst (e.g. with lwo_pack_block); a non-zero
+ *     return aborts the build with LWO_EINVAL. */
+typedef struct lwo_block_source {
+    const void* const* extents;
+    int32_t (*fill)(void* user, int32_t block, void* dst, uint64_t extent_bytes);
+    void* user;
+} lwo_block_source;
+
+typedef struct lwo_stats {
+    uint64_t extent_bytes;       /* bytes of one block extent */
+    uint64_t slot_bytes;         /* bytes of each of the two device slots */
+    uint64_t device_weight_bytes;/* resident prefix + two slots */
+    uint64_t workspace_bytes;    /* activation workspace on the device */
+    uint64_t host_bytes;         /* pinned or registered host bytes */
+    uint64_t h2d_copies;         /* hipMemcpyAsync calls issued for blocks (total) */
+    uint64_t h2d_bytes;          /* bytes those copies moved (total) */
+    uint64_t steps;              /* denoise steps run */
+    uint64_t checksum_mismatches;/* validation mode: blocks whose slot checksum differed */
+    uint64_t registered_ranges;  /* REGISTER mode: coalesced ranges registered */
+    uint64_t registered_bytes;
+    int32_t resident_prefix;     /* k */
+    int32_t head_slot;           /* slot holding (or receiving) block k */
+    int32_t host_mode;           /* lwo_host_mode in effect */
+    int32_t validation;          /* 1 if per-block checksums run before each block */
+    double build_ms;             /* wall time of lwo_build_block_store */
+} lwo_stats;
+
+/* --- layout and packing (host only, no GPU needed) ---------------------- */
+
+/* Tensor table of one block for desc: writes up to cap entries to out (out
+ * may be NULL with cap 0 to query), the count to *n and the extent size to
+ * *extent_bytes.  LWO_EINVAL if cap is too small (count is still written).
+ * Source: [LW] flattened per-block host tensors; [DLO] "Registered
+ * runtime-cache transfer" (each tensor at an offset of one flat buffer). */
+lwo_status lwo_block_layout(const lwo_model_desc* desc, lwo_tensor_info* out, int32_t cap,
+                            int32_t* n, uint64_t* extent_bytes);
+
+/* Flatten one block: tensors[i] (host, float32, row-major, in the order of
+ * lwo_block_layout, excluding the fp8 scale table) are converted to their
+ * stored dtype and written at their offsets in dst (host, dst_bytes >=
+ * extent_bytes); padding is zeroed.  bf16 rounds to nearest-even; fp8 uses
+ * one scale per tensor, s = amax|w| / 448 (1 for an all-zero tensor), codes
+ * = e4m3(w / s) rounded to nearest-even and saturated, and the scales go to
+ * "linear.scales".  Source: [DLO] "Feature compatibility" (per-tensor fp8
+ * linears finalised before offload); [LW] flattened tensors. */
+lwo_status lwo_pack_block(const lwo_model_desc* desc, const float* const* tensors, int32_t n_tensors,
+                          void* dst, uint64_t dst_bytes);
+
+/* Position-weighted SplitMix64 sum over a host buffer (bytes % 8 == 0):
+ * sum_i SplitMix64(w_i ^ (i * 0x9E3779B97F4A7C15)) mod 2^64 over the
+ * little-endian 64-bit words w_i.  The device computes the same sum over a
+ * slot.  Writes *sum. */
+lwo_status lwo_extent_checksum(const void* host, uint64_t bytes, uint64_t* sum);
+
+/* --- registration lifecycle (host only; the callbacks make it testable) -- */
+
+typedef int32_t (*lwo_register_fn)(void* user, void* base, uint64_t bytes);   /* 0 = success */
+typedef int32_t (*lwo_unregister_fn)(void* user, void* base);                /* 0 = success */
+
+/* [DLO] "Registered runtime-cache transfer" and "Failure and lifecycle
+ * boundaries": page-align each [ptr, ptr+bytes) outward to `page`, coalesce
+ * overlapping or adjacent ranges, check the total against budget before
+ * calling reg at all (LWO_EBUDGET, no calls), then call reg on each range in
+ * address order.  If reg fails on a range, every range already registered is
+ * passed to unreg in reverse order and LWO_EREGISTER is returned; if an
+ * unreg fails during that rollback, LWO_EROLLBACK is returned and the
+ * remaining ranges stay registered (the caller must not unmap them).  On
+ * success the coalesced ranges are written to out_base/out_len (cap
+ * entries; LWO_EINVAL before any reg call if cap is too small) and their
+ * count to *n_out. */
+lwo_status lwo_register_ranges(const void* const* ptrs, const uint64_t* bytes, int32_t n, uint64_t page,
+                               uint64_t budget, lwo_register_fn reg, lwo_unregister_fn unreg, void* user,
+                               uint64_t* out_base, uint64_t* out_len, int32_t cap, int32_t* n_out);
+
+/* --- the store ----------------------------------------------------------- */
+
+typedef struct lwo_store lwo_store;   /* opaque */
+
+/* [LW], [DLO] "Startup and runtime sequence": set up the host weight store
+ * (PIN_COPY: one hipHostMalloc extent per block filled from src; REGISTER:
+ * the caller's extents registered read-only through lwo_register_ranges with
+ * hipHostRegister, all-or-nothing within register_budget bytes), the device
+ * arena (two slots of extent_bytes; no resident prefix), the activation
+ * workspace, a non-blocking copy stream at default priority and the
+ * readiness events, then prime block 0 into slot 0.  On `device` (HIP
+ * ordinal).  On any failure everything allocated so far is released and
+ * *out is NULL. */
+lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src,
+                                 int32_t host_mode, uint64_t register_budget, int32_t device,
+                                 lwo_store** out);
+
+/* [DLO] "Feature compatibility" (resident leading layers): keep blocks
+ * 0..k-1 in a device-resident region and stream blocks k..n_blocks-1
+ * through the two slots (0 <= k <= n_blocks; k = n_blocks streams nothing).
+ * Synchronises the store's streams, reallocates the resident region, copies
+ * the prefix and primes block k into slot 0.  The two slots stay allocated.
+ * On failure the previous prefix stays in effect. */
+lwo_status lwo_set_resident_prefix(lwo_store* store, int32_t k);
+
+/* One denoise step over every block, enqueued on hip_stream (a non-null
+ * hipStream_t of the store's device) and returned without waiting:
+ *   x    device, [batch, tokens, hidden] in act_dtype, updated in place;
+ *   cond device, DiT kind [batch, hidden], video kind [batch, 6, hidden],
+ *        act_dtype;
+ *   ctx  device, [batch, ctx_tokens, hidden] act_dtype (video kind), NULL
+ *        for the DiT kind.
+ * Blocks run in order: the resident prefix, then the ring over blocks
+ * k..n-1 where, for each streamed block j, the compute stream waits for
+ * slot(j)'s copy event, the copy stream waits until the other slot's last
+ * block has finished computing and then copies the next block (j+1, or k
+ * after the last) into it ([LW] execution-flow table; [DLO] readiness
+ * events; [ARCH] no reuse before dependent work completes).  With a single
+ * streamed block it stays in its slot and nothing is copied.  The last
+ * prefetch stays in flight across calls.  Caller keeps x, cond, ctx valid
+ * until the stream drains.  Device faults surface as LWO_EHIP at a later
+ * synchronising call. */
+lwo_status lwo_run_denoise_step(lwo_store* store, void* x, const void* cond, const void* ctx,
+                                void* hip_stream);
+
+/* Validation mode (on != 0): before each streamed block the compute stream
+ * checksums the slot on the device and compares it with the host extent's
+ * sum taken at build; mismatches are counted in lwo_stats. */
+lwo_status lwo_set_validation(lwo_store* store, int32_t on);
+
+/* Synchronise, copy block `block` into a slot (or use its resident copy),
+ * checksum it on the device and compare with the host extent's checksum.
+ * Writes both sums; LWO_ECHECKSUM if they differ.  Leaves the ring primed
+ * as it was. */
+lwo_status lwo_block_checksum(lwo_store* store, int32_t block, uint64_t* host_sum, uint64_t* slot_sum);
+
+/* Per-copy timing: when on, every block copy is bracketed by timing events on
+ * the copy stream; lwo_copy_times returns the durations (ms) of the copies
+ * issued by the most recent step (after synchronising), up to cap, count in
+ * *n. */
+lwo_status lwo_set_copy_timing(lwo_store* store, int32_t on);
+lwo_status lwo_copy_times(lwo_store* store, float* ms, int32_t cap, int32_t* n);
+
+/* Synchronise the store's copy stream and snapshot its counters. */
+lwo_status lwo_get_stats(lwo_store* store, lwo_stats* out);
+
+/* [DLO] "Failure and lifecycle boundaries": synchronise outstanding device
+ * work, unregister host ranges (REGISTER mode), free pinned host memory, the
+ * arena, workspace, events and copy stream.  NULL is a no-op.  In REGISTER
+ * mode the caller may unmap its extents once this returns. */
+lwo_status lwo_destroy_block_store(lwo_store* store);
+
+/* Thread-local description of the last failure ("" if none). */
+const char* lwo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LWO_H */

@@ -1,0 +1,17 @@
+"""Layerwise weight offload for a DiT block stack on one MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/lwo.h`` (``liblwo.so``,
+built in-tree by ``layerwise_weight_offload_amd.build``).  Every function
+here only marshals arguments; all work runs in the library's C++ host code
+and HIP kernels.  Device buffers and streams are passed as raw integers
+(``tensor.data_ptr()``, ``stream.cuda_stream``), so the binding itself does
+not depend on PyTorch.
+
+Importing fails loudly if the library has not been built: there is no
+fallback implementation.
+"""
+from ._binding import (  # noqa: F401
+    BF16, F32, FP8_E4M3, HOST_PIN_COPY, HOST_REGISTER, KIND_DIT, KIND_VIDEO, LIB_PATH,
+    LwoError, ModelDesc, Stats, Store, block_layout, build_block_store, extent_checksum, last_error,
+    pack_block, register_ranges, exported_symbols,
+)

@@ -1,0 +1,303 @@
+"""ctypes marshalling for liblwo.so (see include/lwo.h for every contract)."""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblwo.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m layerwise_weight_offload_amd.build "
+                      f"or __graft_entry__.build()); there is no fallback implementation")
+
+_lib = C.CDLL(LIB_PATH)
+
+# enums (include/lwo.h)
+F32, BF16, FP8_E4M3 = 0, 1, 2
+KIND_DIT, KIND_VIDEO = 0, 1
+HOST_PIN_COPY, HOST_REGISTER = 0, 1
+STATUS = {0: "LWO_OK", 1: "LWO_EINVAL", 2: "LWO_ENOMEM", 3: "LWO_EHIP", 4: "LWO_EBUDGET",
+          5: "LWO_EREGISTER", 6: "LWO_EROLLBACK", 7: "LWO_ESTATE", 8: "LWO_ECHECKSUM"}
+
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+
+
+class LwoError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class _Desc(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("kind", "n_blocks", "hidden", "heads", "ffn", "batch", "tokens",
+                                         "ctx_tokens", "act_dtype", "linear_dtype")]
+
+
+class _TensorInfo(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("offset", C.c_uint64), ("bytes", C.c_uint64), ("rank", C.c_int32),
+                ("shape", C.c_int32 * 2), ("dtype", C.c_int32)]
+
+
+_FILL = C.CFUNCTYPE(C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_uint64)
+_REG = C.CFUNCTYPE(C.c_int32, C.c_void_p, C.c_void_p, C.c_uint64)
+_UNREG = C.CFUNCTYPE(C.c_int32, C.c_void_p, C.c_void_p)
+
+
+class _Source(C.Structure):
+    _fields_ = [("extents", C.POINTER(C.c_void_p)), ("fill", _FILL), ("user", C.c_void_p)]
+
+
+class _Stats(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in ("extent_bytes", "slot_bytes", "device_weight_bytes", "workspace_bytes",
+                                          "host_bytes", "h2d_copies", "h2d_bytes", "steps", "checksum_mismatches",
+                                          "registered_ranges", "registered_bytes")] + \
+               [(n, C.c_int32) for n in ("resident_prefix", "head_slot", "host_mode", "validation")] + \
+               [("build_ms", C.c_double)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_P = C.c_void_p
+_lib_block_layout = _sig("lwo_block_layout", C.c_int, C.POINTER(_Desc), C.POINTER(_TensorInfo), C.c_int32,
+                         C.POINTER(C.c_int32), C.POINTER(C.c_uint64))
+_lib_pack_block = _sig("lwo_pack_block", C.c_int, C.POINTER(_Desc), C.POINTER(C.c_void_p), C.c_int32, _P, C.c_uint64)
+_lib_extent_checksum = _sig("lwo_extent_checksum", C.c_int, _P, C.c_uint64, C.POINTER(C.c_uint64))
+_lib_register_ranges = _sig("lwo_register_ranges", C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_uint64), C.c_int32,
+                            C.c_uint64, C.c_uint64, _REG, _UNREG, _P, C.POINTER(C.c_uint64),
+                            C.POINTER(C.c_uint64), C.c_int32, C.POINTER(C.c_int32))
+_lib_build = _sig("lwo_build_block_store", C.c_int, C.POINTER(_Desc), C.POINTER(_Source), C.c_int32, C.c_uint64,
+                  C.c_int32, C.POINTER(_P))
+_lib_set_prefix = _sig("lwo_set_resident_prefix", C.c_int, _P, C.c_int32)
+_lib_run = _sig("lwo_run_denoise_step", C.c_int, _P, _P, _P, _P, _P)
+_lib_set_validation = _sig("lwo_set_validation", C.c_int, _P, C.c_int32)
+_lib_block_checksum = _sig("lwo_block_checksum", C.c_int, _P, C.c_int32, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64))
+_lib_set_copy_timing = _sig("lwo_set_copy_timing", C.c_int, _P, C.c_int32)
+_lib_copy_times = _sig("lwo_copy_times", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32))
+_lib_get_stats = _sig("lwo_get_stats", C.c_int, _P, C.POINTER(_Stats))
+_lib_destroy = _sig("lwo_destroy_block_store", C.c_int, _P)
+_lib_last_error = _sig("lwo_last_error", C.c_char_p)
+
+EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
+            "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_validation",
+            "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_get_stats",
+            "lwo_destroy_block_store", "lwo_last_error"]
+
+
+def exported_symbols() -> list[str]:
+    return list(EXPORTED)
+
+
+def last_error() -> str:
+    return (_lib_last_error() or b"").decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LwoError(status, last_error())
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelDesc:
+    kind: int
+    n_blocks: int
+    hidden: int
+    heads: int
+    ffn: int
+    batch: int
+    tokens: int
+    ctx_tokens: int
+    act_dtype: int
+    linear_dtype: int
+
+    @classmethod
+    def from_workload(cls, w) -> "ModelDesc":
+        """From any object with the lwo_synth.Workload fields."""
+        return cls(KIND_DIT if w.kind == "dit" else KIND_VIDEO, w.n_blocks, w.hidden, w.heads, w.ffn, w.batch,
+                   w.tokens, w.ctx_tokens, DTYPES[w.act_dtype], DTYPES[w.linear_dtype])
+
+    def _c(self) -> _Desc:
+        return _Desc(*dataclasses.astuple(self))
+
+
+def block_layout(desc: ModelDesc):
+    """([dict(name, offset, bytes, shape, dtype)], extent_bytes)."""
+    d = desc._c()
+    n = C.c_int32()
+    ext = C.c_uint64()
+    _check(_lib_block_layout(C.byref(d), None, 0, C.byref(n), C.byref(ext)))
+    arr = (_TensorInfo * n.value)()
+    _check(_lib_block_layout(C.byref(d), arr, n.value, C.byref(n), C.byref(ext)))
+    out = [dict(name=t.name.decode(), offset=t.offset, bytes=t.bytes, shape=tuple(t.shape[:t.rank]), dtype=t.dtype)
+           for t in arr]
+    return out, ext.value
+
+
+def pack_block(desc: ModelDesc, tensors, dst=None, dst_bytes: int | None = None):
+    """Flatten float32 tensors into one extent.  dst: a writable buffer, or an
+    integer address of dst_bytes writable bytes; returns a new uint8 array if
+    dst is None."""
+    _, ext = block_layout(desc)
+    arrs = [np.ascontiguousarray(t, dtype=np.float32) for t in tensors]
+    ptrs = (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    out = None
+    if dst is None:
+        out = np.empty(ext, dtype=np.uint8)
+        addr, cap = out.ctypes.data, ext
+    elif isinstance(dst, int):
+        if dst_bytes is None:
+            raise ValueError("dst_bytes is required with an address")
+        addr, cap = dst, dst_bytes
+    else:
+        view = np.frombuffer(dst, dtype=np.uint8)
+        addr, cap = view.ctypes.data, view.size
+    _check(_lib_pack_block(C.byref(desc._c()), ptrs, len(arrs), C.c_void_p(addr), cap))
+    return out
+
+
+def extent_checksum(buf) -> int:
+    a = np.frombuffer(buf, dtype=np.uint8)
+    s = C.c_uint64()
+    _check(_lib_extent_checksum(C.c_void_p(a.ctypes.data), a.size, C.byref(s)))
+    return s.value
+
+
+def register_ranges(ptrs, sizes, page, budget, reg, unreg, cap=64):
+    """Drive the registration lifecycle with Python callbacks reg(base, len) ->
+    int and unreg(base) -> int (0 = success).  Returns [(base, len)]."""
+    n = len(ptrs)
+    P = (C.c_void_p * max(n, 1))(*ptrs)
+    S = (C.c_uint64 * max(n, 1))(*sizes)
+    rcb = _REG(lambda user, base, ln: int(reg(int(base or 0), int(ln))))
+    ucb = _UNREG(lambda user, base: int(unreg(int(base or 0))))
+    ob = (C.c_uint64 * cap)()
+    ol = (C.c_uint64 * cap)()
+    nout = C.c_int32()
+    _check(_lib_register_ranges(P, S, n, page, budget, rcb, ucb, None, ob, ol, cap, C.byref(nout)))
+    return [(ob[i], ol[i]) for i in range(nout.value)]
+
+
+@dataclasses.dataclass
+class Stats:
+    extent_bytes: int
+    slot_bytes: int
+    device_weight_bytes: int
+    workspace_bytes: int
+    host_bytes: int
+    h2d_copies: int
+    h2d_bytes: int
+    steps: int
+    checksum_mismatches: int
+    registered_ranges: int
+    registered_bytes: int
+    resident_prefix: int
+    head_slot: int
+    host_mode: int
+    validation: int
+    build_ms: float
+
+
+class Store:
+    """Owner of one lwo_store handle (destroy() or context-manager exit frees it)."""
+
+    def __init__(self, handle, desc: ModelDesc, keepalive=None):
+        self._h = handle
+        self.desc = desc
+        self._keep = keepalive
+
+    @property
+    def handle(self) -> int:
+        return self._h.value or 0
+
+    def _live(self):
+        if not self._h:
+            raise LwoError(7, "store already destroyed")
+        return self._h
+
+    def set_resident_prefix(self, k: int) -> None:
+        _check(_lib_set_prefix(self._live(), k))
+
+    def run_denoise_step(self, x: int, cond: int, ctx: int | None, stream: int) -> None:
+        """x, cond, ctx: device addresses; stream: hipStream_t as an integer."""
+        _check(_lib_run(self._live(), C.c_void_p(x), C.c_void_p(cond), C.c_void_p(ctx) if ctx else None,
+                        C.c_void_p(stream)))
+
+    def set_validation(self, on: bool) -> None:
+        _check(_lib_set_validation(self._live(), 1 if on else 0))
+
+    def block_checksum(self, block: int):
+        hs, ss = C.c_uint64(), C.c_uint64()
+        st = _lib_block_checksum(self._live(), block, C.byref(hs), C.byref(ss))
+        if st not in (0, 8):
+            _check(st)
+        return hs.value, ss.value
+
+    def set_copy_timing(self, on: bool) -> None:
+        _check(_lib_set_copy_timing(self._live(), 1 if on else 0))
+
+    def copy_times(self, cap: int = 4096) -> list[float]:
+        buf = (C.c_float * cap)()
+        n = C.c_int32()
+        _check(_lib_copy_times(self._live(), buf, cap, C.byref(n)))
+        return [buf[i] for i in range(min(n.value, cap))]
+
+    def stats(self) -> Stats:
+        s = _Stats()
+        _check(_lib_get_stats(self._live(), C.byref(s)))
+        return Stats(*[getattr(s, f[0]) for f in _Stats._fields_])
+
+    def destroy(self) -> None:
+        if self._h:
+            _check(_lib_destroy(self._h))
+            self._h = None
+            self._keep = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,
+                      register_budget: int = 0, device: int = 0) -> Store:
+    """extents: list of host buffers/addresses (one per block), or fill(b, dst_addr, nbytes) -> None
+    writing block b's flat extent into the store's pinned memory."""
+    src = _Source()
+    keep = []
+    if extents is not None:
+        addrs = [e if isinstance(e, int) else np.frombuffer(e, dtype=np.uint8).ctypes.data for e in extents]
+        arr = (C.c_void_p * len(addrs))(*addrs)
+        keep.append((arr, extents))
+        src.extents = C.cast(arr, C.POINTER(C.c_void_p))
+        src.fill = _FILL()
+    else:
+        def _fill(user, b, dst, nbytes):
+            try:
+                fill(int(b), int(dst), int(nbytes))
+                return 0
+            except Exception as e:   # reported through the library's status
+                import traceback
+                traceback.print_exc()
+                return 1
+        cb = _FILL(_fill)
+        keep.append(cb)
+        src.extents = C.POINTER(C.c_void_p)()
+        src.fill = cb
+    h = C.c_void_p()
+    _check(_lib_build(C.byref(desc._c()), C.byref(src), host_mode, register_budget, device, C.byref(h)))
+    return Store(h, desc, keepalive=keep if host_mode == HOST_REGISTER else None)

@@ -1,0 +1,211 @@
+// One DiT block's forward as a sequence of kernel launches on the compute
+// stream, reading weights through zero-copy views into a slot (or the
+// resident region): every parameter is `slot base + layout offset`, so the
+// weights are never repacked on the device ("Distributed Layerwise Offload",
+// "Registered runtime-cache transfer": parameters are views at offsets of one
+// flat device buffer).
+//
+// The residual stream stays in fp32 for the whole step; LayerNorm outputs,
+// projections and attention outputs are in the activation dtype (or e4m3
+// codes with per-row scales when the linears are fp8).
+#include <algorithm>
+
+#include "kernels.h"
+#include "lwo_internal.h"
+
+namespace lwo {
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
+    const size_t M = (size_t)d.batch * d.tokens, D = d.hidden, F = d.ffn;
+    const size_t Mc = (size_t)d.batch * d.ctx_tokens;
+    const size_t ae = dtype_bytes(d.act_dtype);
+    const bool video = d.kind == LWO_KIND_VIDEO, fp8 = d.linear_dtype == LWO_FP8_E4M3;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t o_xr = take(M * D * 4), o_mod = take((size_t)d.batch * 6 * D * 4), o_h = take(M * D * ae);
+    const size_t o_big = take(M * std::max(3 * D, F) * ae), o_attn = take(M * D * ae);
+    const size_t o_cq = video ? take(M * D * ae) : 0, o_ckv = video ? take(Mc * 2 * D * ae) : 0;
+    const size_t o_q8 = fp8 ? take(M * std::max(D, F)) : 0, o_q8s = fp8 ? take(std::max(M, Mc) * 4) : 0;
+    const size_t o_c8 = fp8 ? take(Mc * D) : 0, o_c8s = fp8 ? take(Mc * 4) : 0;
+    const size_t o_sums = take(16);
+    void* base = nullptr;
+    if (hipMalloc(&base, off) != hipSuccess) {
+        set_error("hipMalloc of the activation workspace (" + std::to_string(off) + " bytes) failed");
+        return LWO_ENOMEM;
+    }
+    char* b = (char*)base;
+    ws->base = base;
+    ws->bytes = off;
+    ws->xr = (float*)(b + o_xr);
+    ws->mod = (float*)(b + o_mod);
+    ws->h = b + o_h;
+    ws->big = b + o_big;
+    ws->attn = b + o_attn;
+    ws->cq = video ? b + o_cq : nullptr;
+    ws->ckv = video ? b + o_ckv : nullptr;
+    ws->q8 = fp8 ? (uint8_t*)(b + o_q8) : nullptr;
+    ws->q8_scale = fp8 ? (float*)(b + o_q8s) : nullptr;
+    ws->ctx8 = fp8 ? (uint8_t*)(b + o_c8) : nullptr;
+    ws->ctx8_scale = fp8 ? (float*)(b + o_c8s) : nullptr;
+    ws->sums = (uint64_t*)(b + o_sums);
+    LWO_HIP_TRY(hipMemset(ws->sums, 0, 16));
+    return LWO_OK;
+}
+
+void workspace_free(Workspace* ws) {
+    if (ws->base) (void)hipFree(ws->base);
+    *ws = Workspace();
+}
+
+#define LWO_LAUNCH(expr)                                                                  \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess) {                                                           \
+            set_error(std::string("kernel launch failed: ") + #expr + ": " + hipGetErrorString(e_)); \
+            return LWO_EHIP;                                                              \
+        }                                                                                 \
+    } while (0)
+
+lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* ctx,
+                              hipStream_t st) {
+    const size_t n = (size_t)d.batch * d.tokens * d.hidden;
+    LWO_LAUNCH(launch_to_f32(x, d.act_dtype, ws.xr, n, st));
+    if (d.linear_dtype == LWO_FP8_E4M3)   // the context feeds the cross K/V linears of every block: quantise once
+        LWO_LAUNCH(launch_quant_rows(ctx, d.batch * d.ctx_tokens, d.hidden, ws.ctx8, ws.ctx8_scale, st));
+    return LWO_OK;
+}
+
+lwo_status enqueue_step_end(const lwo_model_desc& d, const Workspace& ws, void* x, hipStream_t st) {
+    const size_t n = (size_t)d.batch * d.tokens * d.hidden;
+    LWO_LAUNCH(launch_from_f32(ws.xr, x, d.act_dtype, n, st));
+    return LWO_OK;
+}
+
+static GemmArgs gemm_args(const lwo_model_desc& d, const void* a, const void* w, int M, int N, int K, int epi,
+                          const void* bias) {
+    GemmArgs g{};
+    g.a = a; g.w = w; g.M = M; g.N = N; g.K = K;
+    g.dtype = d.linear_dtype;
+    g.act_dtype = d.act_dtype;
+    g.epi = epi;
+    g.bias = bias;
+    g.rows_per_batch = d.tokens;
+    return g;
+}
+
+lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Workspace& ws, const void* cond,
+                         const void* ctx, hipStream_t st) {
+    const int B = d.batch, T = d.tokens, D = d.hidden, F = d.ffn, H = d.heads, dh = D / H;
+    const int M = B * T, Mc = B * d.ctx_tokens;
+    const int act = d.act_dtype, ae = dtype_bytes(act);
+    const bool fp8 = d.linear_dtype == LWO_FP8_E4M3;
+    const int h_dt = fp8 ? LWO_FP8_E4M3 : act;      // LayerNorm output dtype feeding a linear
+    void* h_buf = fp8 ? (void*)ws.q8 : ws.h;
+    char* big = (char*)ws.big;
+    const float* mod = ws.mod;
+    const float* wsc = p.w_scale;
+
+    // fp8: one weight scale per tensor.  The fused QKV (and cross K|V) GEMMs
+    // span several tensors, one per D output columns; the others span one.
+    auto fp8_in = [&](GemmArgs& g, int scale_idx, const float* a_scale, bool fused) {
+        if (!fp8) return;
+        g.w_scale = wsc + scale_idx;
+        g.w_seg = fused ? D : g.N;
+        g.a_scale = a_scale;
+    };
+    auto attn = [&](const void* q, int ldq, const void* k, const void* v, int ldkv, int Tk) {
+        AttnArgs a{};
+        a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldkv; a.v = v; a.ldv = ldkv;
+        a.o = ws.attn; a.ldo = D;
+        a.B = B; a.H = H; a.Tq = T; a.Tk = Tk; a.dh = dh; a.dtype = act;
+        return launch_attention(a, st);
+    };
+
+    if (d.kind == LWO_KIND_DIT) {
+        LWO_LAUNCH(launch_mod_dit(cond, p.ada_w, p.ada_b, act, ws.mod, B, D, st));
+        LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 0, 1, ws.h, act, nullptr, st));
+        GemmArgs g = gemm_args(d, ws.h, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
+        g.out = big; g.ldo = 3 * D;
+        LWO_LAUNCH(launch_gemm(g, st));
+        LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
+        g = gemm_args(d, ws.attn, p.o_w, M, D, D, EPI_GATED, p.o_b);
+        g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
+        LWO_LAUNCH(launch_gemm(g, st));
+        LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 3, 4, ws.h, act, nullptr, st));
+        g = gemm_args(d, ws.h, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
+        g.out = big; g.ldo = F;
+        LWO_LAUNCH(launch_gemm(g, st));
+        g = gemm_args(d, big, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
+        g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
+        LWO_LAUNCH(launch_gemm(g, st));
+        return LWO_OK;
+    }
+
+    // video kind
+    LWO_LAUNCH(launch_mod_video(cond, p.mod_table, act, ws.mod, B, D, st));
+    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 0, 1, h_buf, h_dt, ws.q8_scale, st));
+    GemmArgs g = gemm_args(d, h_buf, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
+    g.out = big; g.ldo = 3 * D;
+    fp8_in(g, 0, ws.q8_scale, true);
+    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(launch_rmsnorm_qk(big, act, M, D, p.q_norm, p.k_norm, st));
+    LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
+    const void* a_in = ws.attn;
+    if (fp8) { LWO_LAUNCH(launch_quant_rows(ws.attn, M, D, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    g = gemm_args(d, a_in, p.o_w, M, D, D, EPI_GATED, p.o_b);
+    g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
+    fp8_in(g, 3, ws.q8_scale, false);
+    LWO_LAUNCH(launch_gemm(g, st));
+
+    // cross-attention: ungated, plain LayerNorm on the queries, keys/values from the context
+    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, nullptr, 0, 0, h_buf, h_dt, ws.q8_scale, st));
+    g = gemm_args(d, h_buf, p.cq_w, M, D, D, EPI_STORE, p.cq_b);
+    g.out = ws.cq; g.ldo = D;
+    fp8_in(g, 4, ws.q8_scale, false);
+    LWO_LAUNCH(launch_gemm(g, st));
+    g = gemm_args(d, fp8 ? (const void*)ws.ctx8 : ctx, p.ck_w, Mc, 2 * D, D, EPI_STORE, p.ckv_b);
+    g.out = ws.ckv; g.ldo = 2 * D;
+    fp8_in(g, 5, ws.ctx8_scale, true);
+    LWO_LAUNCH(launch_gemm(g, st));
+    const char* ckv = (const char*)ws.ckv;
+    LWO_LAUNCH(attn(ws.cq, D, ckv, ckv + (size_t)D * ae, 2 * D, d.ctx_tokens));
+    a_in = ws.attn;
+    if (fp8) { LWO_LAUNCH(launch_quant_rows(ws.attn, M, D, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    g = gemm_args(d, a_in, p.co_w, M, D, D, EPI_RESID, p.co_b);
+    g.xr = ws.xr; g.ldx = D;
+    fp8_in(g, 7, ws.q8_scale, false);
+    LWO_LAUNCH(launch_gemm(g, st));
+
+    // FFN
+    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 3, 4, h_buf, h_dt, ws.q8_scale, st));
+    g = gemm_args(d, h_buf, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
+    g.out = big; g.ldo = F;
+    fp8_in(g, 8, ws.q8_scale, false);
+    LWO_LAUNCH(launch_gemm(g, st));
+    a_in = big;
+    if (fp8) { LWO_LAUNCH(launch_quant_rows(big, M, F, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    g = gemm_args(d, a_in, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
+    g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
+    fp8_in(g, 9, ws.q8_scale, false);
+    LWO_LAUNCH(launch_gemm(g, st));
+    return LWO_OK;
+}
+
+lwo_status enqueue_checksum(const void* dev, uint64_t bytes, uint64_t* acc, hipStream_t st) {
+    LWO_LAUNCH(launch_checksum(dev, bytes, acc, st));
+    return LWO_OK;
+}
+
+lwo_status enqueue_checksum_compare(uint64_t* acc, uint64_t expect, hipStream_t st) {
+    LWO_LAUNCH(launch_checksum_compare(acc, expect, st));
+    return LWO_OK;
+}
+
+lwo_status enqueue_zero_u64(uint64_t* p, int n, hipStream_t st) {
+    LWO_LAUNCH(launch_zero_u64(p, n, st));
+    return LWO_OK;
+}
+
+}  // namespace lwo

@@ -1,0 +1,333 @@
+// Row-wise and elementwise kernels of the DiT block (HBM-bound): residual
+// conversion, adaLN modulation, LayerNorm (+ modulation, + fp8 row
+// quantisation), q/k RMSNorm, fp8 row quantisation and the slot checksum.
+//
+// Every row kernel gives one 64-lane wavefront to one row and keeps the row
+// in registers, so LayerNorm takes its mean and variance in two exact
+// passes without re-reading HBM; 4 wavefronts share a 256-thread workgroup.
+#include "../../include/lwo.h"
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace lwo {
+
+__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const bf16* p) {
+    bf16x4 v = *(const bf16x4*)p;
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+__device__ __forceinline__ void store4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void store4(bf16* p, float4 v) {
+    bf16x4 o;
+    o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+    *(bf16x4*)p = o;
+}
+
+// ------------------------------------------------------------------ residual conversion
+
+template <typename T>
+__global__ void k_to_f32(const T* __restrict__ x, float* __restrict__ xr, size_t n4) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i < n4; i += (size_t)gridDim.x * blockDim.x) store4(xr + 4 * i, load4(x + 4 * i));
+}
+
+template <typename T>
+__global__ void k_from_f32(const float* __restrict__ xr, T* __restrict__ x, size_t n4) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i < n4; i += (size_t)gridDim.x * blockDim.x) store4(x + 4 * i, load4(xr + 4 * i));
+}
+
+static int grid_for(size_t n, int per_block) {
+    size_t g = (n + per_block - 1) / per_block;
+    return (int)(g < 8192 ? (g ? g : 1) : 8192);
+}
+
+hipError_t launch_to_f32(const void* x, int dt, float* xr, size_t n, hipStream_t st) {
+    size_t n4 = n / 4;
+    if (dt == LWO_F32) k_to_f32<float><<<grid_for(n4, 256), 256, 0, st>>>((const float*)x, xr, n4);
+    else k_to_f32<bf16><<<grid_for(n4, 256), 256, 0, st>>>((const bf16*)x, xr, n4);
+    return hipGetLastError();
+}
+
+hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream_t st) {
+    size_t n4 = n / 4;
+    if (dt == LWO_F32) k_from_f32<float><<<grid_for(n4, 256), 256, 0, st>>>(xr, (float*)x, n4);
+    else k_from_f32<bf16><<<grid_for(n4, 256), 256, 0, st>>>(xr, (bf16*)x, n4);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ adaLN modulation
+
+// DiT kind: mod[b, n] = sum_k SiLU(cond[b, k]) W[n, k] + bias[n], n < 6D (one wavefront per n).
+template <typename T>
+__global__ __launch_bounds__(256) void k_mod_dit(const T* __restrict__ cond, const T* __restrict__ w,
+                                                 const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
+    const int n = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (n >= 6 * D) return;
+    const T* wr = w + (size_t)n * D;
+    for (int b = 0; b < B; ++b) {
+        const T* c = cond + (size_t)b * D;
+        float s = 0.0f;
+        for (int k = 4 * lane; k < D; k += 4 * kWave) {
+            float4 wv = load4(wr + k), cv = load4(c + k);
+            s += silu(cv.x) * wv.x + silu(cv.y) * wv.y + silu(cv.z) * wv.z + silu(cv.w) * wv.w;
+        }
+        s = wave_sum(s);
+        if (lane == 0) mod[(size_t)b * 6 * D + n] = s + to_f(bias[n]);
+    }
+}
+
+// Video kind: mod[b, i, d] = cond[b, i, d] + table[i, d].
+template <typename T>
+__global__ void k_mod_video(const T* __restrict__ cond, const T* __restrict__ table, float* __restrict__ mod,
+                            int B, int D) {
+    const int n = 6 * D;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * n; i += gridDim.x * blockDim.x)
+        mod[i] = to_f(cond[i]) + to_f(table[i % n]);
+}
+
+hipError_t launch_mod_dit(const void* cond, const void* w, const void* b, int dt, float* mod, int B, int D,
+                          hipStream_t st) {
+    dim3 grid((6 * D + 3) / 4);
+    if (dt == LWO_F32) k_mod_dit<float><<<grid, 256, 0, st>>>((const float*)cond, (const float*)w, (const float*)b, mod, B, D);
+    else k_mod_dit<bf16><<<grid, 256, 0, st>>>((const bf16*)cond, (const bf16*)w, (const bf16*)b, mod, B, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* mod, int B, int D, hipStream_t st) {
+    int g = grid_for((size_t)B * 6 * D, 256);
+    if (dt == LWO_F32) k_mod_video<float><<<g, 256, 0, st>>>((const float*)cond, (const float*)table, mod, B, D);
+    else k_mod_video<bf16><<<g, 256, 0, st>>>((const bf16*)cond, (const bf16*)table, mod, B, D);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ LayerNorm (+ modulation, + fp8)
+
+// OUT: 0 float, 1 bf16, 2 fp8 codes + row scale.  NV4 = float4 chunks per lane (>= D / 256).
+template <int OUT, bool MOD, int NV4>
+__global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M, int D, int T,
+                                            const float* __restrict__ mod, int shc, int scc,
+                                            void* __restrict__ out, float* __restrict__ out_scale) {
+    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (row >= M) return;
+    const int n4 = D / 4;
+    const float* x = xr + (size_t)row * D;
+    float4 v[NV4];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int c = lane + kWave * i;
+        v[i] = c < n4 ? load4(x + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(s) / (float)D;
+    float s2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n4) {
+            float a = v[i].x - mean, b = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
+            s2 += (a * a + b * b) + (cc * cc + d * d);
+        }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)D + 1e-6f);
+    const int bi = row / T;
+    const float* shift = MOD ? mod + ((size_t)bi * 6 + shc) * D : nullptr;
+    const float* scale = MOD ? mod + ((size_t)bi * 6 + scc) * D : nullptr;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int c = lane + kWave * i;
+        float4 y = make_float4((v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd,
+                               (v[i].w - mean) * rstd);
+        if (MOD && c < n4) {
+            const float4 sc = load4(scale + 4 * c), sh = load4(shift + 4 * c);
+            y.x = y.x * (1.0f + sc.x) + sh.x;
+            y.y = y.y * (1.0f + sc.y) + sh.y;
+            y.z = y.z * (1.0f + sc.z) + sh.z;
+            y.w = y.w * (1.0f + sc.w) + sh.w;
+        }
+        if (OUT == 2) {
+            if (c < n4) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
+            v[i] = y;
+        } else if (c < n4) {
+            if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * c, y);
+            else store4((bf16*)out + (size_t)row * D + 4 * c, y);
+        }
+    }
+    if (OUT == 2) {
+        amax = wave_max(amax);
+        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+        uint8_t* o = (uint8_t*)out + (size_t)row * D;
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int c = lane + kWave * i;
+            if (c < n4) {
+                uint32_t lo = pack2_e4m3(v[i].x * inv, v[i].y * inv), hi = pack2_e4m3(v[i].z * inv, v[i].w * inv);
+                *(uint32_t*)(o + 4 * c) = lo | (hi << 16);
+            }
+        }
+        if (lane == 0) out_scale[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+}
+
+template <int OUT, bool MOD>
+static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float* mod, int shc, int scc, void* out,
+                              float* out_scale, hipStream_t st) {
+    const int need = (D / 4 + kWave - 1) / kWave;
+    dim3 grid((M + 3) / 4);
+#define LWO_LN_CASE(NV)                                                                                     \
+    if (need <= NV) {                                                                                       \
+        k_ln<OUT, MOD, NV><<<grid, 256, 0, st>>>(xr, M, D, T, mod, shc, scc, out, out_scale);              \
+        return hipGetLastError();                                                                           \
+    }
+    LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(5) LWO_LN_CASE(8)
+    LWO_LN_CASE(12) LWO_LN_CASE(16) LWO_LN_CASE(20) LWO_LN_CASE(24) LWO_LN_CASE(32)
+#undef LWO_LN_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln(const float* xr, int M, int D, int T, const float* mod, int shift_chunk, int scale_chunk,
+                     void* out, int out_dt, float* out_scale, hipStream_t st) {
+    const bool m = mod != nullptr;
+    if (out_dt == LWO_F32) return m ? ln_dispatch<0, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
+                                    : ln_dispatch<0, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
+    if (out_dt == LWO_BF16) return m ? ln_dispatch<1, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
+                                     : ln_dispatch<1, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
+    return m ? ln_dispatch<2, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
+             : ln_dispatch<2, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
+}
+
+// ------------------------------------------------------------------ q/k RMSNorm
+
+template <typename T, int NV4>
+__global__ __launch_bounds__(256) void k_rmsnorm_qk(T* __restrict__ qkv, int M, int D, const T* __restrict__ gq,
+                                                    const T* __restrict__ gk) {
+    const int w = blockIdx.x * 4 + threadIdx.x / kWave;   // (row, part)
+    const int lane = threadIdx.x % kWave;
+    if (w >= 2 * M) return;
+    const int row = w >> 1, part = w & 1;
+    T* x = qkv + (size_t)row * 3 * D + (size_t)part * D;
+    const T* g = part ? gk : gq;
+    const int n4 = D / 4;
+    float4 v[NV4];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int c = lane + kWave * i;
+        v[i] = c < n4 ? load4(x + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+    }
+    const float r = 1.0f / sqrtf(wave_sum(s) / (float)D + 1e-6f);
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n4) {
+            const float4 gv = load4(g + 4 * c);
+            store4(x + 4 * c, make_float4(v[i].x * r * gv.x, v[i].y * r * gv.y, v[i].z * r * gv.z, v[i].w * r * gv.w));
+        }
+    }
+}
+
+template <typename T>
+static hipError_t rms_dispatch(T* qkv, int M, int D, const T* gq, const T* gk, hipStream_t st) {
+    const int need = (D / 4 + kWave - 1) / kWave;
+    dim3 grid((2 * M + 3) / 4);
+#define LWO_RMS_CASE(NV)                                                          \
+    if (need <= NV) {                                                             \
+        k_rmsnorm_qk<T, NV><<<grid, 256, 0, st>>>(qkv, M, D, gq, gk);             \
+        return hipGetLastError();                                                 \
+    }
+    LWO_RMS_CASE(1) LWO_RMS_CASE(2) LWO_RMS_CASE(4) LWO_RMS_CASE(8) LWO_RMS_CASE(12) LWO_RMS_CASE(16)
+    LWO_RMS_CASE(20) LWO_RMS_CASE(24) LWO_RMS_CASE(32)
+#undef LWO_RMS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_rmsnorm_qk(void* qkv, int dt, int M, int D, const void* gq, const void* gk, hipStream_t st) {
+    if (dt == LWO_F32) return rms_dispatch<float>((float*)qkv, M, D, (const float*)gq, (const float*)gk, st);
+    return rms_dispatch<bf16>((bf16*)qkv, M, D, (const bf16*)gq, (const bf16*)gk, st);
+}
+
+// ------------------------------------------------------------------ fp8 row quantisation
+
+// One wavefront per row: amax over the row, then codes = e4m3(x * (448 / amax)), scale = amax / 448.
+__global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in, int M, int N,
+                                                    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (row >= M) return;
+    const bf16* x = in + (size_t)row * N;
+    float amax = 0.0f;
+    for (int c = lane; c < N / 8; c += kWave) {
+        bf16x8 v = *(const bf16x8*)(x + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+    }
+    amax = wave_max(amax);
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    uint8_t* o = codes + (size_t)row * N;
+    for (int c = lane; c < N / 8; c += kWave) {
+        bf16x8 v = *(const bf16x8*)(x + 8 * c);
+        uint32_t w0 = pack2_e4m3((float)v[0] * inv, (float)v[1] * inv) | (pack2_e4m3((float)v[2] * inv, (float)v[3] * inv) << 16);
+        uint32_t w1 = pack2_e4m3((float)v[4] * inv, (float)v[5] * inv) | (pack2_e4m3((float)v[6] * inv, (float)v[7] * inv) << 16);
+        *(uint2*)(o + 8 * c) = make_uint2(w0, w1);
+    }
+    if (lane == 0) scales[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st) {
+    k_quant_rows<<<(M + 3) / 4, 256, 0, st>>>((const bf16*)in, M, N, codes, scales);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ slot checksum
+
+__device__ __forceinline__ uint64_t splitmix64_next(uint64_t s) {
+    uint64_t z = s + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// acc[0] += sum_i SplitMix64(w_i ^ (i * golden)) over n words (integer sum: any order gives the same bits).
+__global__ __launch_bounds__(256) void k_checksum(const uint64_t* __restrict__ w, uint64_t n,
+                                                  unsigned long long* __restrict__ acc) {
+    uint64_t s = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        s += splitmix64_next(w[i] ^ (i * 0x9E3779B97F4A7C15ull));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor((unsigned long long)s, o);
+    if ((threadIdx.x % kWave) == 0) atomicAdd(acc, (unsigned long long)s);
+}
+
+__global__ void k_checksum_compare(unsigned long long* acc, unsigned long long expect) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && acc[0] != expect) atomicAdd(acc + 1, 1ull);
+}
+
+__global__ void k_zero_u64(unsigned long long* p, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_checksum(const void* dev, uint64_t bytes, uint64_t* acc, hipStream_t st) {
+    const uint64_t n = bytes / 8;
+    int g = (int)((n + 256 * 16 - 1) / (256 * 16));
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    k_checksum<<<g, 256, 0, st>>>((const uint64_t*)dev, n, (unsigned long long*)acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_checksum_compare(uint64_t* acc, uint64_t expect, hipStream_t st) {
+    k_checksum_compare<<<1, 64, 0, st>>>((unsigned long long*)acc, (unsigned long long)expect);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u64(uint64_t* p, int n, hipStream_t st) {
+    k_zero_u64<<<(n + 63) / 64, 64, 0, st>>>((unsigned long long*)p, n);
+    return hipGetLastError();
+}
+
+}  // namespace lwo

@@ -1,0 +1,481 @@
+// The block store: host weight extents, the two-slot device arena, the copy
+// stream with its readiness events, and the ring that streams blocks
+// through the slots during a denoise step.
+//
+// Design sources (offloader documentation pages):
+//  * "CPU Offloading for Diffusion Models", "Layerwise (Blockwise) Offloading
+//    / How It Works": a dedicated copy stream prefetches block i+1 while
+//    block i computes, parameters are kept as flattened pinned host tensors,
+//    and the last block prefetches block 0 (execution-flow table).
+//  * "Distributed Layerwise Offload", "Startup and runtime sequence": two
+//    shared device slots sized for the largest streamed block, compute waits
+//    until the current slot is ready, the next block goes to the alternate
+//    slot, the first block is primed at enable; "Feature compatibility":
+//    resident leading layers; "Registered runtime-cache transfer" and
+//    "Failure and lifecycle boundaries": page-aligned, coalesced, budgeted,
+//    read-only, all-or-nothing host registration, and shutdown order
+//    (synchronise, unregister, then release).
+//  * "CPU Offloading", "Cross-strategy invariants": device storage is not
+//    reused until dependent compute or transfer work is complete; "Shared
+//    lifecycle": a failed enable leaves no partial state.
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <thread>
+
+#include "lwo_internal.h"
+
+using namespace lwo;
+
+struct lwo_store {
+    lwo_model_desc d{};
+    Layout L;
+    int device = 0;
+    int host_mode = LWO_HOST_PIN_COPY;
+    std::vector<void*> host;              // per-block host extent
+    bool host_owned = false;              // PIN_COPY: allocated with hipHostMalloc
+    std::vector<uint64_t> reg_base, reg_len;
+    std::vector<uint64_t> host_sums;      // lazily computed host checksums
+    bool sums_ready = false;
+    char* slot[2] = {nullptr, nullptr};
+    int slot_block[2] = {-1, -1};         // block held (or being received) by each slot
+    char* resident = nullptr;
+    int k = 0;
+    int head_slot = 0;                    // slot holding (or receiving) block k
+    hipStream_t copy = nullptr;
+    hipEvent_t copy_done[2] = {nullptr, nullptr};
+    hipEvent_t compute_done[2] = {nullptr, nullptr};
+    Workspace ws;
+    bool validation = false;
+    bool timing = false;
+    std::vector<hipEvent_t> tev;          // timing events, two per copy of the last step
+    int n_timed = 0;
+    uint64_t h2d_copies = 0, h2d_bytes = 0, steps = 0;
+    double build_ms = 0;
+    bool dead = false;
+};
+
+// ------------------------------------------------------------------ registration
+
+extern "C" lwo_status lwo_register_ranges(const void* const* ptrs, const uint64_t* bytes, int32_t n, uint64_t page,
+                                          uint64_t budget, lwo_register_fn reg, lwo_unregister_fn unreg, void* user,
+                                          uint64_t* out_base, uint64_t* out_len, int32_t cap, int32_t* n_out) {
+    clear_error();
+    if (n < 0 || (n && (!ptrs || !bytes)) || !reg || !unreg || page == 0 || (page & (page - 1))) {
+        set_error("register: bad arguments (page must be a power of two)");
+        return LWO_EINVAL;
+    }
+    // page-align every range outward, then coalesce overlapping or adjacent ranges
+    std::vector<std::pair<uint64_t, uint64_t>> r;   // [begin, end)
+    for (int i = 0; i < n; ++i) {
+        if (!bytes[i]) continue;
+        uint64_t b = (uint64_t)(uintptr_t)ptrs[i];
+        uint64_t e = b + bytes[i];
+        r.emplace_back(b & ~(page - 1), (e + page - 1) & ~(page - 1));
+    }
+    std::sort(r.begin(), r.end());
+    std::vector<std::pair<uint64_t, uint64_t>> c;
+    for (auto& x : r) {
+        if (!c.empty() && x.first <= c.back().second) c.back().second = std::max(c.back().second, x.second);
+        else c.push_back(x);
+    }
+    uint64_t total = 0;
+    for (auto& x : c) total += x.second - x.first;
+    if (n_out) *n_out = (int32_t)c.size();
+    if (cap < (int32_t)c.size() || (!c.empty() && (!out_base || !out_len))) {
+        set_error("register: output capacity smaller than the coalesced range count");
+        return LWO_EINVAL;
+    }
+    if (total > budget) {   // checked before any registration call
+        set_error("register: " + std::to_string(total) + " bytes exceed the budget of " + std::to_string(budget));
+        return LWO_EBUDGET;
+    }
+    for (size_t i = 0; i < c.size(); ++i) {
+        if (reg(user, (void*)(uintptr_t)c[i].first, c[i].second - c[i].first) != 0) {
+            bool rb_ok = true;
+            for (size_t j = i; j-- > 0;)
+                if (unreg(user, (void*)(uintptr_t)c[j].first) != 0) rb_ok = false;
+            if (!rb_ok) {
+                set_error("register: range " + std::to_string(i) + " failed and a rollback unregister failed; "
+                          "the ranges that could not be unregistered must stay mapped");
+                return LWO_EROLLBACK;
+            }
+            set_error("register: range " + std::to_string(i) + " failed; all earlier ranges were unregistered");
+            return LWO_EREGISTER;
+        }
+    }
+    for (size_t i = 0; i < c.size(); ++i) {
+        out_base[i] = c[i].first;
+        out_len[i] = c[i].second - c[i].first;
+    }
+    return LWO_OK;
+}
+
+static int32_t hip_register_cb(void*, void* base, uint64_t bytes) {
+    return hipHostRegister(base, bytes, hipHostRegisterReadOnly) == hipSuccess ? 0 : 1;
+}
+static int32_t hip_unregister_cb(void*, void* base) {
+    return hipHostUnregister(base) == hipSuccess ? 0 : 1;
+}
+
+// ------------------------------------------------------------------ teardown
+
+static void release(lwo_store* s) {
+    if (!s) return;
+    (void)hipSetDevice(s->device);
+    if (s->copy) (void)hipStreamSynchronize(s->copy);
+    (void)hipDeviceSynchronize();   // compute that may still read a slot runs on caller streams
+    if (s->host_mode == LWO_HOST_REGISTER) {
+        for (size_t i = s->reg_base.size(); i-- > 0;) (void)hipHostUnregister((void*)(uintptr_t)s->reg_base[i]);
+        s->reg_base.clear();
+        s->reg_len.clear();
+    }
+    if (s->host_owned)
+        for (void* p : s->host)
+            if (p) (void)hipHostFree(p);
+    s->host.clear();
+    for (int i = 0; i < 2; ++i) {
+        if (s->slot[i]) (void)hipFree(s->slot[i]);
+        if (s->copy_done[i]) (void)hipEventDestroy(s->copy_done[i]);
+        if (s->compute_done[i]) (void)hipEventDestroy(s->compute_done[i]);
+    }
+    for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
+    if (s->resident) (void)hipFree(s->resident);
+    workspace_free(&s->ws);
+    if (s->copy) (void)hipStreamDestroy(s->copy);
+    delete s;
+}
+
+// ------------------------------------------------------------------ helpers
+
+static lwo_status prime_head(lwo_store* s) {
+    // Block k goes to slot 0 on the copy stream ([DLO] prime the first block).
+    s->head_slot = 0;
+    s->slot_block[0] = s->slot_block[1] = -1;
+    if (s->k >= s->d.n_blocks) return LWO_OK;
+    LWO_HIP_TRY(hipMemcpyAsync(s->slot[0], s->host[s->k], s->L.extent_bytes, hipMemcpyHostToDevice, s->copy));
+    LWO_HIP_TRY(hipEventRecord(s->copy_done[0], s->copy));
+    s->slot_block[0] = s->k;
+    s->h2d_copies++;
+    s->h2d_bytes += s->L.extent_bytes;
+    return LWO_OK;
+}
+
+static void compute_host_sums(lwo_store* s) {
+    if (s->sums_ready) return;
+    const int n = s->d.n_blocks;
+    s->host_sums.assign(n, 0);
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < nt; ++t)
+        th.emplace_back([s, t, nt, n] {
+            for (int b = (int)t; b < n; b += (int)nt) s->host_sums[b] = extent_checksum_host(s->host[b], s->L.extent_bytes);
+        });
+    for (auto& x : th) x.join();
+    s->sums_ready = true;
+}
+
+static lwo_status check_store(lwo_store* s) {
+    if (!s) { set_error("store is NULL"); return LWO_EINVAL; }
+    if (s->dead) { set_error("store is not usable after a failed call"); return LWO_ESTATE; }
+    return LWO_OK;
+}
+
+// ------------------------------------------------------------------ build
+
+static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uint64_t budget) {
+    const uint64_t ext = s->L.extent_bytes;
+    const int n = s->d.n_blocks;
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    s->host.assign(n, nullptr);
+    if (mode == LWO_HOST_PIN_COPY) {
+        s->host_owned = true;
+        for (int b = 0; b < n; ++b) {
+            void* p = nullptr;
+            if (hipHostMalloc(&p, ext, hipHostMallocDefault) != hipSuccess || !p) {
+                set_error("hipHostMalloc of block " + std::to_string(b) + " (" + std::to_string(ext) + " bytes) failed");
+                return LWO_ENOMEM;
+            }
+            s->host[b] = p;
+            if (src->extents) {
+                if (!src->extents[b]) { set_error("extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
+                std::memcpy(p, src->extents[b], ext);
+            } else if (src->fill(src->user, b, p, ext) != 0) {
+                set_error("fill callback failed for block " + std::to_string(b));
+                return LWO_EINVAL;
+            }
+        }
+    } else {
+        if (!src->extents) { set_error("REGISTER mode needs caller extents"); return LWO_EINVAL; }
+        const uint64_t page = 4096;
+        std::vector<uint64_t> lens(n, ext);
+        for (int b = 0; b < n; ++b) {
+            if (!src->extents[b] || ((uintptr_t)src->extents[b] % page)) {
+                set_error("REGISTER mode needs page-aligned extents (block " + std::to_string(b) + ")");
+                return LWO_EINVAL;
+            }
+            s->host[b] = const_cast<void*>(src->extents[b]);
+        }
+        std::vector<uint64_t> base(n), len(n);
+        int32_t nr = 0;
+        lwo_status st = lwo_register_ranges(src->extents, lens.data(), n, page, budget, hip_register_cb,
+                                            hip_unregister_cb, nullptr, base.data(), len.data(), n, &nr);
+        if (st != LWO_OK) return st;
+        s->reg_base.assign(base.begin(), base.begin() + nr);
+        s->reg_len.assign(len.begin(), len.begin() + nr);
+        for (int b = 0; b < n; ++b) {   // every extent must now be known to HIP as registered host memory
+            unsigned int flags = 0;
+            if (hipHostGetFlags(&flags, s->host[b]) != hipSuccess) {
+                set_error("registered extent " + std::to_string(b) + " is not recognised as pinned");
+                return LWO_EREGISTER;
+            }
+        }
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (hipMalloc(&s->slot[i], ext) != hipSuccess) { s->slot[i] = nullptr; set_error("hipMalloc of a slot failed"); return LWO_ENOMEM; }
+        LWO_HIP_TRY(hipEventCreateWithFlags(&s->copy_done[i], hipEventDisableTiming));
+        LWO_HIP_TRY(hipEventCreateWithFlags(&s->compute_done[i], hipEventDisableTiming));
+    }
+    LWO_TRY(workspace_alloc(s->d, &s->ws));
+    LWO_HIP_TRY(hipStreamCreateWithFlags(&s->copy, hipStreamNonBlocking));
+    LWO_TRY(prime_head(s));
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t host_mode,
+                                            uint64_t register_budget, int32_t device, lwo_store** out) {
+    clear_error();
+    if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
+    *out = nullptr;
+    LWO_TRY(validate_desc(desc));
+    if (!src || (!src->extents && !src->fill)) { set_error("block source has neither extents nor fill"); return LWO_EINVAL; }
+    if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER) { set_error("host_mode"); return LWO_EINVAL; }
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+        set_error("device " + std::to_string(device) + " is not available");
+        return LWO_EINVAL;
+    }
+    auto t0 = std::chrono::steady_clock::now();
+    lwo_store* s = new (std::nothrow) lwo_store();
+    if (!s) { set_error("out of host memory"); return LWO_ENOMEM; }
+    s->d = *desc;
+    s->L = make_layout(*desc);
+    s->device = device;
+    s->host_mode = host_mode;
+    lwo_status st = build(s, src, host_mode, register_budget);
+    if (st != LWO_OK) {
+        std::string msg = lwo_last_error();
+        release(s);   // fail closed: nothing of the partial build survives
+        set_error(msg);
+        return st;
+    }
+    s->build_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    *out = s;
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_destroy_block_store(lwo_store* s) {
+    clear_error();
+    release(s);
+    return LWO_OK;
+}
+
+// ------------------------------------------------------------------ resident prefix
+
+extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    if (k < 0 || k > s->d.n_blocks) { set_error("resident prefix out of range"); return LWO_EINVAL; }
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    LWO_HIP_TRY(hipDeviceSynchronize());
+    const uint64_t ext = s->L.extent_bytes;
+    char* region = nullptr;
+    if (k > 0) {
+        if (hipMalloc(&region, ext * (uint64_t)k) != hipSuccess) {
+            set_error("hipMalloc of the resident region (" + std::to_string(ext * (uint64_t)k) + " bytes) failed");
+            return LWO_ENOMEM;   // previous prefix stays in effect
+        }
+        for (int b = 0; b < k; ++b) {
+            if (hipMemcpyAsync(region + ext * (uint64_t)b, s->host[b], ext, hipMemcpyHostToDevice, s->copy) != hipSuccess) {
+                (void)hipFree(region);
+                set_error("copy of resident block " + std::to_string(b) + " failed");
+                return LWO_EHIP;
+            }
+        }
+        if (hipStreamSynchronize(s->copy) != hipSuccess) {
+            (void)hipFree(region);
+            set_error("copy of the resident prefix failed");
+            return LWO_EHIP;
+        }
+    }
+    if (s->resident) (void)hipFree(s->resident);
+    s->resident = region;
+    s->k = k;
+    LWO_TRY(prime_head(s));
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    return LWO_OK;
+}
+
+// ------------------------------------------------------------------ the step
+
+static lwo_status validate_slot(lwo_store* s, const char* base, int block, hipStream_t st) {
+    LWO_TRY(enqueue_zero_u64(s->ws.sums, 1, st));
+    LWO_TRY(enqueue_checksum(base, s->L.extent_bytes, s->ws.sums, st));
+    return enqueue_checksum_compare(s->ws.sums, s->host_sums[block], st);
+}
+
+static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* ctx, hipStream_t st) {
+    const lwo_model_desc& d = s->d;
+    const uint64_t ext = s->L.extent_bytes;
+    const int n = d.n_blocks, k = s->k, m = n - k;
+    LWO_TRY(enqueue_step_begin(d, s->ws, x, ctx, st));
+    for (int b = 0; b < k; ++b) {
+        const char* base = s->resident + ext * (uint64_t)b;
+        LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, base), s->ws, cond, ctx, st));
+    }
+    if (m > 0) {
+        for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
+        s->tev.clear();
+        s->n_timed = 0;
+        int cur = s->head_slot;
+        for (int j = k; j < n; ++j) {
+            // RAW: the block's bytes must have landed before its kernels read them.
+            LWO_HIP_TRY(hipStreamWaitEvent(st, s->copy_done[cur], 0));
+            int nxt = cur;
+            if (m > 1) {
+                const int nb = (j + 1 < n) ? j + 1 : k;   // circular: the last block prefetches block k
+                nxt = 1 - cur;
+                if (s->slot_block[nxt] != nb) {
+                    // WAR: the alternate slot's previous block must have finished computing.
+                    LWO_HIP_TRY(hipStreamWaitEvent(s->copy, s->compute_done[nxt], 0));
+                    hipEvent_t e0 = nullptr, e1 = nullptr;
+                    if (s->timing) {
+                        LWO_HIP_TRY(hipEventCreate(&e0));
+                        LWO_HIP_TRY(hipEventCreate(&e1));
+                        s->tev.push_back(e0);
+                        s->tev.push_back(e1);
+                        LWO_HIP_TRY(hipEventRecord(e0, s->copy));
+                    }
+                    LWO_HIP_TRY(hipMemcpyAsync(s->slot[nxt], s->host[nb], ext, hipMemcpyHostToDevice, s->copy));
+                    if (s->timing) { LWO_HIP_TRY(hipEventRecord(e1, s->copy)); s->n_timed++; }
+                    LWO_HIP_TRY(hipEventRecord(s->copy_done[nxt], s->copy));
+                    s->slot_block[nxt] = nb;
+                    s->h2d_copies++;
+                    s->h2d_bytes += ext;
+                }
+            }
+            if (s->validation) LWO_TRY(validate_slot(s, s->slot[cur], j, st));
+            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st));
+            LWO_HIP_TRY(hipEventRecord(s->compute_done[cur], st));
+            cur = nxt;
+        }
+        s->head_slot = cur;   // the slot holding (or receiving) block k for the next step
+    }
+    LWO_TRY(enqueue_step_end(d, s->ws, x, st));
+    s->steps++;
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_run_denoise_step(lwo_store* s, void* x, const void* cond, const void* ctx, void* hip_stream) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    if (!hip_stream) { set_error("run needs a non-null stream (the legacy null stream would serialise with the copy stream)"); return LWO_EINVAL; }
+    if (!x || !cond) { set_error("x and cond are required"); return LWO_EINVAL; }
+    if (s->d.kind == LWO_KIND_VIDEO && !ctx) { set_error("video kind needs ctx"); return LWO_EINVAL; }
+    if (s->d.kind == LWO_KIND_DIT && ctx) { set_error("DiT kind takes no ctx"); return LWO_EINVAL; }
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    lwo_status st = run_step(s, x, cond, ctx, (hipStream_t)hip_stream);
+    if (st != LWO_OK) s->dead = true;   // the ring's events no longer describe the slots
+    return st;
+}
+
+// ------------------------------------------------------------------ validation and stats
+
+extern "C" lwo_status lwo_set_validation(lwo_store* s, int32_t on) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    if (on) compute_host_sums(s);
+    s->validation = on != 0;
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_set_copy_timing(lwo_store* s, int32_t on) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    s->timing = on != 0;
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_copy_times(lwo_store* s, float* ms, int32_t cap, int32_t* n) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    int cnt = s->n_timed;
+    if (n) *n = cnt;
+    for (int i = 0; i < cnt && i < cap && ms; ++i)
+        LWO_HIP_TRY(hipEventElapsedTime(&ms[i], s->tev[2 * i], s->tev[2 * i + 1]));
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* host_sum, uint64_t* slot_sum) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    if (block < 0 || block >= s->d.n_blocks || !host_sum || !slot_sum) { set_error("bad block or output"); return LWO_EINVAL; }
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_HIP_TRY(hipDeviceSynchronize());
+    compute_host_sums(s);
+    const uint64_t ext = s->L.extent_bytes;
+    const char* base = nullptr;
+    if (block < s->k) {
+        base = s->resident + ext * (uint64_t)block;
+    } else if (s->slot_block[0] == block || s->slot_block[1] == block) {
+        base = s->slot[s->slot_block[0] == block ? 0 : 1];
+    } else {
+        // borrow the slot the ring is not about to read
+        int sl = 1 - s->head_slot;
+        LWO_HIP_TRY(hipMemcpyAsync(s->slot[sl], s->host[block], ext, hipMemcpyHostToDevice, s->copy));
+        LWO_HIP_TRY(hipEventRecord(s->copy_done[sl], s->copy));
+        s->slot_block[sl] = block;
+        base = s->slot[sl];
+    }
+    LWO_TRY(enqueue_zero_u64(s->ws.sums, 1, s->copy));
+    LWO_TRY(enqueue_checksum(base, ext, s->ws.sums, s->copy));
+    uint64_t got = 0;
+    LWO_HIP_TRY(hipMemcpyAsync(&got, s->ws.sums, 8, hipMemcpyDeviceToHost, s->copy));
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    *host_sum = s->host_sums[block];
+    *slot_sum = got;
+    if (got != s->host_sums[block]) { set_error("slot checksum differs from the host extent"); return LWO_ECHECKSUM; }
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
+    clear_error();
+    if (!s || !o) { set_error("NULL argument"); return LWO_EINVAL; }
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_HIP_TRY(hipDeviceSynchronize());
+    std::memset(o, 0, sizeof(*o));
+    const uint64_t ext = s->L.extent_bytes;
+    o->extent_bytes = ext;
+    o->slot_bytes = ext;
+    o->device_weight_bytes = ext * (uint64_t)(2 + s->k);
+    o->workspace_bytes = s->ws.bytes;
+    o->host_bytes = ext * (uint64_t)s->d.n_blocks;
+    o->h2d_copies = s->h2d_copies;
+    o->h2d_bytes = s->h2d_bytes;
+    o->steps = s->steps;
+    uint64_t mism = 0;
+    if (s->ws.sums) LWO_HIP_TRY(hipMemcpy(&mism, s->ws.sums + 1, 8, hipMemcpyDeviceToHost));
+    o->checksum_mismatches = mism;
+    o->registered_ranges = s->reg_base.size();
+    for (uint64_t l : s->reg_len) o->registered_bytes += l;
+    o->resident_prefix = s->k;
+    o->head_slot = s->head_slot;
+    o->host_mode = s->host_mode;
+    o->validation = s->validation;
+    o->build_ms = s->build_ms;
+    return LWO_OK;
+}

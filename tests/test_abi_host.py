@@ -1,0 +1,202 @@
+"""The C-ABI library on the host (no GPU): exported symbols, block layout,
+packing and checksum bit-exact against the oracle, descriptor validation and
+the all-or-nothing registration lifecycle."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import lwo_synth
+from oracle import checksum as o_checksum
+from oracle import layout as o_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lwo.h")
+
+DT = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lwo_[a-z_]+)\s*\(", src)) - {"lwo_register_fn", "lwo_unregister_fn"})
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert "lwo_run_denoise_step" in declared and "lwo_build_block_store" in declared
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lwo_\w+)", out))
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    assert sorted(lib.exported_symbols()) == declared
+
+
+@pytest.mark.parametrize("name", sorted(lwo_synth.WORKLOADS))
+def test_layout_matches_oracle(lib, name):
+    w = lwo_synth.get(name)
+    got, ext = lib.block_layout(lib.ModelDesc.from_workload(w))
+    want, want_ext = o_layout.layout_for(w)
+    assert ext == want_ext
+    assert [(t["name"], t["offset"], t["bytes"], t["shape"], t["dtype"]) for t in got] == \
+           [(s.name, s.offset, s.nbytes, tuple(s.shape), DT[s.dtype]) for s in want]
+
+
+def _edge_tensors(w, b):
+    """Generator draws with a few planted rounding edge cases."""
+    t = lwo_synth.block_tensors(w, b)
+    edges = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, 1e-30, -1e-30, 3e38, 2 ** -130,
+                      0.5 + 2 ** -10, 7.0, 15.5], dtype=np.float32)
+    for a in t:
+        n = min(a.size, edges.size)
+        a.reshape(-1)[:n] = edges[:n] * (0.02 if a.size > 4096 else 1.0)
+    return t
+
+
+@pytest.mark.parametrize("name", ["dit_t_fp32", "dit_t_bf16", "video_t_fp32", "video_t_bf16", "video_t_fp8",
+                                  "dit_tiny_fp32"])
+def test_pack_bit_exact_vs_oracle(lib, name):
+    w = lwo_synth.get(name)
+    desc = lib.ModelDesc.from_workload(w)
+    for b in range(2):
+        t = lwo_synth.block_tensors(w, b) if b == 0 else _edge_tensors(w, b)
+        got = lib.pack_block(desc, t)
+        want = np.frombuffer(o_layout.pack_block(w, t), np.uint8)
+        assert got.size == want.size
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (name, b, bad[:10])
+
+
+def test_fp8_pack_ties_and_saturation(lib):
+    """Values exactly between two e4m3 codes, scaled so that w / s lands on them."""
+    w = lwo_synth.get("video_t_fp8")
+    desc = lib.ModelDesc.from_workload(w)
+    t = lwo_synth.block_tensors(w, 0)
+    q = t[1]   # attn.q.w: force amax = 448 so s = 1 and codes are the values themselves
+    from oracle import codecs
+    pos = codecs.E4M3_VALUES[:127]
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([[448.0], mids, -mids, pos, -pos]).astype(np.float32)
+    q.reshape(-1)[:vals.size] = vals
+    q.reshape(-1)[vals.size:] = 0.0
+    got = lib.pack_block(desc, t)
+    want = np.frombuffer(o_layout.pack_block(w, t), np.uint8)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("nbytes", [0, 8, 4096, 1 << 20])
+def test_checksum_matches_oracle(lib, nbytes):
+    buf = np.random.default_rng(nbytes).integers(0, 256, nbytes, dtype=np.uint8).tobytes()
+    assert lib.extent_checksum(buf) == o_checksum.extent_checksum(buf)
+
+
+def test_checksum_of_packed_extent(lib):
+    w = lwo_synth.get("dit_t_bf16")
+    ext = lib.pack_block(lib.ModelDesc.from_workload(w), lwo_synth.block_tensors(w, 0))
+    assert lib.extent_checksum(ext) == o_checksum.extent_checksum(ext.tobytes())
+
+
+@pytest.mark.parametrize("field,value", [("heads", 3), ("hidden", 200), ("n_blocks", 0), ("tokens", 0),
+                                         ("act_dtype", 2), ("ctx_tokens", 5), ("linear_dtype", 2), ("ffn", 100)])
+def test_descriptor_validation(lib, field, value):
+    import dataclasses
+    w = lwo_synth.get("dit_t_bf16")
+    d = dataclasses.replace(lib.ModelDesc.from_workload(w), **{field: value})
+    with pytest.raises(lib.LwoError) as e:
+        lib.block_layout(d)
+    assert e.value.name == "LWO_EINVAL" and "invalid model desc" in str(e.value)
+
+
+def test_pack_rejects_bad_arguments(lib):
+    w = lwo_synth.get("dit_t_fp32")
+    desc = lib.ModelDesc.from_workload(w)
+    t = lwo_synth.block_tensors(w, 0)
+    with pytest.raises(lib.LwoError):
+        lib.pack_block(desc, t[:-1])
+    with pytest.raises(lib.LwoError):
+        lib.pack_block(desc, t, dst=bytearray(16))
+
+
+def test_build_fails_closed_without_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    w = lwo_synth.get("dit_tiny_fp32")
+    desc = lib.ModelDesc.from_workload(w)
+    calls = []
+    with pytest.raises(lib.LwoError) as e:
+        lib.build_block_store(desc, fill=lambda b, dst, n: calls.append(b))
+    assert e.value.name == "LWO_EINVAL" and "not available" in str(e.value)
+    assert calls == []
+
+
+# ------------------------------------------------------------------ registration lifecycle
+
+class FakePlatform:
+    def __init__(self, fail_at=None, unreg_fail=()):
+        self.fail_at = fail_at
+        self.unreg_fail = set(unreg_fail)
+        self.log = []
+        self.live = {}
+
+    def reg(self, base, ln):
+        i = len([x for x in self.log if x[0] == "reg"])
+        self.log.append(("reg", base, ln))
+        if self.fail_at is not None and i == self.fail_at:
+            return 1
+        self.live[base] = ln
+        return 0
+
+    def unreg(self, base):
+        self.log.append(("unreg", base))
+        if base in self.unreg_fail:
+            return 1
+        self.live.pop(base)
+        return 0
+
+
+P = 4096
+
+
+def test_register_aligns_and_coalesces(lib):
+    f = FakePlatform()
+    ptrs = [10 * P + 100, 10 * P + 3000, 12 * P, 20 * P + 5, 13 * P - 1]
+    sizes = [50, 2000, 10, P, 2]
+    got = lib.register_ranges(ptrs, sizes, P, 1 << 40, f.reg, f.unreg)
+    # [10P, 11P) + [10P, 12P) + [12P, 13P) + [12P, 14P) (13P-1 .. 13P+1 touches two pages) merge to
+    # [10P, 14P); [20P+5, 21P+5) becomes [20P, 22P) and stays apart
+    assert got == [(10 * P, 4 * P), (20 * P, 2 * P)]
+    assert [x for x in f.log if x[0] == "reg"] == [("reg", 10 * P, 4 * P), ("reg", 20 * P, 2 * P)]
+
+
+def test_register_budget_checked_before_any_call(lib):
+    f = FakePlatform()
+    with pytest.raises(lib.LwoError) as e:
+        lib.register_ranges([0, 4 * P], [P, P], P, 2 * P - 1, f.reg, f.unreg)
+    assert e.value.name == "LWO_EBUDGET"
+    assert f.log == []
+    assert lib.register_ranges([0, 4 * P], [P, P], P, 2 * P, f.reg, f.unreg) == [(0, P), (4 * P, P)]
+
+
+@pytest.mark.parametrize("fail_at", [0, 1, 3])
+def test_register_failure_rolls_back_in_reverse(lib, fail_at):
+    f = FakePlatform(fail_at=fail_at)
+    ptrs = [i * 4 * P for i in range(5)]
+    with pytest.raises(lib.LwoError) as e:
+        lib.register_ranges(ptrs, [P] * 5, P, 1 << 40, f.reg, f.unreg)
+    assert e.value.name == "LWO_EREGISTER"
+    assert f.live == {}
+    unregs = [x[1] for x in f.log if x[0] == "unreg"]
+    assert unregs == [ptrs[j] for j in range(fail_at - 1, -1, -1)]
+
+
+def test_register_rollback_failure_is_reported(lib):
+    ptrs = [i * 4 * P for i in range(4)]
+    f = FakePlatform(fail_at=3, unreg_fail={ptrs[1]})
+    with pytest.raises(lib.LwoError) as e:
+        lib.register_ranges(ptrs, [P] * 4, P, 1 << 40, f.reg, f.unreg)
+    assert e.value.name == "LWO_EROLLBACK"
+    assert set(f.live) == {ptrs[1]}      # the range that could not be unregistered stays registered
+    assert [x[1] for x in f.log if x[0] == "unreg"] == [ptrs[2], ptrs[1], ptrs[0]]

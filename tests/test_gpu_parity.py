@@ -1,0 +1,138 @@
+"""GPU parity through the C ABI: streamed execution against the float64 oracle,
+streamed == resident bit for bit, slot bytes == host bytes.
+
+Tolerances (relative L2 over the whole output, float64):
+  * fp32 workloads: 1e-4 on x_out and on the block-stack update x_out - x_in
+    (fp32 accumulation over K <= 4608 gives ~1e-6; the bound is the stated one);
+  * bf16 workloads: 2e-2 on x_out (the stated bound) and 3e-2 on the update:
+    every GEMM input is rounded to bf16 (relative 2^-9 per element), the
+    attention probabilities are rounded to bf16, and the output returns in
+    bf16, so a few 1e-3 per block is expected; 3e-2 leaves room for three
+    blocks without admitting a wrong term (a wrong term moves the update by
+    O(1)).
+"""
+import numpy as np
+import pytest
+
+import lwo_synth
+from oracle import dit as o_dit
+
+from .conftest import gpu_available
+from .gpu_util import device_inputs, make_store, oracle_out, run_steps, to_f64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _parity(lwo, name, tol_out, tol_delta, k=0, steps=1):
+    w = lwo_synth.get(name)
+    print(f"[parity] {name} k={k} steps={steps}", flush=True)
+    x0, want = oracle_out(w, steps=steps)
+    with make_store(lwo, w, k=k) as st:
+        x, cond, ctx = device_inputs(w)
+        run_steps(st, x, cond, ctx, steps=steps)
+        got = to_f64(x).reshape(want.shape)
+    assert np.isfinite(got).all()
+    e_out = o_dit.rel_l2(got, want)
+    e_delta = o_dit.rel_l2(got - x0, want - x0)
+    print(f"[parity] {name}: rel_l2(out)={e_out:.3e} rel_l2(update)={e_delta:.3e}", flush=True)
+    assert e_out <= tol_out and e_delta <= tol_delta, (e_out, e_delta)
+
+
+def test_dit_tiny_fp32_full(lib):
+    _parity(lib, "dit_tiny_fp32", 1e-4, 1e-4)
+
+
+@pytest.mark.parametrize("name", ["dit_t_fp32", "video_t_fp32"])
+def test_fp32_ragged(lib, name):
+    _parity(lib, name, 1e-4, 1e-4)
+
+
+@pytest.mark.parametrize("name", ["dit_t_bf16", "dit_t64_bf16", "video_t_bf16"])
+def test_bf16_ragged(lib, name):
+    _parity(lib, name, 2e-2, 3e-2)
+
+
+def test_two_steps_fp32(lib):
+    _parity(lib, "dit_t_fp32", 1e-4, 1e-4, steps=2)
+
+
+@pytest.mark.parametrize("name,ks", [("dit_t_bf16", (0, 1, 2, 3)), ("video_t_fp32", (0, 1, 3)),
+                                     ("dit_tiny_fp32", (0, 1, 4))])
+def test_streamed_equals_resident(lib, name, ks):
+    """Same kernels on the same bytes: every resident prefix gives identical bits,
+    over three consecutive steps (odd ring lengths flip the slot parity)."""
+    w = lwo_synth.get(name)
+    outs = {}
+    for k in ks:
+        print(f"[resident] {name} k={k}", flush=True)
+        with make_store(lib, w, k=k) as st:
+            x, cond, ctx = device_inputs(w)
+            run_steps(st, x, cond, ctx, steps=3)
+            outs[k] = x.cpu().view(-1).view(dtype=__import__("torch").int16 if w.act_dtype == "bf16" else
+                                             __import__("torch").int32).numpy().copy()
+    ref = outs[ks[0]]
+    for k in ks[1:]:
+        assert np.array_equal(outs[k], ref), k
+
+
+def test_slot_checksums_and_validation(lib):
+    w = lwo_synth.get("video_t_bf16")
+    from oracle import checksum as o_ck
+    from oracle import layout as o_layout
+    with make_store(lib, w) as st:
+        for b in range(w.n_blocks):
+            hs, ss = st.block_checksum(b)
+            assert hs == ss == o_ck.extent_checksum(o_layout.pack_block(w, lwo_synth.block_tensors(w, b)))
+        st.set_validation(True)
+        x, cond, ctx = device_inputs(w)
+        run_steps(st, x, cond, ctx, steps=2)
+        s = st.stats()
+        assert s.validation == 1 and s.checksum_mismatches == 0
+
+
+def test_copy_schedule_and_arena(lib):
+    """Two slots sized to the extent; one prime copy, then one copy per streamed block per step."""
+    w = lwo_synth.get("dit_t_fp32")   # 3 blocks
+    with make_store(lib, w) as st:
+        s0 = st.stats()
+        assert s0.h2d_copies == 1 and s0.device_weight_bytes == 2 * s0.extent_bytes
+        x, cond, ctx = device_inputs(w)
+        run_steps(st, x, cond, ctx, steps=2)
+        s = st.stats()
+        assert s.h2d_copies == 1 + 2 * 3 and s.h2d_bytes == s.h2d_copies * s.extent_bytes
+        st.set_resident_prefix(1)
+        s = st.stats()
+        assert s.resident_prefix == 1 and s.device_weight_bytes == 3 * s.extent_bytes
+        c0 = s.h2d_copies
+        run_steps(st, x, cond, ctx, steps=2)   # ring of two: both blocks stay in the two slots
+        assert st.stats().h2d_copies == c0 + 1
+
+
+def test_zero_gate_identity_gpu(lib):
+    w = lwo_synth.get("dit_t_bf16")
+    D = w.hidden
+
+    def tensors(b):
+        t = lwo_synth.block_tensors(w, b)
+        for g in (2, 5):
+            t[0][g * D:(g + 1) * D] = 0   # ada.w gate rows
+            t[1][g * D:(g + 1) * D] = 0   # ada.b gate entries
+        return t
+
+    with make_store(lib, w, tensors=tensors) as st:
+        x, cond, ctx = device_inputs(w)
+        x_in = x.clone()
+        run_steps(st, x, cond, ctx, steps=2)
+        assert bool((x == x_in).all())
+
+
+def test_run_argument_errors(lib):
+    w = lwo_synth.get("dit_tiny_fp32")
+    with make_store(lib, w) as st:
+        x, cond, ctx = device_inputs(w)
+        with pytest.raises(lib.LwoError):
+            st.run_denoise_step(x.data_ptr(), cond.data_ptr(), None, 0)          # null stream
+        with pytest.raises(lib.LwoError):
+            st.run_denoise_step(x.data_ptr(), cond.data_ptr(), x.data_ptr(), 1)   # ctx on the DiT kind
+        with pytest.raises(lib.LwoError):
+            st.set_resident_prefix(w.n_blocks + 1)
