@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Denoise-step benchmark of layerwise weight offload on one MI355X.
+
+One step = one pass of the whole block stack over one batch of synthetic
+input: every streamed block's weights are copied host -> device through the
+two slots while the previous block computes.  Default workload: the
+DiT-XL-shaped stack (28 blocks, D 1152, 16 heads, FFN 4608, batch 2, 1024
+tokens, bf16), all 28 blocks streamed.
+
+Timed regions (HIP events recorded on the stream the library enqueues on):
+  resident  blocks 0..L-1 kept on the device (no copies)       -> T_res
+  streamed  blocks k..L-1 streamed through the two slots        -> T_str (the value)
+  kernels   resident again, with per-kernel events              -> roofline of the dominant kernel
+plus a pinned-memory H2D peak (hipMemcpyAsync from hipHostMalloc'd memory,
+block-sized and 1 GiB copies, best of 10) and the oracle's time on the host
+for a bounded sample of blocks.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise-step ms streamed vs resident; H2D GB/s; overlap %; block TFLOP/s"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def pinned_peak(torch, nbytes: int, stream, reps: int = 10) -> float:
+    """Best-of-reps GB/s of one hipMemcpyAsync of nbytes from pinned host memory."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    best = 0.0
+    with torch.cuda.stream(stream):
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src, non_blocking=True)
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle (float64, every weight resident) on a bounded sample of blocks."""
+    import numpy as np
+    import lwo_synth
+    from oracle import dit as o_dit
+    from oracle import layout as o_layout
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    x, cond, ctx = o_dit.decode_inputs(w, *lwo_synth.step_inputs(w))
+    done, spent = 0, 0.0
+    while done < w.n_blocks and (done == 0 or spent < seconds):
+        ext = o_layout.pack_block(w, lwo_synth.block_tensors(w, done))   # packing is not timed
+        t0 = time.perf_counter()
+        x = o_dit.stack_forward(w, [ext], x, cond, ctx, blocks=[0])
+        spent += time.perf_counter() - t0
+        done += 1
+        log(f"oracle block {done}: {spent:.1f} s so far")
+    per_block_ms = spent / done * 1e3
+    return {"value": round(per_block_ms * w.n_blocks, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.n_blocks} blocks of one step timed ({spent:.1f} s), "
+                      f"per-block time x {w.n_blocks}; float64 NumPy, weights decoded from the packed extents"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit_xl_bf16")
+    ap.add_argument("--resident-prefix", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import layerwise_weight_offload_amd as lwo
+    import lwo_synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = lwo_synth.get(args.workload)
+    k = w.resident_prefix if args.resident_prefix is None else args.resident_prefix
+    L = w.n_blocks
+    desc = lwo.ModelDesc.from_workload(w)
+    _, ext = lwo.block_layout(desc)
+
+    # ---- build the store from the seeded generator (drawn ahead on host threads)
+    blocks = lwo_synth.iter_blocks(w)
+
+    def fill(b, dst, n):
+        bb, t = next(blocks)
+        assert bb == b
+        lwo.pack_block(desc, t, dst=dst, dst_bytes=n)
+
+    t0 = time.perf_counter()
+    store = lwo.build_block_store(desc, fill=fill)
+    log(f"built {L} x {ext / 1e6:.2f} MB extents in {time.perf_counter() - t0:.1f} s")
+
+    dt = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
+    xs, cs, cxs = lwo_synth.step_inputs(w)
+    x0 = torch.from_numpy(xs).to("cuda:0").to(dt)
+    cond = torch.from_numpy(cs).to("cuda:0").to(dt)
+    ctx = None if cxs is None else torch.from_numpy(cxs).to("cuda:0").to(dt)
+    x = x0.clone()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def region(steps: int, warmup: int) -> float:
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            store.run_denoise_step(x.data_ptr(), cond.data_ptr(), ctx.data_ptr() if ctx is not None else None,
+                                   s.cuda_stream)
+        s.synchronize()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            store.run_denoise_step(x.data_ptr(), cond.data_ptr(), ctx.data_ptr() if ctx is not None else None,
+                                   s.cuda_stream)
+        e1.record(s)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # ---- all resident
+    store.set_resident_prefix(L)
+    t_res = region(args.steps, args.warmup)
+    log(f"resident: {t_res:.3f} ms/step")
+
+    # ---- per-kernel timing (resident, same kernels)
+    store.set_kernel_timing(True)
+    region(args.steps, 0)
+    kstats = store.kernel_stats()
+    store.set_kernel_timing(False)
+
+    # ---- streamed
+    store.set_resident_prefix(k)
+    t_str = region(args.steps, args.warmup)
+    log(f"streamed (k={k}): {t_str:.3f} ms/step")
+    store.set_copy_timing(True)
+    region(1, 0)
+    copy_ms = store.copy_times()
+    store.set_copy_timing(False)
+    st = store.stats()
+
+    # ---- pinned H2D peak
+    peak_block = pinned_peak(torch, ext, s)
+    peak_gib = pinned_peak(torch, 1 << 30, s, reps=5)
+    peak = max(peak_block, peak_gib)
+    log(f"pinned H2D peak: block-sized {peak_block:.1f} GB/s, 1 GiB {peak_gib:.1f} GB/s")
+
+    m = L - k
+    copies_per_step = m if m >= 3 else 0
+    bytes_per_step = copies_per_step * ext
+    h2d_gbps = bytes_per_step / (t_str * 1e-3) / 1e9 if bytes_per_step else 0.0
+    t_copy = bytes_per_step / (peak_block * 1e9) * 1e3 if bytes_per_step else 0.0
+    overlap = None
+    if t_copy > 0:
+        overlap = max(0.0, min(1.0, (t_res + t_copy - t_str) / min(t_res, t_copy)))
+    per_copy = [ext / (c * 1e-3) / 1e9 for c in copy_ms if c > 0]
+
+    steps_timed = args.steps
+    flops_step = sum(kk["flops"] for kk in kstats) / steps_timed
+    block_tflops = flops_step / (t_res * 1e-3) / 1e12
+    lin_dt = w.linear_dtype if w.linear_dtype != "f32" else "f32"
+    dom = max(kstats, key=lambda kk: kk["total_ms"])
+    avg_ms = dom["total_ms"] / dom["launches"]
+    if dom["flops"] > 0:
+        kdt = "fp8" if "fp8" in dom["name"] else ("f32" if "f32" in dom["name"] else "bf16")
+        ach = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[kdt], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS[kdt], 4)}
+    else:
+        ach = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    roof.update({"kernel": dom["name"], "avg_launch_ms": round(avg_ms, 4), "launches_per_step": dom["launches"] // steps_timed,
+                 "traffic": None})
+
+    kernels = {kk["name"]: {"ms_per_step": round(kk["total_ms"] / steps_timed, 4),
+                            "launches_per_step": kk["launches"] // steps_timed,
+                            "tflops": round(kk["flops"] / (kk["total_ms"] * 1e-3) / 1e12, 1) if kk["flops"] else None,
+                            "gbps": round(kk["bytes"] / (kk["total_ms"] * 1e-3) / 1e9, 1)}
+               for kk in sorted(kstats, key=lambda kk: -kk["total_ms"])}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        store.destroy()   # release pinned host memory before the oracle allocates
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(t_str, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_str, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8+bf16"}[w.linear_dtype],
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs)",
+        "config": {"workload": w.name, "kind": w.kind, "blocks": L, "hidden": w.hidden, "heads": w.heads,
+                   "ffn": w.ffn, "batch": w.batch, "tokens": w.tokens, "ctx_tokens": w.ctx_tokens,
+                   "act_dtype": w.act_dtype, "linear_dtype": w.linear_dtype, "resident_prefix": k,
+                   "streamed_blocks": m, "host_mode": "pin_copy", "extent_bytes": ext},
+        "resident_ms": round(t_res, 3),
+        "streamed_over_resident": round(t_str / t_res, 4),
+        "h2d_gbps": round(h2d_gbps, 2),
+        "pinned_peak_gbps": round(peak, 2),
+        "pinned_peak_block_gbps": round(peak_block, 2),
+        "h2d_frac_of_pinned_peak": round(h2d_gbps / peak_block, 4) if bytes_per_step else None,
+        "per_copy_gbps_median": round(float(np.median(per_copy)), 2) if per_copy else None,
+        "copy_ms_if_serial": round(t_copy, 3),
+        "overlap_pct": None if overlap is None else round(100 * overlap, 1),
+        "block_tflops": round(block_tflops, 2),
+        "block_mfma_frac": round(block_tflops / MFMA_PEAK_TFLOPS[lin_dt if lin_dt != "fp8" else "bf16"], 4),
+        "h2d_copies_total": st.h2d_copies,
+        "build_s": round(st.build_ms / 1e3, 2),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

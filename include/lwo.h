@@ -247,6 +247,24 @@ lwo_status lwo_block_checksum(lwo_store* store, int32_t block, uint64_t* host_su
 lwo_status lwo_set_copy_timing(lwo_store* store, int32_t on);
 lwo_status lwo_copy_times(lwo_store* store, float* ms, int32_t cap, int32_t* n);
 
+/* Per-kernel timing: when on, every kernel a step enqueues for a block is
+ * bracketed by timing events on the compute stream.  lwo_kernel_stats
+ * synchronises and returns, per kernel (one entry per kernel symbol), the
+ * launches, their total duration and their total algorithmic flops and HBM
+ * bytes since timing was switched on (or last reset by on = 1 again).  cap
+ * entries at most (out may be NULL with cap 0 to query the count); count in
+ * *n (LWO_EINVAL if cap is too small). */
+typedef struct lwo_kernel_stat {
+    char name[48];
+    uint64_t launches;
+    double total_ms;
+    double flops;          /* algorithmic: 2MNK per GEMM, 4 B H Tq Tk d per attention */
+    double bytes;          /* algorithmic HBM bytes: operands read once, results written once */
+} lwo_kernel_stat;
+
+lwo_status lwo_set_kernel_timing(lwo_store* store, int32_t on);
+lwo_status lwo_kernel_stats(lwo_store* store, lwo_kernel_stat* out, int32_t cap, int32_t* n);
+
 /* Synchronise the store's copy stream and snapshot its counters. */
 lwo_status lwo_get_stats(lwo_store* store, lwo_stats* out);
 

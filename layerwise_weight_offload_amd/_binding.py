@@ -59,6 +59,11 @@ class _Stats(C.Structure):
                [("build_ms", C.c_double)]
 
 
+class _KStat(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_uint64), ("total_ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -83,12 +88,15 @@ _lib_block_checksum = _sig("lwo_block_checksum", C.c_int, _P, C.c_int32, C.POINT
 _lib_set_copy_timing = _sig("lwo_set_copy_timing", C.c_int, _P, C.c_int32)
 _lib_copy_times = _sig("lwo_copy_times", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32))
 _lib_get_stats = _sig("lwo_get_stats", C.c_int, _P, C.POINTER(_Stats))
+_lib_set_kernel_timing = _sig("lwo_set_kernel_timing", C.c_int, _P, C.c_int32)
+_lib_kernel_stats = _sig("lwo_kernel_stats", C.c_int, _P, C.POINTER(_KStat), C.c_int32, C.POINTER(C.c_int32))
 _lib_destroy = _sig("lwo_destroy_block_store", C.c_int, _P)
 _lib_last_error = _sig("lwo_last_error", C.c_char_p)
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
             "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_validation",
-            "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_get_stats",
+            "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
+            "lwo_kernel_stats", "lwo_get_stats",
             "lwo_destroy_block_store", "lwo_last_error"]
 
 
@@ -248,6 +256,19 @@ class Store:
         n = C.c_int32()
         _check(_lib_copy_times(self._live(), buf, cap, C.byref(n)))
         return [buf[i] for i in range(min(n.value, cap))]
+
+    def set_kernel_timing(self, on: bool) -> None:
+        """Switch per-kernel timing on (resetting the totals) or off."""
+        _check(_lib_set_kernel_timing(self._live(), 1 if on else 0))
+
+    def kernel_stats(self) -> list[dict]:
+        """[dict(name, launches, total_ms, flops, bytes)] since timing was switched on."""
+        n = C.c_int32()
+        _check(_lib_kernel_stats(self._live(), None, 0, C.byref(n)))
+        arr = (_KStat * max(n.value, 1))()
+        _check(_lib_kernel_stats(self._live(), arr, n.value, C.byref(n)))
+        return [dict(name=k.name.decode(), launches=k.launches, total_ms=k.total_ms, flops=k.flops, bytes=k.bytes)
+                for k in arr[:n.value]]
 
     def stats(self) -> Stats:
         s = _Stats()

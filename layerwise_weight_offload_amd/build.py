@@ -1,6 +1,9 @@
 """Build liblwo.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m layerwise_weight_offload_amd.build
+    python layerwise_weight_offload_amd/build.py
+
+(run it as a script: importing the package would load the library it is
+about to replace).
 
 Every source under csrc/ is compiled with hipcc for gfx950 only; packed fp32
 VALU instructions are disabled for all device code.

@@ -9,6 +9,7 @@
 // projections and attention outputs are in the activation dtype (or e4m3
 // codes with per-row scales when the linears are fp8).
 #include <algorithm>
+#include <cstdio>
 
 #include "kernels.h"
 #include "lwo_internal.h"
@@ -59,6 +60,52 @@ void workspace_free(Workspace* ws) {
     *ws = Workspace();
 }
 
+// ------------------------------------------------------------------ kernel timing
+
+hipEvent_t KernelTimer::get() {
+    hipEvent_t e = nullptr;
+    if (!pool.empty()) { e = pool.back(); pool.pop_back(); return e; }
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+int KernelTimer::cls(const char* name) {
+    for (size_t i = 0; i < agg.size(); ++i)
+        if (agg[i].name == name) return (int)i;
+    agg.push_back(Agg());
+    agg.back().name = name;
+    return (int)agg.size() - 1;
+}
+
+lwo_status KernelTimer::collect() {
+    for (Rec& r : pending) {
+        LWO_HIP_TRY(hipEventSynchronize(r.b));
+        float ms = 0.0f;
+        LWO_HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+        Agg& a = agg[r.cls];
+        a.launches++;
+        a.ms += ms;
+        a.flops += r.flops;
+        a.bytes += r.bytes;
+        pool.push_back(r.a);
+        pool.push_back(r.b);
+    }
+    pending.clear();
+    return LWO_OK;
+}
+
+void KernelTimer::reset() {
+    for (Rec& r : pending) { pool.push_back(r.a); pool.push_back(r.b); }
+    pending.clear();
+    agg.clear();
+}
+
+void KernelTimer::destroy() {
+    reset();
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    pool.clear();
+}
+
 #define LWO_LAUNCH(expr)                                                                  \
     do {                                                                                  \
         hipError_t e_ = (expr);                                                           \
@@ -96,7 +143,7 @@ static GemmArgs gemm_args(const lwo_model_desc& d, const void* a, const void* w,
 }
 
 lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Workspace& ws, const void* cond,
-                         const void* ctx, hipStream_t st) {
+                         const void* ctx, hipStream_t st, KernelTimer* kt) {
     const int B = d.batch, T = d.tokens, D = d.hidden, F = d.ffn, H = d.heads, dh = D / H;
     const int M = B * T, Mc = B * d.ctx_tokens;
     const int act = d.act_dtype, ae = dtype_bytes(act);
@@ -115,81 +162,117 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
         g.w_seg = fused ? D : g.N;
         g.a_scale = a_scale;
     };
+    // Timing wrapper: events around one launch, attributed to the kernel symbol `name`.
+    auto timed = [&](const char* name, double flops, double bytes, auto&& launch) -> hipError_t {
+        if (!kt || !kt->on) return launch();
+        KernelTimer::Rec r{kt->cls(name), kt->get(), kt->get(), flops, bytes};
+        if (!r.a || !r.b) return hipErrorOutOfMemory;
+        hipError_t e = hipEventRecord(r.a, st);
+        if (e == hipSuccess) e = launch();
+        if (e == hipSuccess) e = hipEventRecord(r.b, st);
+        kt->pending.push_back(r);
+        return e;
+    };
+    const char* dtn = act == LWO_F32 ? "f32" : (fp8 ? "fp8" : "bf16");
+    auto gemm = [&](const GemmArgs& g) {
+        static const char* epn[] = {"store", "gelu", "gated", "resid"};
+        char name[48];
+        snprintf(name, sizeof(name), "gemm_%s_%s", dtn, epn[g.epi]);
+        const double ea = dtype_bytes(g.dtype), eo = g.epi <= EPI_GELU ? ae : 8.0;
+        const double bytes = (double)g.M * g.K * ea + (double)g.N * g.K * ea + (double)g.M * g.N * eo;
+        return timed(name, 2.0 * g.M * g.N * g.K, bytes, [&] { return launch_gemm(g, st); });
+    };
     auto attn = [&](const void* q, int ldq, const void* k, const void* v, int ldkv, int Tk) {
         AttnArgs a{};
         a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldkv; a.v = v; a.ldv = ldkv;
         a.o = ws.attn; a.ldo = D;
         a.B = B; a.H = H; a.Tq = T; a.Tk = Tk; a.dh = dh; a.dtype = act;
-        return launch_attention(a, st);
+        char name[48];
+        snprintf(name, sizeof(name), "attn_%s_d%d", act == LWO_F32 ? "f32" : "bf16", dh);
+        const double flops = 4.0 * B * H * (double)T * Tk * dh;
+        const double bytes = (double)B * ((double)T * D * 2 + 2.0 * Tk * D) * ae;
+        return timed(name, flops, bytes, [&] { return launch_attention(a, st); });
+    };
+    auto ln = [&](const float* m, int shc, int scc, void* out, int out_dt, float* osc) {
+        const double bytes = (double)M * D * (4 + dtype_bytes(out_dt)) + (m ? 2.0 * B * D * 4 : 0.0);
+        return timed(m ? "layernorm_mod" : "layernorm", 0.0, bytes,
+                     [&] { return launch_ln(ws.xr, M, D, T, m, shc, scc, out, out_dt, osc, st); });
+    };
+    auto quant = [&](const void* in, int rows, int n, uint8_t* codes, float* sc) {
+        return timed("quant_rows_fp8", 0.0, (double)rows * n * 3,
+                     [&] { return launch_quant_rows(in, rows, n, codes, sc, st); });
     };
 
     if (d.kind == LWO_KIND_DIT) {
-        LWO_LAUNCH(launch_mod_dit(cond, p.ada_w, p.ada_b, act, ws.mod, B, D, st));
-        LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 0, 1, ws.h, act, nullptr, st));
+        LWO_LAUNCH(timed("adaln_modulation", 2.0 * B * 6 * D * D, 6.0 * D * D * ae,
+                         [&] { return launch_mod_dit(cond, p.ada_w, p.ada_b, act, ws.mod, B, D, st); }));
+        LWO_LAUNCH(ln(mod, 0, 1, ws.h, act, nullptr));
         GemmArgs g = gemm_args(d, ws.h, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
         g.out = big; g.ldo = 3 * D;
-        LWO_LAUNCH(launch_gemm(g, st));
+        LWO_LAUNCH(gemm(g));
         LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
         g = gemm_args(d, ws.attn, p.o_w, M, D, D, EPI_GATED, p.o_b);
         g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
-        LWO_LAUNCH(launch_gemm(g, st));
-        LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 3, 4, ws.h, act, nullptr, st));
+        LWO_LAUNCH(gemm(g));
+        LWO_LAUNCH(ln(mod, 3, 4, ws.h, act, nullptr));
         g = gemm_args(d, ws.h, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
         g.out = big; g.ldo = F;
-        LWO_LAUNCH(launch_gemm(g, st));
+        LWO_LAUNCH(gemm(g));
         g = gemm_args(d, big, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
         g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
-        LWO_LAUNCH(launch_gemm(g, st));
+        LWO_LAUNCH(gemm(g));
         return LWO_OK;
     }
 
     // video kind
-    LWO_LAUNCH(launch_mod_video(cond, p.mod_table, act, ws.mod, B, D, st));
-    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 0, 1, h_buf, h_dt, ws.q8_scale, st));
+    LWO_LAUNCH(timed("modulation_add", 6.0 * B * D, 6.0 * B * D * (2 * ae + 4),
+                     [&] { return launch_mod_video(cond, p.mod_table, act, ws.mod, B, D, st); }));
+    LWO_LAUNCH(ln(mod, 0, 1, h_buf, h_dt, ws.q8_scale));
     GemmArgs g = gemm_args(d, h_buf, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
     g.out = big; g.ldo = 3 * D;
     fp8_in(g, 0, ws.q8_scale, true);
-    LWO_LAUNCH(launch_gemm(g, st));
-    LWO_LAUNCH(launch_rmsnorm_qk(big, act, M, D, p.q_norm, p.k_norm, st));
+    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(timed("rmsnorm_qk", 0.0, 4.0 * M * D * ae,
+                     [&] { return launch_rmsnorm_qk(big, act, M, D, p.q_norm, p.k_norm, st); }));
     LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
     const void* a_in = ws.attn;
-    if (fp8) { LWO_LAUNCH(launch_quant_rows(ws.attn, M, D, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    if (fp8) { LWO_LAUNCH(quant(ws.attn, M, D, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.o_w, M, D, D, EPI_GATED, p.o_b);
     g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
     fp8_in(g, 3, ws.q8_scale, false);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
 
     // cross-attention: ungated, plain LayerNorm on the queries, keys/values from the context
-    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, nullptr, 0, 0, h_buf, h_dt, ws.q8_scale, st));
+    LWO_LAUNCH(ln(nullptr, 0, 0, h_buf, h_dt, ws.q8_scale));
     g = gemm_args(d, h_buf, p.cq_w, M, D, D, EPI_STORE, p.cq_b);
     g.out = ws.cq; g.ldo = D;
     fp8_in(g, 4, ws.q8_scale, false);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
     g = gemm_args(d, fp8 ? (const void*)ws.ctx8 : ctx, p.ck_w, Mc, 2 * D, D, EPI_STORE, p.ckv_b);
     g.out = ws.ckv; g.ldo = 2 * D;
     fp8_in(g, 5, ws.ctx8_scale, true);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
     const char* ckv = (const char*)ws.ckv;
     LWO_LAUNCH(attn(ws.cq, D, ckv, ckv + (size_t)D * ae, 2 * D, d.ctx_tokens));
     a_in = ws.attn;
-    if (fp8) { LWO_LAUNCH(launch_quant_rows(ws.attn, M, D, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    if (fp8) { LWO_LAUNCH(quant(ws.attn, M, D, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.co_w, M, D, D, EPI_RESID, p.co_b);
     g.xr = ws.xr; g.ldx = D;
     fp8_in(g, 7, ws.q8_scale, false);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
 
     // FFN
-    LWO_LAUNCH(launch_ln(ws.xr, M, D, T, mod, 3, 4, h_buf, h_dt, ws.q8_scale, st));
+    LWO_LAUNCH(ln(mod, 3, 4, h_buf, h_dt, ws.q8_scale));
     g = gemm_args(d, h_buf, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
     g.out = big; g.ldo = F;
     fp8_in(g, 8, ws.q8_scale, false);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
     a_in = big;
-    if (fp8) { LWO_LAUNCH(launch_quant_rows(big, M, F, ws.q8, ws.q8_scale, st)); a_in = ws.q8; }
+    if (fp8) { LWO_LAUNCH(quant(big, M, F, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
     g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
     fp8_in(g, 9, ws.q8_scale, false);
-    LWO_LAUNCH(launch_gemm(g, st));
+    LWO_LAUNCH(gemm(g));
     return LWO_OK;
 }
 

@@ -99,9 +99,24 @@ struct Workspace {
 lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws);
 void workspace_free(Workspace* ws);
 
-// Enqueue one block's forward on `stream`.
+// Optional per-kernel timing: events around each launch, aggregated per kernel symbol.
+struct KernelTimer {
+    struct Rec { int cls; hipEvent_t a, b; double flops, bytes; };
+    struct Agg { std::string name; uint64_t launches = 0; double ms = 0, flops = 0, bytes = 0; };
+    bool on = false;
+    std::vector<Rec> pending;
+    std::vector<Agg> agg;
+    std::vector<hipEvent_t> pool;
+    hipEvent_t get();
+    int cls(const char* name);
+    lwo_status collect();   // synchronise pending events into agg
+    void reset();
+    void destroy();
+};
+
+// Enqueue one block's forward on `stream` (kt may be null).
 lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Workspace& ws,
-                         const void* cond, const void* ctx, hipStream_t stream);
+                         const void* cond, const void* ctx, hipStream_t stream, KernelTimer* kt);
 
 // Step prologue/epilogue: x (act dtype) -> fp32 residual, and back.
 lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* ctx,

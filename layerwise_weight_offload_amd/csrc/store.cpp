@@ -52,6 +52,7 @@ struct lwo_store {
     int n_timed = 0;
     uint64_t h2d_copies = 0, h2d_bytes = 0, steps = 0;
     double build_ms = 0;
+    KernelTimer kt;
     bool dead = false;
 };
 
@@ -141,6 +142,7 @@ static void release(lwo_store* s) {
     }
     for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
     if (s->resident) (void)hipFree(s->resident);
+    s->kt.destroy();
     workspace_free(&s->ws);
     if (s->copy) (void)hipStreamDestroy(s->copy);
     delete s;
@@ -333,7 +335,7 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
     LWO_TRY(enqueue_step_begin(d, s->ws, x, ctx, st));
     for (int b = 0; b < k; ++b) {
         const char* base = s->resident + ext * (uint64_t)b;
-        LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, base), s->ws, cond, ctx, st));
+        LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, base), s->ws, cond, ctx, st, &s->kt));
     }
     if (m > 0) {
         for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
@@ -367,7 +369,7 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
                 }
             }
             if (s->validation) LWO_TRY(validate_slot(s, s->slot[cur], j, st));
-            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st));
+            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st, &s->kt));
             LWO_HIP_TRY(hipEventRecord(s->compute_done[cur], st));
             cur = nxt;
         }
@@ -449,6 +451,37 @@ extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* 
     *host_sum = s->host_sums[block];
     *slot_sum = got;
     if (got != s->host_sums[block]) { set_error("slot checksum differs from the host extent"); return LWO_ECHECKSUM; }
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_set_kernel_timing(lwo_store* s, int32_t on) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_HIP_TRY(hipDeviceSynchronize());
+    s->kt.reset();
+    s->kt.on = on != 0;
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_kernel_stats(lwo_store* s, lwo_kernel_stat* out, int32_t cap, int32_t* n) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    LWO_HIP_TRY(hipSetDevice(s->device));
+    LWO_TRY(s->kt.collect());
+    const int cnt = (int)s->kt.agg.size();
+    if (n) *n = cnt;
+    if (!out && cap == 0) return LWO_OK;   // count query
+    if (cnt > cap || !out) { set_error("kernel_stats: capacity too small"); return LWO_EINVAL; }
+    for (int i = 0; i < cnt; ++i) {
+        const KernelTimer::Agg& a = s->kt.agg[i];
+        std::memset(&out[i], 0, sizeof(out[i]));
+        std::strncpy(out[i].name, a.name.c_str(), sizeof(out[i].name) - 1);
+        out[i].launches = a.launches;
+        out[i].total_ms = a.ms;
+        out[i].flops = a.flops;
+        out[i].bytes = a.bytes;
+    }
     return LWO_OK;
 }
 
