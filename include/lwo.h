@@ -274,6 +274,53 @@ lwo_status lwo_get_stats(lwo_store* store, lwo_stats* out);
  * mode the caller may unmap its extents once this returns. */
 lwo_status lwo_destroy_block_store(lwo_store* store);
 
+/* --- single kernels ------------------------------------------------------
+ * The kernels a denoise step enqueues, callable one at a time on `stream`
+ * (device pointers; nothing is synchronised).  They let a caller compose its
+ * own block or check one kernel at full size.  Arguments are validated
+ * before launch (LWO_EINVAL: null or misaligned pointer, a leading dimension
+ * smaller than the row, an unsupported size); device pointers must be
+ * 16-byte aligned and leading dimensions multiples of 8 elements. */
+
+/* Linear layer Y = A W^T + bias with a fused epilogue (the workload's
+ * Linear(out, in) with weight [N, K]):
+ *   epilogue 0: out[m, n] = Y               1: out[m, n] = GELU_tanh(Y)
+ *            2: xr[m, n] += gate[(m / rows_per_gate) * gate_ld + n] * Y
+ *            3: xr[m, n] += Y
+ * dtype F32: A, W, bias, out float32.  BF16: A, W, bias, out bf16.
+ * FP8_E4M3: A and W e4m3 codes, Y = (A W^T) * w_scale[n / w_seg] *
+ * a_scale[m] + bias with bias and out bf16.  xr and gate are float32.
+ * K must be a multiple of 16 (F32), 64 (BF16) or 128 (FP8); lda = K, ldw = K. */
+lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void* a, const float* a_scale, const void* w,
+                         const float* w_scale, int32_t w_seg, const void* bias, int32_t M, int32_t N, int32_t K,
+                         void* out, int32_t ldo, float* xr, int32_t ldx, const float* gate, int32_t gate_ld,
+                         int32_t rows_per_gate, void* stream);
+
+/* Softmax attention without a mask, per batch b and head h:
+ * O[b, t, h*d:(h+1)*d] = softmax(Q_bh K_bh^T / sqrt(d)) V_bh, rows of Q/O at
+ * b*Tq + t, rows of K/V at b*Tk + t, head h in columns [h*d, (h+1)*d).
+ * dtype F32 or BF16 for q, k, v, o; head_dim 64, 72 or 128. */
+lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq, const void* k, int32_t ldk, const void* v,
+                            int32_t ldv, void* o, int32_t ldo, int32_t batch, int32_t heads, int32_t tq,
+                            int32_t tk, int32_t head_dim, void* stream);
+
+/* Row LayerNorm (eps 1e-6, no affine) of float32 x [M, D] (row stride D);
+ * with mod ([B, 6, D] float32, b = row / rows_per_batch) the result is
+ * LN(x)(1 + mod[b, scale_chunk]) + mod[b, shift_chunk].  out_dtype F32/BF16
+ * writes out [M, D]; FP8_E4M3 writes e4m3 codes to out and per-row scales
+ * amax/448 to out_scale (codes = e4m3(y * 448 / amax), float32 arithmetic). */
+lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int32_t rows_per_batch, const float* mod,
+                            int32_t shift_chunk, int32_t scale_chunk, void* out, int32_t out_dtype,
+                            float* out_scale, void* stream);
+
+/* bf16 rows [M, N] -> e4m3 codes [M, N] and per-row scales (as above). */
+lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* codes, float* scales, void* stream);
+
+/* In place on rows of width 3D (q | k | v): q <- RMSNorm(q) * gq and
+ * k <- RMSNorm(k) * gk over the D features (eps 1e-6); dtype F32 or BF16. */
+lwo_status lwo_op_rmsnorm_qk(int32_t dtype, void* qkv, int32_t M, int32_t D, const void* gq, const void* gk,
+                             void* stream);
+
 /* Thread-local description of the last failure ("" if none). */
 const char* lwo_last_error(void);
 

@@ -92,16 +92,53 @@ _lib_set_kernel_timing = _sig("lwo_set_kernel_timing", C.c_int, _P, C.c_int32)
 _lib_kernel_stats = _sig("lwo_kernel_stats", C.c_int, _P, C.POINTER(_KStat), C.c_int32, C.POINTER(C.c_int32))
 _lib_destroy = _sig("lwo_destroy_block_store", C.c_int, _P)
 _lib_last_error = _sig("lwo_last_error", C.c_char_p)
+_I = C.c_int32
+_lib_op_linear = _sig("lwo_op_linear", C.c_int, _I, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _I, _P)
+_lib_op_attention = _sig("lwo_op_attention", C.c_int, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P)
+_lib_op_layernorm = _sig("lwo_op_layernorm", C.c_int, _P, _I, _I, _I, _P, _I, _I, _P, _I, _P, _P)
+_lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P, _P)
+_lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
             "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
-            "lwo_kernel_stats", "lwo_get_stats",
+            "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
+            "lwo_op_quantize_rows", "lwo_op_rmsnorm_qk",
             "lwo_destroy_block_store", "lwo_last_error"]
 
 
 def exported_symbols() -> list[str]:
     return list(EXPORTED)
+
+
+def _v(p):
+    return C.c_void_p(p) if p else None
+
+
+def op_linear(dtype, epilogue, a, w, M, N, K, stream, *, a_scale=0, w_scale=0, w_seg=0, bias=0, out=0, ldo=0,
+              xr=0, ldx=0, gate=0, gate_ld=0, rows_per_gate=0):
+    """All pointers are device addresses (ints); see lwo_op_linear."""
+    _check(_lib_op_linear(dtype, epilogue, _v(a), _v(a_scale), _v(w), _v(w_scale), w_seg, _v(bias), M, N, K,
+                          _v(out), ldo, _v(xr), ldx, _v(gate), gate_ld, rows_per_gate, _v(stream)))
+
+
+def op_attention(dtype, q, ldq, k, ldk, v, ldv, o, ldo, batch, heads, tq, tk, head_dim, stream):
+    _check(_lib_op_attention(dtype, _v(q), ldq, _v(k), ldk, _v(v), ldv, _v(o), ldo, batch, heads, tq, tk, head_dim,
+                             _v(stream)))
+
+
+def op_layernorm(x, M, D, out, out_dtype, stream, *, mod=0, rows_per_batch=1, shift_chunk=0, scale_chunk=0,
+                 out_scale=0):
+    _check(_lib_op_layernorm(_v(x), M, D, rows_per_batch, _v(mod), shift_chunk, scale_chunk, _v(out), out_dtype,
+                             _v(out_scale), _v(stream)))
+
+
+def op_quantize_rows(inp, M, N, codes, scales, stream):
+    _check(_lib_op_quantize_rows(_v(inp), M, N, _v(codes), _v(scales), _v(stream)))
+
+
+def op_rmsnorm_qk(dtype, qkv, M, D, gq, gk, stream):
+    _check(_lib_op_rmsnorm_qk(dtype, _v(qkv), M, D, _v(gq), _v(gk), _v(stream)))
 
 
 def last_error() -> str:

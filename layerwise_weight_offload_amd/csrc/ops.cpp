@@ -1,0 +1,108 @@
+// Single-kernel entry points of the C ABI: argument validation, then the
+// same launchers the denoise step uses.
+#include "kernels.h"
+#include "lwo_internal.h"
+
+using namespace lwo;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+lwo_status bad(const std::string& m) {
+    set_error(m);
+    return LWO_EINVAL;
+}
+
+lwo_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) {
+        set_error(std::string(what) + ": " + hipGetErrorString(e));
+        return LWO_EHIP;
+    }
+    return LWO_OK;
+}
+
+}  // namespace
+
+extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void* a, const float* a_scale,
+                                    const void* w, const float* w_scale, int32_t w_seg, const void* bias, int32_t M,
+                                    int32_t N, int32_t K, void* out, int32_t ldo, float* xr, int32_t ldx,
+                                    const float* gate, int32_t gate_ld, int32_t rows_per_gate, void* stream) {
+    clear_error();
+    if (dtype != LWO_F32 && dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) return bad("linear: dtype");
+    if (epilogue < EPI_STORE || epilogue > EPI_RESID) return bad("linear: epilogue");
+    if (M < 0 || N < 1 || K < 1) return bad("linear: sizes");
+    const int kq = dtype == LWO_F32 ? 16 : (dtype == LWO_BF16 ? 64 : 128);
+    if (K % kq) return bad("linear: K must be a multiple of " + std::to_string(kq));
+    if (N % 8) return bad("linear: N must be a multiple of 8");
+    if (!a || !w || !aligned16(a) || !aligned16(w)) return bad("linear: a and w must be 16-byte aligned device pointers");
+    if (bias && ((uintptr_t)bias & 3u)) return bad("linear: bias alignment");
+    if (dtype == LWO_FP8_E4M3 && (!a_scale || !w_scale || w_seg < 1)) return bad("linear: fp8 needs a_scale, w_scale and w_seg");
+    if (epilogue <= EPI_GELU) {
+        if (!out || ldo < N) return bad("linear: out and ldo >= N required");
+    } else {
+        if (!xr || ldx < N) return bad("linear: xr and ldx >= N required");
+        if (epilogue == EPI_GATED && (!gate || gate_ld < N || rows_per_gate < 1)) return bad("linear: gate, gate_ld >= N and rows_per_gate required");
+    }
+    if (!stream) return bad("linear: stream is NULL");
+    GemmArgs g{};
+    g.a = a; g.w = w; g.M = M; g.N = N; g.K = K; g.dtype = dtype;
+    g.act_dtype = dtype == LWO_F32 ? LWO_F32 : LWO_BF16;
+    g.epi = epilogue; g.bias = bias; g.out = out; g.ldo = ldo; g.xr = xr; g.ldx = ldx;
+    g.gate = gate; g.gate_ld = gate_ld; g.rows_per_batch = rows_per_gate > 0 ? rows_per_gate : 1;
+    g.w_scale = w_scale; g.w_seg = w_seg > 0 ? w_seg : 1; g.a_scale = a_scale;
+    return launched(launch_gemm(g, (hipStream_t)stream), "linear");
+}
+
+extern "C" lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq, const void* k, int32_t ldk,
+                                       const void* v, int32_t ldv, void* o, int32_t ldo, int32_t batch, int32_t heads,
+                                       int32_t tq, int32_t tk, int32_t head_dim, void* stream) {
+    clear_error();
+    if (dtype != LWO_F32 && dtype != LWO_BF16) return bad("attention: dtype must be F32 or BF16");
+    if (head_dim != 64 && head_dim != 72 && head_dim != 128) return bad("attention: head_dim must be 64, 72 or 128");
+    if (batch < 1 || heads < 1 || tq < 0 || tk < 1) return bad("attention: sizes");
+    const int D = heads * head_dim;
+    if (ldq < D || ldk < D || ldv < D || ldo < D) return bad("attention: leading dimensions must cover heads*head_dim");
+    if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8) return bad("attention: leading dimensions must be multiples of 8");
+    if (!q || !k || !v || !o || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return bad("attention: pointers must be 16-byte aligned device pointers");
+    if (!stream) return bad("attention: stream is NULL");
+    AttnArgs a{};
+    a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv; a.o = o; a.ldo = ldo;
+    a.B = batch; a.H = heads; a.Tq = tq; a.Tk = tk; a.dh = head_dim; a.dtype = dtype;
+    return launched(launch_attention(a, (hipStream_t)stream), "attention");
+}
+
+extern "C" lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int32_t rows_per_batch, const float* mod,
+                                       int32_t shift_chunk, int32_t scale_chunk, void* out, int32_t out_dtype,
+                                       float* out_scale, void* stream) {
+    clear_error();
+    if (M < 0 || D < 4 || D % 4 || D > 8192) return bad("layernorm: D must be a multiple of 4 and at most 8192");
+    if (out_dtype != LWO_F32 && out_dtype != LWO_BF16 && out_dtype != LWO_FP8_E4M3) return bad("layernorm: out_dtype");
+    if (!x || !out || !aligned16(x) || !aligned16(out)) return bad("layernorm: x and out must be 16-byte aligned");
+    if (mod && (rows_per_batch < 1 || shift_chunk < 0 || shift_chunk > 5 || scale_chunk < 0 || scale_chunk > 5 || !aligned16(mod)))
+        return bad("layernorm: modulation arguments");
+    if (out_dtype == LWO_FP8_E4M3 && !out_scale) return bad("layernorm: fp8 output needs out_scale");
+    if (!stream) return bad("layernorm: stream is NULL");
+    return launched(launch_ln(x, M, D, rows_per_batch > 0 ? rows_per_batch : 1, mod, shift_chunk, scale_chunk, out,
+                              out_dtype, out_scale, (hipStream_t)stream), "layernorm");
+}
+
+extern "C" lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* codes, float* scales,
+                                           void* stream) {
+    clear_error();
+    if (M < 0 || N < 8 || N % 8) return bad("quantize_rows: N must be a positive multiple of 8");
+    if (!in || !codes || !scales || !aligned16(in) || ((uintptr_t)codes & 7u)) return bad("quantize_rows: pointers");
+    if (!stream) return bad("quantize_rows: stream is NULL");
+    return launched(launch_quant_rows(in, M, N, codes, scales, (hipStream_t)stream), "quantize_rows");
+}
+
+extern "C" lwo_status lwo_op_rmsnorm_qk(int32_t dtype, void* qkv, int32_t M, int32_t D, const void* gq, const void* gk,
+                                        void* stream) {
+    clear_error();
+    if (dtype != LWO_F32 && dtype != LWO_BF16) return bad("rmsnorm_qk: dtype");
+    if (M < 0 || D < 4 || D % 4 || D > 8192) return bad("rmsnorm_qk: D must be a multiple of 4 and at most 8192");
+    if (!qkv || !gq || !gk || !aligned16(qkv) || !aligned16(gq) || !aligned16(gk)) return bad("rmsnorm_qk: pointers");
+    if (!stream) return bad("rmsnorm_qk: stream is NULL");
+    return launched(launch_rmsnorm_qk(qkv, dtype, M, D, gq, gk, (hipStream_t)stream), "rmsnorm_qk");
+}

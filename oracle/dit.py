@@ -129,7 +129,19 @@ def dit_block(x: np.ndarray, cond: np.ndarray, p: dict, heads: int) -> np.ndarra
     return x
 
 
-def video_block(x: np.ndarray, cond: np.ndarray, ctx: np.ndarray, p: dict, heads: int) -> np.ndarray:
+def fp8_activation(z: np.ndarray, stored_bf16: bool) -> np.ndarray:
+    """Emulate the input of an fp8 linear: the activation (rounded to bf16
+    first when it is stored in bf16 before quantisation) is quantised per row
+    to e4m3 with scale amax/448 in float32 and dequantised exactly."""
+    z32 = z.astype(np.float32)
+    if stored_bf16:
+        z32 = codecs.bf16_round(z32).astype(np.float32)
+    q, s = codecs.quantize_rows_e4m3(z32)
+    return codecs.e4m3_decode(q) * s.astype(np.float64)[..., None]
+
+
+def video_block(x: np.ndarray, cond: np.ndarray, ctx: np.ndarray, p: dict, heads: int,
+                fp8_act: bool = False) -> np.ndarray:
     """Video DiT block.
 
     m = cond + M_blk (cond [B,6,D], the block's own [6,D] table); same chunk
@@ -138,30 +150,35 @@ def video_block(x: np.ndarray, cond: np.ndarray, ctx: np.ndarray, p: dict, heads
     q = RMS_gq(Lin_q(h)), k = RMS_gk(Lin_k(h)) over the full hidden width,
     v = Lin_v(h);  x = x + gate1 * Lin_o(Attn(q, k, v));
     x = x + Lin_co(Attn(Lin_cq(LN(x)), Lin_ck(ctx), Lin_cv(ctx)))  (ungated);
-    h = LN(x)(1 + scale2) + shift2;  x = x + gate2 * Lin_fc2(GELU(Lin_fc1(h)))."""
+    h = LN(x)(1 + scale2) + shift2;  x = x + gate2 * Lin_fc2(GELU(Lin_fc1(h))).
+
+    fp8_act=True additionally quantises the input of every linear per row to
+    e4m3 (the approximation an fp8 GEMM makes; see fp8_activation)."""
     B, T, D = x.shape
+    qa = (lambda z, stored_bf16=False: fp8_activation(z, stored_bf16)) if fp8_act else (lambda z, stored_bf16=False: z)
     m = cond + p["mod.table"][None, :, :]
     sh1, sc1, g1, sh2, sc2, g2 = chunks6(m)
-    h = layer_norm(x) * (1.0 + sc1) + sh1
+    h = qa(layer_norm(x) * (1.0 + sc1) + sh1)
     bq, bk, bv = p["attn.qkv.b"][:D], p["attn.qkv.b"][D:2 * D], p["attn.qkv.b"][2 * D:]
     q = rms_norm(linear(h, p["attn.q.w"], bq), p["attn.q.norm"])
     k = rms_norm(linear(h, p["attn.k.w"], bk), p["attn.k.norm"])
     v = linear(h, p["attn.v.w"], bv)
-    x = x + g1 * linear(attention(q, k, v, heads), p["attn.o.w"], p["attn.o.b"])
-    cq = linear(layer_norm(x), p["cross.q.w"], p["cross.q.b"])
+    x = x + g1 * linear(qa(attention(q, k, v, heads), True), p["attn.o.w"], p["attn.o.b"])
+    cq = linear(qa(layer_norm(x)), p["cross.q.w"], p["cross.q.b"])
     bck, bcv = p["cross.kv.b"][:D], p["cross.kv.b"][D:]
-    ck = linear(ctx, p["cross.k.w"], bck)
-    cv = linear(ctx, p["cross.v.w"], bcv)
-    x = x + linear(attention(cq, ck, cv, heads), p["cross.o.w"], p["cross.o.b"])
-    h = layer_norm(x) * (1.0 + sc2) + sh2
-    x = x + g2 * linear(gelu_tanh(linear(h, p["ffn.fc1.w"], p["ffn.fc1.b"])), p["ffn.fc2.w"], p["ffn.fc2.b"])
+    ctx_in = qa(ctx, True)
+    ck = linear(ctx_in, p["cross.k.w"], bck)
+    cv = linear(ctx_in, p["cross.v.w"], bcv)
+    x = x + linear(qa(attention(cq, ck, cv, heads), True), p["cross.o.w"], p["cross.o.b"])
+    h = qa(layer_norm(x) * (1.0 + sc2) + sh2)
+    x = x + g2 * linear(qa(gelu_tanh(linear(h, p["ffn.fc1.w"], p["ffn.fc1.b"])), True), p["ffn.fc2.w"], p["ffn.fc2.b"])
     return x
 
 
-def block_forward(w, x, cond, ctx, params: dict) -> np.ndarray:
+def block_forward(w, x, cond, ctx, params: dict, fp8_act: bool = False) -> np.ndarray:
     if w.kind == "dit":
         return dit_block(x, cond, params, w.heads)
-    return video_block(x, cond, ctx, params, w.heads)
+    return video_block(x, cond, ctx, params, w.heads, fp8_act=fp8_act)
 
 
 # ------------------------------------------------------------------ stack
@@ -177,7 +194,7 @@ def decode_inputs(w, x, cond, ctx):
     return dec(x), dec(cond), dec(ctx)
 
 
-def stack_forward(w, extents, x, cond, ctx, blocks=None) -> np.ndarray:
+def stack_forward(w, extents, x, cond, ctx, blocks=None, fp8_act: bool = False) -> np.ndarray:
     """Apply blocks (default: all) in order to float64 inputs.
 
     ``extents`` is a sequence (or callable b -> bytes) giving each block's
@@ -187,7 +204,7 @@ def stack_forward(w, extents, x, cond, ctx, blocks=None) -> np.ndarray:
     for b in blocks:
         ext = extents(b) if callable(extents) else extents[b]
         params = layout.unpack_block(w, ext)
-        x = block_forward(w, x, cond, ctx, params)
+        x = block_forward(w, x, cond, ctx, params, fp8_act=fp8_act)
     return x
 
 
