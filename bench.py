@@ -55,8 +55,24 @@ def pinned_peak(torch, nbytes: int, stream, reps: int = 10) -> float:
     return best
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle (float64, every weight resident) on a bounded sample of blocks."""
+def block_flops(w) -> float:
+    """Algorithmic FLOPs of one block: 2MNK per linear, 4 B H Tq Tk d per attention."""
+    B, T, D, F, Tc = w.batch, w.tokens, w.hidden, w.ffn, w.ctx_tokens
+    M = B * T
+    gemm = 2.0 * M * D * (3 * D + D + 2 * F)
+    attn = 4.0 * B * T * T * D
+    if w.kind == "video":
+        gemm += 2.0 * M * D * (2 * D) + 2.0 * B * Tc * D * 2 * D
+        attn += 4.0 * B * T * Tc * D
+    else:
+        gemm += 2.0 * B * D * 6 * D
+    return gemm + attn
+
+
+def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12):
+    """The oracle (float64, every weight resident) on a bounded sample: whole
+    blocks of the step while the time budget lasts; for a block above
+    max_block_flops, one block at fewer tokens, scaled by the FLOP ratio."""
     import numpy as np
     import lwo_synth
     from oracle import dit as o_dit
@@ -66,19 +82,30 @@ def cpu_baseline(w, seconds: float):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:
         cores = os.cpu_count() or 1
-    x, cond, ctx = o_dit.decode_inputs(w, *lwo_synth.step_inputs(w))
+    scale, note = 1.0, ""
+    if block_flops(w) > max_block_flops:
+        t_sub = 2048
+        ws = w.with_(tokens=t_sub)
+        scale = block_flops(w) / block_flops(ws)
+        note = (f"; one block at {t_sub} of {w.tokens} tokens, scaled by the algorithmic FLOP ratio "
+                f"{scale:.1f} (an extrapolation)")
+        w_run = ws
+    else:
+        w_run = w
+    x, cond, ctx = o_dit.decode_inputs(w_run, *lwo_synth.step_inputs(w_run))
     done, spent = 0, 0.0
-    while done < w.n_blocks and (done == 0 or spent < seconds):
-        ext = o_layout.pack_block(w, lwo_synth.block_tensors(w, done))   # packing is not timed
+    while done < w.n_blocks and (done == 0 or (spent < seconds and scale == 1.0)):
+        ext = o_layout.pack_block(w_run, lwo_synth.block_tensors(w_run, done))   # packing is not timed
         t0 = time.perf_counter()
-        x = o_dit.stack_forward(w, [ext], x, cond, ctx, blocks=[0])
+        x = o_dit.stack_forward(w_run, [ext], x, cond, ctx, blocks=[0])
         spent += time.perf_counter() - t0
         done += 1
         log(f"oracle block {done}: {spent:.1f} s so far")
-    per_block_ms = spent / done * 1e3
+    per_block_ms = spent / done * 1e3 * scale
     return {"value": round(per_block_ms * w.n_blocks, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {w.n_blocks} blocks of one step timed ({spent:.1f} s), "
-                      f"per-block time x {w.n_blocks}; float64 NumPy, weights decoded from the packed extents"}
+                      f"per-block time x {w.n_blocks}; float64 NumPy, weights decoded from the packed extents"
+                      + note}
 
 
 def main() -> int:
@@ -119,6 +146,8 @@ def main() -> int:
         bb, t = next(blocks)
         assert bb == b
         lwo.pack_block(desc, t, dst=dst, dst_bytes=n)
+        if b % 8 == 7 or b == L - 1:
+            log(f"packed block {b + 1}/{L}")
 
     t0 = time.perf_counter()
     store = lwo.build_block_store(desc, fill=fill)

@@ -225,9 +225,19 @@ lwo_status lwo_set_resident_prefix(lwo_store* store, int32_t k);
  * streamed block it stays in its slot and nothing is copied.  The last
  * prefetch stays in flight across calls.  Caller keeps x, cond, ctx valid
  * until the stream drains.  Device faults surface as LWO_EHIP at a later
- * synchronising call. */
+ * synchronising call.
+ * Pacing: before enqueuing, the call waits on the host until at most
+ * max_inflight - 1 earlier steps of this store are still executing (default
+ * max_inflight 1: the previous step has finished).  The next step's first
+ * block is already in its slot (the circular prefetch), so the device does
+ * not idle; unbounded host run-ahead measured slower on MI355X (queued
+ * cross-stream waits stall the copy engine). */
 lwo_status lwo_run_denoise_step(lwo_store* store, void* x, const void* cond, const void* ctx,
                                 void* hip_stream);
+
+/* Set the pacing depth of lwo_run_denoise_step (1..16, or 0 for no host
+ * wait at all). */
+lwo_status lwo_set_max_inflight(lwo_store* store, int32_t max_inflight);
 
 /* Validation mode (on != 0): before each streamed block the compute stream
  * checksums the slot on the device and compares it with the host extent's

@@ -84,6 +84,7 @@ _lib_build = _sig("lwo_build_block_store", C.c_int, C.POINTER(_Desc), C.POINTER(
 _lib_set_prefix = _sig("lwo_set_resident_prefix", C.c_int, _P, C.c_int32)
 _lib_run = _sig("lwo_run_denoise_step", C.c_int, _P, _P, _P, _P, _P)
 _lib_set_validation = _sig("lwo_set_validation", C.c_int, _P, C.c_int32)
+_lib_set_max_inflight = _sig("lwo_set_max_inflight", C.c_int, _P, C.c_int32)
 _lib_block_checksum = _sig("lwo_block_checksum", C.c_int, _P, C.c_int32, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64))
 _lib_set_copy_timing = _sig("lwo_set_copy_timing", C.c_int, _P, C.c_int32)
 _lib_copy_times = _sig("lwo_copy_times", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32))
@@ -100,7 +101,8 @@ _lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P
 _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
-            "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_validation",
+            "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
+            "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
             "lwo_op_quantize_rows", "lwo_op_rmsnorm_qk",
@@ -274,6 +276,10 @@ class Store:
         """x, cond, ctx: device addresses; stream: hipStream_t as an integer."""
         _check(_lib_run(self._live(), C.c_void_p(x), C.c_void_p(cond), C.c_void_p(ctx) if ctx else None,
                         C.c_void_p(stream)))
+
+    def set_max_inflight(self, n: int) -> None:
+        """Pacing depth of run_denoise_step (0: never wait on the host)."""
+        _check(_lib_set_max_inflight(self._live(), n))
 
     def set_validation(self, on: bool) -> None:
         _check(_lib_set_validation(self._live(), 1 if on else 0))

@@ -53,6 +53,8 @@ struct lwo_store {
     uint64_t h2d_copies = 0, h2d_bytes = 0, steps = 0;
     double build_ms = 0;
     KernelTimer kt;
+    int max_inflight = 1;                 // pacing depth of run (0: no host wait)
+    hipEvent_t step_done[16] = {};        // completion of recent steps, ring indexed by step number
     bool dead = false;
 };
 
@@ -141,6 +143,8 @@ static void release(lwo_store* s) {
         if (s->compute_done[i]) (void)hipEventDestroy(s->compute_done[i]);
     }
     for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
+    for (hipEvent_t e : s->step_done)
+        if (e) (void)hipEventDestroy(e);
     if (s->resident) (void)hipFree(s->resident);
     s->kt.destroy();
     workspace_free(&s->ws);
@@ -240,6 +244,7 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
     }
     LWO_TRY(workspace_alloc(s->d, &s->ws));
     LWO_HIP_TRY(hipStreamCreateWithFlags(&s->copy, hipStreamNonBlocking));
+    for (hipEvent_t& e : s->step_done) LWO_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     LWO_TRY(prime_head(s));
     LWO_HIP_TRY(hipStreamSynchronize(s->copy));
     return LWO_OK;
@@ -343,8 +348,15 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
         s->n_timed = 0;
         int cur = s->head_slot;
         for (int j = k; j < n; ++j) {
+            if (s->slot_block[cur] != j) { set_error("ring state corrupted"); return LWO_ESTATE; }
             // RAW: the block's bytes must have landed before its kernels read them.
             LWO_HIP_TRY(hipStreamWaitEvent(st, s->copy_done[cur], 0));
+            if (s->validation) LWO_TRY(validate_slot(s, s->slot[cur], j, st));
+            // The block's kernels go in before the prefetch call: the runtime may
+            // block the host inside hipMemcpyAsync when many copies are queued,
+            // and the compute queue must not starve meanwhile.
+            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st, &s->kt));
+            LWO_HIP_TRY(hipEventRecord(s->compute_done[cur], st));
             int nxt = cur;
             if (m > 1) {
                 const int nb = (j + 1 < n) ? j + 1 : k;   // circular: the last block prefetches block k
@@ -368,14 +380,12 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
                     s->h2d_bytes += ext;
                 }
             }
-            if (s->validation) LWO_TRY(validate_slot(s, s->slot[cur], j, st));
-            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st, &s->kt));
-            LWO_HIP_TRY(hipEventRecord(s->compute_done[cur], st));
             cur = nxt;
         }
         s->head_slot = cur;   // the slot holding (or receiving) block k for the next step
     }
     LWO_TRY(enqueue_step_end(d, s->ws, x, st));
+    LWO_HIP_TRY(hipEventRecord(s->step_done[s->steps % 16], st));
     s->steps++;
     return LWO_OK;
 }
@@ -388,12 +398,22 @@ extern "C" lwo_status lwo_run_denoise_step(lwo_store* s, void* x, const void* co
     if (s->d.kind == LWO_KIND_VIDEO && !ctx) { set_error("video kind needs ctx"); return LWO_EINVAL; }
     if (s->d.kind == LWO_KIND_DIT && ctx) { set_error("DiT kind takes no ctx"); return LWO_EINVAL; }
     LWO_HIP_TRY(hipSetDevice(s->device));
+    if (s->max_inflight > 0 && s->steps >= (uint64_t)s->max_inflight)   // pacing: bound host run-ahead
+        LWO_HIP_TRY(hipEventSynchronize(s->step_done[(s->steps - s->max_inflight) % 16]));
     lwo_status st = run_step(s, x, cond, ctx, (hipStream_t)hip_stream);
     if (st != LWO_OK) s->dead = true;   // the ring's events no longer describe the slots
     return st;
 }
 
 // ------------------------------------------------------------------ validation and stats
+
+extern "C" lwo_status lwo_set_max_inflight(lwo_store* s, int32_t max_inflight) {
+    clear_error();
+    LWO_TRY(check_store(s));
+    if (max_inflight < 0 || max_inflight > 16) { set_error("max_inflight must be 0..16"); return LWO_EINVAL; }
+    s->max_inflight = max_inflight;
+    return LWO_OK;
+}
 
 extern "C" lwo_status lwo_set_validation(lwo_store* s, int32_t on) {
     clear_error();

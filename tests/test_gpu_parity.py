@@ -164,3 +164,20 @@ def test_fp8_video(lib):
     print(f"[parity] fp8: rel_l2(out, plain)={e_plain:.3e} update vs plain={e_plain_upd:.3e} "
           f"update vs emulated={e_emul:.3e}", flush=True)
     assert e_plain <= 5e-2 and e_emul <= 4e-2 and e_emul < e_plain_upd
+
+
+def test_pacing_depth_does_not_change_results(lib):
+    """Host pacing only changes when steps are enqueued, never what they compute."""
+    w = lwo_synth.get("video_t_bf16")
+    import torch
+    outs = []
+    for depth in (1, 0, 3):
+        with make_store(lib, w) as st:
+            st.set_max_inflight(depth)
+            x, cond, ctx = device_inputs(w)
+            run_steps(st, x, cond, ctx, steps=4)
+            outs.append(x.cpu().view(torch.int16).numpy().copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    with make_store(lib, w) as st:
+        with pytest.raises(lib.LwoError):
+            st.set_max_inflight(17)
