@@ -1,18 +1,21 @@
 // Linear layers of the DiT block, Y = A W^T with a fused epilogue (bias,
 // GELU-tanh, gated or plain residual add into the fp32 residual stream).
 //
-// * k_gemm_mfma: bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
-//   (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) operands,
-//   fp32 accumulation.  Both operands are K-contiguous ([M,K] activations,
-//   [N,K] weights), so each lane's MFMA fragment is one or two 16-byte LDS
-//   reads from a row.  Tiles are 128x128 outputs per 256-thread workgroup
-//   (2x2 wavefronts of 64x64 each, i.e. 2x2 MFMA 32x32 blocks), 128 bytes of
-//   K per stage (64 bf16 or 128 fp8 elements), LDS double-buffered with a
-//   16-byte row pad so that the 16 lanes of one LDS access phase hit
-//   distinct banks.  No split-K: every output is produced by one lane in a
-//   fixed order, so results are deterministic run to run.
+// Both kernels below take bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) operands and
+// accumulate in fp32.  Both operands are K-contiguous ([M,K] activations,
+// [N,K] weights), so each lane's MFMA fragment is one or two 16-byte LDS
+// reads from a row.  No split-K: every output is produced by one lane in a
+// fixed order, so results are deterministic run to run.
+// * k_gemm_deep: large products; 256x256 tiles, direct-to-LDS loads three
+//   stages ahead, LDS-staged vector epilogue (details at the kernel).
+// * k_gemm_mfma: everything else; 128x128 tiles (2x2 wavefronts of 64x64),
+//   128 bytes of K per stage, register-staged double-buffered LDS with a
+//   16-byte row pad.
 // * k_gemm_f32: fp32 FMA tiles (64x64, 4x4 per thread) for the fp32
 //   workloads, where bf16 rounding would exceed a 1e-4 tolerance.
+#include <type_traits>
+
 #include "../../include/lwo.h"
 #include "kcommon.h"
 #include "kernels.h"
@@ -81,48 +84,89 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 
 // ------------------------------------------------------------------ MFMA tiles (bf16 / fp8)
 
-constexpr int kBM = 128, kBN = 128, kBKB = 128;    // tile rows, tile cols, K bytes per stage
-constexpr int kRowB = kBKB + 16;                    // LDS row stride in bytes (16-byte pad)
+constexpr int kBKB = 128;             // K bytes per LDS stage: 64 bf16 or 128 fp8 elements
+constexpr int kRowB = kBKB + 16;      // LDS row stride in bytes (16-byte pad)
 
-template <bool FP8, int EPI>
+// Tile index -> (tile row, tile col).  Workgroups are handed to the 8 XCDs
+// round-robin, so consecutive ids land on different L2s; the remap gives each
+// XCD a contiguous run of tiles, and inside that run tiles go in groups of
+// kGroupM tile rows (column-major within a group) so that the A rows and the
+// W columns a group touches stay in that XCD's L2.
+constexpr int kXcds = 8, kGroupM = 8;
+
+__device__ __forceinline__ void tile_of(int pid, int nt_m, int nt_n, int& tm, int& tn) {
+    const int total = nt_m * nt_n;
+    const int x = pid % kXcds, idx = pid / kXcds;
+    const int base = total / kXcds, rem = total % kXcds;
+    const int t = x * base + min(x, rem) + idx;      // bijection of [0, total)
+    const int per_group = kGroupM * nt_n;
+    const int g = t / per_group, first_m = g * kGroupM;
+    const int gsz = min(nt_m - first_m, kGroupM);
+    const int r = t % per_group;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+}
+
+// BM x BN output tile per 256-thread workgroup: 2x2 wavefronts, each owning
+// (BM/2) x (BN/2) = TM x TN MFMA 32x32 blocks.
+template <int BM, int BN, bool FP8, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char As[2][kBM * kRowB];
-    __shared__ __attribute__((aligned(16))) unsigned char Ws[2][kBN * kRowB];
+    constexpr int TM = BM / 64, TN = BN / 64;        // MFMA blocks per wavefront along M and N
+    constexpr int LA = BM / 32, LW = BN / 32;        // 16-byte global loads per thread per stage
+    constexpr int KS = FP8 ? 2 : 4;                  // MFMA k-steps per stage
+    __shared__ __attribute__((aligned(16))) unsigned char As[2][BM * kRowB];
+    __shared__ __attribute__((aligned(16))) unsigned char Ws[2][BN * kRowB];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / 2, wn = wave % 2, l32 = lane % 32, half = lane / 32;
-    const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+    int tmi, tni;
+    tile_of(blockIdx.x, (g.M + BM - 1) / BM, (g.N + BN - 1) / BN, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
     const int esz = FP8 ? 1 : 2;
     const size_t rowA = (size_t)g.K * esz;          // bytes per row of A and W
     const unsigned char* A = (const unsigned char*)g.a;
     const unsigned char* W = (const unsigned char*)g.w;
     const int ch = tid % 8;                          // 16-byte chunk within the 128-byte stage row
-    intx4 ra[4], rw[4];
+    intx4 ra[LA], rw[LW];
     const intx4 z = {0, 0, 0, 0};
 
     auto gload = [&](int kb) {   // kb: byte offset along K
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < LA; ++i) {
             const int r = tid / 8 + 32 * i;
             ra[i] = (m0 + r < g.M) ? *(const intx4*)(A + (size_t)(m0 + r) * rowA + kb + ch * 16) : z;
+        }
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const int r = tid / 8 + 32 * i;
             rw[i] = (n0 + r < g.N) ? *(const intx4*)(W + (size_t)(n0 + r) * rowA + kb + ch * 16) : z;
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tid / 8 + 32 * i;
-            *(intx4*)&As[buf][r * kRowB + ch * 16] = ra[i];
-            *(intx4*)&Ws[buf][r * kRowB + ch * 16] = rw[i];
-        }
+        for (int i = 0; i < LA; ++i) *(intx4*)&As[buf][(tid / 8 + 32 * i) * kRowB + ch * 16] = ra[i];
+#pragma unroll
+        for (int i = 0; i < LW; ++i) *(intx4*)&Ws[buf][(tid / 8 + 32 * i) * kRowB + ch * 16] = rw[i];
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Fragment of k-step ks: bf16 = one 16-byte read (8 elements), fp8 = two (32 elements).
+    typedef typename std::conditional<FP8, intx8, bf16x8>::type frag_t;
+    auto frag = [&](const unsigned char* base, int row, int ks) -> frag_t {
+        if constexpr (FP8) {
+            const unsigned char* p = base + row * kRowB + ks * 64 + half * 32;
+            const intx4 lo = *(const intx4*)p, hi = *(const intx4*)(p + 16);
+            return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            return __builtin_bit_cast(bf16x8, *(const intx4*)(base + row * kRowB + ks * 32 + half * 16));
+        }
+    };
 
     const int nk = (int)(rowA / kBKB);
     gload(0);
@@ -133,45 +177,30 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
         if (kt + 1 < nk) gload((kt + 1) * kBKB);
         const unsigned char* as = As[buf];
         const unsigned char* ws = Ws[buf];
-        if (!FP8) {
+        frag_t af[2][TM], bfr[2][TN];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {          // 16 bf16 of K per MFMA
-                bf16x8 af[2], bfr[2];
+        for (int i = 0; i < TM; ++i) af[0][i] = frag(as, wm * (BM / 2) + i * 32 + l32, 0);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    af[i] = __builtin_bit_cast(bf16x8, *(const intx4*)&as[(wm * 64 + i * 32 + l32) * kRowB + ks * 32 + half * 16]);
+        for (int j = 0; j < TN; ++j) bfr[0][j] = frag(ws, wn * (BN / 2) + j * 32 + l32, 0);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    bfr[j] = __builtin_bit_cast(bf16x8, *(const intx4*)&ws[(wn * 64 + j * 32 + l32) * kRowB + ks * 32 + half * 16]);
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cb = ks & 1, nb = cb ^ 1;
+            if (ks + 1 < KS) {   // read the next k-step's fragments while this one multiplies
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < TM; ++i) af[nb][i] = frag(as, wm * (BM / 2) + i * 32 + l32, ks + 1);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TN; ++j) bfr[nb][j] = frag(ws, wn * (BN / 2) + j * 32 + l32, ks + 1);
             }
-        } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {          // 64 fp8 of K per MFMA
-                intx8 af[2], bfr[2];
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const unsigned char* p = &as[(wm * 64 + i * 32 + l32) * kRowB + ks * 64 + half * 32];
-                    intx4 lo = *(const intx4*)p, hi = *(const intx4*)(p + 16);
-                    af[i] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const unsigned char* p = &ws[(wn * 64 + j * 32 + l32) * kRowB + ks * 64 + half * 32];
-                    intx4 lo = *(const intx4*)p, hi = *(const intx4*)(p + 16);
-                    bfr[j] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)   // formats 0/0: e4m3 x e4m3; scale exponents 127 = 2^0
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j],
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (FP8)   // formats 0/0: e4m3 x e4m3; scale exponents 127 = 2^0
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[cb][i], bfr[cb][j], acc[i][j],
                                                                                     0, 0, 0, 127, 0, 127);
-            }
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+                }
         }
         if (kt + 1 < nk) lstore(buf ^ 1);
         __syncthreads();
@@ -180,16 +209,16 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
     // Accumulator layout of a 32x32 MFMA block: register r of lane l holds
     // row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * (BN / 2) + j * 32 + l32;
             if (n >= g.N) continue;
             float wsc = 1.0f;
             if (FP8) wsc = g.w_scale[n / g.w_seg];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                 if (m < g.M) {
                     float v = acc[i][j][r];
                     if (FP8) v = v * wsc * g.a_scale[m];
@@ -199,17 +228,285 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
         }
 }
 
+// ------------------------------------------------------------------ 256x256 tiles, deep prefetch
+
+// Large shapes.  256x256 outputs per workgroup (2x2 wavefronts of 128x128 =
+// 4x4 MFMA blocks each).  K advances in 64-byte stages (32 bf16 or 64 fp8
+// elements) held in four LDS buffers; each stage is fetched with
+// global_load_lds three stages ahead of its use, so about three stages of
+// MFMA work cover the load latency.  The wait before a stage is
+// `s_waitcnt vmcnt(16)` (this wavefront's loads for the two later stages may
+// still be in flight) followed by a plain s_barrier: the workgroup barrier
+// of the language would also drain those later loads.  LDS rows are 64 bytes
+// (four 16-byte chunks); chunk c of row r sits at c ^ f(r) with
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3, which puts the rows one fragment read
+// touches on distinct banks for 32- and 64-bank LDS alike.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// 16-byte LDS read issued as an instruction the compiler does not track: its
+// completion is awaited explicitly (lds_wait), so the compiler's own waits,
+// which cannot tell the buffers in flight from the one being read, stay out
+// of the loop.  The low 32 bits of a generic LDS address are the LDS offset.
+__device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
+    intx4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p));
+    return v;
+}
+
+template <bool FP8, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, TM = 4, TN = 4;
+    constexpr int SB = 64, DIST = 3;                 // stage bytes per row, prefetch distance (4 buffers)
+    constexpr int KS = FP8 ? 1 : 2;                  // MFMA k-steps per stage
+    constexpr int LI = 4;                            // 16-row load instructions per wavefront per operand
+    // Four buffers per operand as separate arrays, used with compile-time
+    // indices (the k loop is unrolled by four): the compiler can then tell the
+    // buffer a load fills from the one being read, and does not stall every
+    // LDS read on the loads still in flight.
+    __shared__ __attribute__((aligned(1024))) unsigned char A_0[BM * SB], A_1[BM * SB], A_2[BM * SB], A_3[BM * SB];
+    __shared__ __attribute__((aligned(1024))) unsigned char W_0[BN * SB], W_1[BN * SB], W_2[BN * SB], W_3[BN * SB];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / 2, wn = wave % 2, l32 = lane % 32, half = lane / 32;
+    int tmi, tni;
+    tile_of(blockIdx.x, (g.M + BM - 1) / BM, (g.N + BN - 1) / BN, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const size_t rowA = (size_t)g.K * (FP8 ? 1 : 2);
+    const unsigned char* A0 = (const unsigned char*)g.a + (size_t)m0 * rowA;
+    const unsigned char* W0 = (const unsigned char*)g.w + (size_t)n0 * rowA;
+    uint32_t offA[LI], offW[LI];
+#pragma unroll
+    for (int i = 0; i < LI; ++i) {
+        const int r = (wave * LI + i) * 16 + lane / 4;
+        const uint32_t c = (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
+        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + c;
+        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + c;
+    }
+    auto abuf = [&](auto b) -> unsigned char* {
+        if constexpr (decltype(b)::value == 0) return A_0;
+        else if constexpr (decltype(b)::value == 1) return A_1;
+        else if constexpr (decltype(b)::value == 2) return A_2;
+        else return A_3;
+    };
+    auto wbuf = [&](auto b) -> unsigned char* {
+        if constexpr (decltype(b)::value == 0) return W_0;
+        else if constexpr (decltype(b)::value == 1) return W_1;
+        else if constexpr (decltype(b)::value == 2) return W_2;
+        else return W_3;
+    };
+    auto issue = [&](auto b, int kb) {
+        unsigned char* ad = abuf(b);
+        unsigned char* wd = wbuf(b);
+#pragma unroll
+        for (int i = 0; i < LI; ++i)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A0 + offA[i] + kb),
+                                             (__attribute__((address_space(3))) void*)(ad + (wave * LI + i) * 16 * SB),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LI; ++i)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W0 + offW[i] + kb),
+                                             (__attribute__((address_space(3))) void*)(wd + (wave * LI + i) * 16 * SB),
+                                             16, 0, 0);
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Fragments: bf16 one 16-byte read per operand block and k-step, fp8 two.
+    constexpr int RP = FP8 ? 2 : 1;                  // reads per fragment
+    constexpr int NR = (TM + TN) * RP;               // reads per k-step (8 bf16, 16 fp8)
+    static_assert(FP8 || NR == 8, "lds_wait encodes 8 outstanding reads");
+    intx4 fa[2][TM][RP], fb[2][TN][RP];
+    auto reads = [&](int slot, const unsigned char* as, const unsigned char* ws, int ks) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * 128 + i * 32 + l32, sw = swz64(row);
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int c = FP8 ? half * 2 + q : ks * 2 + half;
+                fa[slot][i][q] = lds_read16(as + row * SB + ((c ^ sw) * 16));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int row = wn * 128 + j * 32 + l32, sw = swz64(row);
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int c = FP8 ? half * 2 + q : ks * 2 + half;
+                fb[slot][j][q] = lds_read16(ws + row * SB + ((c ^ sw) * 16));
+            }
+        }
+    };
+    // Wait until at most `pending` LDS reads are outstanding; the fragments of
+    // `slot` pass through the wait so the MFMAs that use them cannot move above it.
+    auto lds_wait = [&](int slot, int pending) {   // pending: 0 or 8 (a literal after inlining)
+        if (pending == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[slot][0][0]));
+        else asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fa[slot][0][0]));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int q = 0; q < RP; ++q) asm volatile("" : "+v"(fa[slot][i][q]));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < RP; ++q) asm volatile("" : "+v"(fb[slot][j][q]));
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (FP8) {
+                    const intx4 a0 = fa[slot][i][0], a1 = fa[slot][i][1], b0 = fb[slot][j][0], b1 = fb[slot][j][1];
+                    const intx8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    const intx8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                    // formats 0/0: e4m3 x e4m3; scale exponents 127 = 2^0
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 127, 0, 127);
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[slot][i][0]),
+                                                                        __builtin_bit_cast(bf16x8, fb[slot][j][0]),
+                                                                        acc[i][j], 0, 0, 0);
+                }
+            }
+    };
+
+    const int nk = (int)(rowA / SB);
+    // One stage: wait for its tiles, refill the buffer freed one stage ago
+    // (three stages ahead), multiply; the reads for k-step ks+1 are in flight
+    // while the MFMAs of k-step ks run.  B is read, (B + 3) % 4 filled.
+    auto stage = [&](auto b, int kt) {
+        // This wavefront's loads for stage kt are done (the 2 x 8 of the two later
+        // stages may be outstanding); the barrier makes every wavefront's loads
+        // visible and guarantees the buffer refilled below is no longer read.
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        issue(std::integral_constant<int, (decltype(b)::value + DIST) % 4>{}, min(kt + DIST, nk - 1) * SB);
+        const unsigned char* as = abuf(b);
+        const unsigned char* ws = wbuf(b);
+        reads(0, as, ws, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
+                reads((ks + 1) & 1, as, ws, ks + 1);
+                lds_wait(ks & 1, NR);   // bf16 only (fp8 has one k-step per stage)
+            } else {
+                lds_wait(ks & 1, 0);
+            }
+            mma(ks & 1);
+        }
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, min(1, nk - 1) * SB);
+    issue(std::integral_constant<int, 2>{}, min(2, nk - 1) * SB);
+    for (int kt = 0; kt < nk; kt += 4) {   // nk % 4 == 0 (launcher); past the end issue() re-loads the last stage
+        stage(std::integral_constant<int, 0>{}, kt);
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+        stage(std::integral_constant<int, 2>{}, kt + 2);
+        stage(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing re-loads before the workgroup ends
+    __syncthreads();                                    // every wavefront is done with the stage buffers
+
+    // Epilogue through LDS.  Per 32-row slice of its 128x128 block, a
+    // wavefront writes the fp32 accumulators into its own 16 KB buffer (row
+    // stride 128 floats), reads them back as row-contiguous float4s and applies
+    // the epilogue with 8- or 16-byte global accesses; for the residual forms
+    // all loads of a half-slice are issued before any store.
+    float* lds = (float*)(wave == 0 ? A_0 : wave == 1 ? A_1 : wave == 2 ? A_2 : A_3);
+    const int c4 = lane % 32;                           // float4 column chunk of this lane
+    const int nb = n0 + wn * 128 + 4 * c4;              // its first output column
+    const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
+    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (ncol && g.bias) {
+        const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nb);
+        bias4 = make_float4((float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]);
+    }
+    if (FP8 && ncol)
+        ws4 = make_float4(g.w_scale[nb / g.w_seg], g.w_scale[(nb + 1) / g.w_seg], g.w_scale[(nb + 2) / g.w_seg],
+                          g.w_scale[(nb + 3) / g.w_seg]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                lds[(8 * (r / 4) + 4 * half + (r % 4)) * 128 + j * 32 + l32] = acc[i][j][r];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                       // two half-slices of 8 row pairs
+            float4 v[8], xo[8], gt[8];
+            int mrow[8];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int row = (h * 8 + it) * 2 + half;
+                mrow[it] = m0 + wm * 128 + i * 32 + row;
+                float4 a4 = *(const float4*)&lds[row * 128 + 4 * c4];
+                if (FP8) {
+                    const float as = mrow[it] < g.M ? g.a_scale[mrow[it]] : 0.0f;
+                    a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
+                }
+                v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
+                if (EPI >= EPI_GATED && ncol && mrow[it] < g.M) {
+                    xo[it] = *(const float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb);
+                    gt[it] = EPI == EPI_GATED
+                                 ? *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb)
+                                 : make_float4(1.f, 1.f, 1.f, 1.f);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                if (!ncol || mrow[it] >= g.M) continue;
+                const float4 y = v[it];
+                if (EPI <= EPI_GELU) {
+                    bf16x4 o;
+                    if (EPI == EPI_GELU) {
+                        o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
+                        o[2] = (bf16)gelu_tanh(y.z); o[3] = (bf16)gelu_tanh(y.w);
+                    } else {
+                        o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
+                    }
+                    *(bf16x4*)((bf16*)g.out + (size_t)mrow[it] * g.ldo + nb) = o;
+                } else {
+                    const float4 x = xo[it], gg = gt[it];
+                    *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
+                        make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next slice overwrites
+    }
+}
+
 // ------------------------------------------------------------------ launch
+
+template <int BM, int BN, int EPI>
+static void launch_mfma(const GemmArgs& g, hipStream_t st) {
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    if (g.dtype == LWO_BF16) k_gemm_mfma<BM, BN, false, EPI><<<tiles, 256, 0, st>>>(g);
+    else k_gemm_mfma<BM, BN, true, EPI><<<tiles, 256, 0, st>>>(g);
+}
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     if (g.dtype == LWO_F32) {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
         k_gemm_f32<EPI><<<grid, 256, 0, st>>>(g);
+        return hipGetLastError();
+    }
+    const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    const size_t row_bytes = (size_t)g.K * (g.dtype == LWO_BF16 ? 2 : 1);
+    // Large products: 256x256 tiles with deep prefetch, when they give at least one
+    // workgroup per CU and the k loop unrolls by four 64-byte stages; otherwise
+    // 128x128 tiles.
+    if (big_tiles >= 256 && row_bytes % 256 == 0) {
+        if (g.dtype == LWO_BF16) k_gemm_deep<false, EPI><<<(int)big_tiles, 256, 0, st>>>(g);
+        else k_gemm_deep<true, EPI><<<(int)big_tiles, 256, 0, st>>>(g);
     } else {
-        dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM);
-        if (g.dtype == LWO_BF16) k_gemm_mfma<false, EPI><<<grid, 256, 0, st>>>(g);
-        else k_gemm_mfma<true, EPI><<<grid, 256, 0, st>>>(g);
+        launch_mfma<128, 128, EPI>(g, st);
     }
     return hipGetLastError();
 }

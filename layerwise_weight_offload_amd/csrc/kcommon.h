@@ -35,10 +35,18 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// tanh(t) = 1 - 2 / (exp(2t) + 1), with exp(2t) = 2^(2t log2 e) on v_exp_f32.
+// Inline (no call, so kernels holding large accumulator sets do not spill);
+// absolute error about 1e-7, saturating to +-1 for |t| > 44 without NaN.
+__device__ __forceinline__ float tanh_fast(float t) {
+    const float e = __builtin_amdgcn_exp2f(fminf(t * 2.8853900817779268f, 126.0f));   // 2 log2(e)
+    return 1.0f - 2.0f / (e + 1.0f);
+}
+
 __device__ __forceinline__ float gelu_tanh(float u) {
     // 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))
     const float k0 = 0.7978845608028654f;
-    return 0.5f * u * (1.0f + tanhf(k0 * (u + 0.044715f * u * u * u)));
+    return 0.5f * u * (1.0f + tanh_fast(k0 * (u + 0.044715f * u * u * u)));
 }
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }

@@ -36,13 +36,14 @@ extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void*
     if (K % kq) return bad("linear: K must be a multiple of " + std::to_string(kq));
     if (N % 8) return bad("linear: N must be a multiple of 8");
     if (!a || !w || !aligned16(a) || !aligned16(w)) return bad("linear: a and w must be 16-byte aligned device pointers");
-    if (bias && ((uintptr_t)bias & 3u)) return bad("linear: bias alignment");
+    if (bias && ((uintptr_t)bias & 7u)) return bad("linear: bias must be 8-byte aligned");
     if (dtype == LWO_FP8_E4M3 && (!a_scale || !w_scale || w_seg < 1)) return bad("linear: fp8 needs a_scale, w_scale and w_seg");
     if (epilogue <= EPI_GELU) {
-        if (!out || ldo < N) return bad("linear: out and ldo >= N required");
+        if (!out || ldo < N || ldo % 8 || !aligned16(out)) return bad("linear: out (16-byte aligned) and ldo >= N, a multiple of 8, required");
     } else {
-        if (!xr || ldx < N) return bad("linear: xr and ldx >= N required");
-        if (epilogue == EPI_GATED && (!gate || gate_ld < N || rows_per_gate < 1)) return bad("linear: gate, gate_ld >= N and rows_per_gate required");
+        if (!xr || ldx < N || ldx % 8 || !aligned16(xr)) return bad("linear: xr (16-byte aligned) and ldx >= N, a multiple of 8, required");
+        if (epilogue == EPI_GATED && (!gate || gate_ld < N || gate_ld % 8 || rows_per_gate < 1 || !aligned16(gate)))
+            return bad("linear: gate (16-byte aligned), gate_ld >= N (a multiple of 8) and rows_per_gate required");
     }
     if (!stream) return bad("linear: stream is NULL");
     GemmArgs g{};
