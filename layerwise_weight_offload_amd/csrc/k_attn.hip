@@ -20,6 +20,8 @@
 // k_attn_f32: one query per lane with fp32 FMA, for the fp32 workloads.
 #include <math.h>
 
+#include <type_traits>
+
 #include "../../include/lwo.h"
 #include "kcommon.h"
 #include "kernels.h"
@@ -155,6 +157,223 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         }
 }
 
+// ------------------------------------------------------------------ head dim 128
+
+// k_attn_d128: 512-thread workgroups own 256 queries of one (batch, head),
+// 32 per wavefront, with the same S^T = K Q^T / O^T += V^T P^T formulation
+// as k_attn_bf16.  Per 64-key tile:
+//  * K and V land in LDS with global_load_lds (16 bytes per lane, no
+//    register round trip), double-buffered: the tile after the current one
+//    is in flight while the current one is multiplied.  Rows are 256 bytes;
+//    the 16-byte chunk c of row r sits at c ^ (r % 16) for K (a fragment
+//    read touches 16 rows in one chunk column) and at c ^ 4 (r % 4) for V.
+//  * V^T fragments come from ds_read_b64_tr_b16: within each group of 16
+//    lanes, lane 4y + c addresses four consecutive 16-bit values and lane j
+//    receives value j % 4 of lanes j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4.
+//    With lane 4y + c pointing at key K0 + y, columns d0 + 4c .. d0 + 4c + 3,
+//    lane j gets V[K0 .. K0 + 3][d0 + j]: four keys of one output column, in
+//    the key order of the probability operand.
+//  * The softmax reference point moves only when a score exceeds it by more
+//    than 2^8 (base-2 exponent 8); until then the probabilities and the row
+//    sum keep the older reference, which changes no result (both share it)
+//    and skips most rescales of the 64 output accumulators.
+// LDS reads issued as instructions the compiler does not track (their
+// completion is awaited with explicit lgkmcnt waits, so loads still in flight
+// into the other buffer do not stall them); `off` must fold to a constant.
+#define LDS_RD128(v, addr, off) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(off))
+#define LDS_RD64_TR16(v, addr, off) asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(off))
+
+__global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
+    constexpr int DH = 128, BN = 64, QW = 32, NW = 8, RB = DH * 2, KS = DH / 16, NT = DH / 32;
+    constexpr int TB = BN * RB;                      // bytes per K or V tile (16 KB)
+    constexpr int KOFF = 0, VOFF = 2 * TB;           // K buffers at 0, TB; V buffers at 2 TB, 3 TB
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int l32 = lane % 32, half = lane / 32;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int Tq = a.Tq, Tk = a.Tk;
+    const int qi = blockIdx.x * (NW * QW) + wave * QW + l32;
+    const unsigned char* Kg = (const unsigned char*)a.k + ((size_t)b * Tk * a.ldk + h * DH) * 2;
+    const unsigned char* Vg = (const unsigned char*)a.v + ((size_t)b * Tk * a.ldv + h * DH) * 2;
+
+    // Loads: wavefront w fills rows 8w .. 8w + 7 of each tile, four rows per instruction.
+    int lrow[2], kcol[2], vcol[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        lrow[i] = (wave * 2 + i) * 4 + lane / 16;
+        const int p = lane % 16;
+        kcol[i] = (p ^ (lrow[i] % 16)) * 16;
+        vcol[i] = (p ^ (4 * (lrow[i] % 4))) * 16;
+    }
+    auto issue = [&](auto buf, int key0) {
+        constexpr int B = decltype(buf)::value;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const size_t key = (size_t)min(key0 + lrow[i], Tk - 1);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kg + key * a.ldk * 2 + kcol[i]),
+                                             (__attribute__((address_space(3))) void*)(smem + KOFF + B * TB + (wave * 2 + i) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vg + key * a.ldv * 2 + vcol[i]),
+                                             (__attribute__((address_space(3))) void*)(smem + VOFF + B * TB + (wave * 2 + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    const intx4 z = {0, 0, 0, 0};
+    intx4 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        qf[s] = qi < Tq ? *(const intx4*)((const bf16*)a.q + (size_t)(b * Tq + qi) * a.ldq + h * DH + s * 16 + half * 8) : z;
+
+    floatx16 oacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] = 0.0f;
+    float m_i = -INFINITY, l_i = 0.0f;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d)
+
+    // Per-lane LDS addresses; buffer and key offsets go into the instruction.
+    const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+    uint32_t kaddr[KS], vaddr[NT];
+#pragma unroll
+    for (int st = 0; st < KS; ++st)   // K row t*32 + l32 (row % 16 == l32 % 16), chunk 2 st + half
+        kaddr[st] = sbase + KOFF + l32 * RB + (((2 * st + half) ^ (l32 % 16)) * 16);
+    {
+        const int j16 = lane % 16, ty = j16 / 4, tc = j16 % 4, g2 = (lane / 16) % 2;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)   // V row t*32 + 16 ks + 4 half + ty (+ 8): row % 4 == ty
+            vaddr[nt] = sbase + VOFF + (4 * half + ty) * RB + ((4 * nt + 2 * g2 + tc / 2) ^ (4 * ty)) * 16 + 8 * (tc % 2);
+    }
+
+    auto tile = [&](auto buf, int key0) {
+        constexpr int BO = decltype(buf)::value * TB;
+        // ---- S^T = K Q^T for 64 keys, in four batches of four k-steps (batch
+        // u: 32-key half u / 2, k-steps 4 (u % 2) .. + 3); two batches in flight.
+        floatx16 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+        intx4 kf[2][4];
+#define KREAD(u)                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
+        LDS_RD128(kf[(u) % 2][i], kaddr[4 * ((u) % 2) + i], BO + ((u) / 2) * 32 * RB);
+        KREAD(0);
+        KREAD(1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < 3) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                asm volatile("" : "+v"(kf[u % 2][i]));
+                s[u / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[u % 2][i]),
+                                                                   __builtin_bit_cast(bf16x8, qf[4 * (u % 2) + i]),
+                                                                   s[u / 2], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep batch u's MFMAs ahead of the reads that reuse its registers
+            if (u == 0) { KREAD(2); }
+            if (u == 1) { KREAD(3); }
+        }
+#undef KREAD
+        // s[t][r]: key key0 + 32t + 8(r/4) + 4 half + r%4, query qi
+        if (key0 + BN > Tk) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (key0 + t * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= Tk) s[t][r] = -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        const bool need = mx > m_i + 8.0f;
+        if (__ballot(need)) {
+            const float m_new = need ? mx : m_i;
+            const float corr = __builtin_amdgcn_exp2f(m_i - m_new);
+            l_i *= corr;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[nt][r] *= corr;
+            m_i = m_new;
+        }
+        const float nm = -m_i;
+        float rs = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, nm));
+                s[t][r] = p;
+                rs += p;
+            }
+        rs += __shfl_xor(rs, 32);
+        l_i += rs;
+
+        // ---- O^T += V^T P^T, 16 keys per k-step; the reads of one 32-key half in flight together
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            __builtin_amdgcn_sched_barrier(0);   // one half's V fragments live at a time
+            intx2 vf[2][NT][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    LDS_RD64_TR16(vf[ks][nt][0], vaddr[nt], BO + (t * 32 + 16 * ks) * RB);
+                    LDS_RD64_TR16(vf[ks][nt][1], vaddr[nt], BO + (t * 32 + 16 * ks + 8) * RB);
+                }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 0) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+                else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                bf16x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    asm volatile("" : "+v"(vf[ks][nt][0]), "+v"(vf[ks][nt][1]));
+                    const intx4 v4 = {vf[ks][nt][0][0], vf[ks][nt][0][1], vf[ks][nt][1][0], vf[ks][nt][1][1]};
+                    oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pf, oacc[nt],
+                                                                       0, 0, 0);
+                }
+            }
+        }
+    };
+
+    const int ntile = (Tk + BN - 1) / BN;
+    issue(std::integral_constant<int, 0>{}, 0);
+    for (int j = 0; j < ntile; j += 2) {
+        // Tile j in buffer 0: its loads are this wavefront's only outstanding ones; the
+        // barrier publishes every wavefront's loads and frees buffer 1 for tile j + 1.
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (j + 1 < ntile) issue(std::integral_constant<int, 1>{}, (j + 1) * BN);
+        tile(std::integral_constant<int, 0>{}, j * BN);
+        if (j + 1 >= ntile) break;
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (j + 2 < ntile) issue(std::integral_constant<int, 0>{}, (j + 2) * BN);
+        tile(std::integral_constant<int, 1>{}, (j + 1) * BN);
+    }
+
+    if (qi >= Tq) return;
+    const float inv = 1.0f / l_i;
+    bf16* O = (bf16*)a.o + (size_t)(b * Tq + qi) * a.ldo + h * DH;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[nt][4 * g + e] * inv);
+            *(bf16x4*)(O + nt * 32 + 8 * g + 4 * half) = o;
+        }
+}
+
 template <int DH>
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     __shared__ float Ks[32][DH];
@@ -209,7 +428,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
         switch (a.dh) {
             case 64: k_attn_bf16<64><<<grid, 256, 0, st>>>(a); break;
             case 72: k_attn_bf16<72><<<grid, 256, 0, st>>>(a); break;
-            case 128: k_attn_bf16<128><<<grid, 256, 0, st>>>(a); break;
+            case 128: {
+                dim3 g128((a.Tq + 255) / 256, a.H, a.B);
+                k_attn_d128<<<g128, 512, 0, st>>>(a);
+                break;
+            }
             default: return hipErrorInvalidValue;
         }
     } else {

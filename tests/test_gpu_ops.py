@@ -196,6 +196,8 @@ def _attn_case(lib, dtype, B, H, Tq, Tk, d, fused_qkv, n_rows, seed):
     (2, 16, 1024, 1024, 72, True, 1024),      # DiT-XL: every row
     (1, 4, 333, 333, 64, True, 333),          # ragged, d 64
     (2, 2, 200, 40, 72, False, 200),          # cross with fewer keys than one tile
+    (2, 3, 77, 40, 128, False, 77),           # d 128: one partial query block, one partial key tile
+    (1, 2, 300, 130, 128, True, 300),         # d 128: ragged queries, three key tiles, the last partial
 ])
 def test_attention_bf16(lib, B, H, Tq, Tk, d, fused, rows):
     print(f"[attention bf16] B={B} H={H} Tq={Tq} Tk={Tk} d={d}", flush=True)
