@@ -7,11 +7,13 @@
 // [N,K] weights), so each lane's MFMA fragment is one or two 16-byte LDS
 // reads from a row.  No split-K: every output is produced by one lane in a
 // fixed order, so results are deterministic run to run.
-// * k_gemm_deep: large products; 256x256 tiles, direct-to-LDS loads three
-//   stages ahead, LDS-staged vector epilogue (details at the kernel).
-// * k_gemm_mfma: everything else; 128x128 tiles (2x2 wavefronts of 64x64),
-//   128 bytes of K per stage, register-staged double-buffered LDS with a
-//   16-byte row pad.
+// * k_gemm_deep: K rows a multiple of 256 bytes (every block product);
+//   256x256, 256x128, 128x128 or 128x64 tiles by problem size, direct-to-LDS
+//   loads three stages ahead, LDS-staged vector epilogue (details at the
+//   kernel).
+// * k_gemm_mfma: other K; 128x128 tiles (2x2 wavefronts of 64x64), 128
+//   bytes of K per stage, register-staged double-buffered LDS with a 16-byte
+//   row pad.
 // * k_gemm_f32: fp32 FMA tiles (64x64, 4x4 per thread) for the fp32
 //   workloads, where bf16 rounding would exceed a 1e-4 tolerance.
 #include <type_traits>
@@ -228,17 +230,18 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
         }
 }
 
-// ------------------------------------------------------------------ 256x256 tiles, deep prefetch
+// ------------------------------------------------------------------ deep prefetch, direct-to-LDS
 
-// Large shapes.  256x256 outputs per workgroup (2x2 wavefronts of 128x128 =
-// 4x4 MFMA blocks each).  K advances in 64-byte stages (32 bf16 or 64 fp8
-// elements) held in four LDS buffers; each stage is fetched with
-// global_load_lds three stages ahead of its use, so about three stages of
-// MFMA work cover the load latency.  The wait before a stage is
-// `s_waitcnt vmcnt(16)` (this wavefront's loads for the two later stages may
-// still be in flight) followed by a plain s_barrier: the workgroup barrier
-// of the language would also drain those later loads.  LDS rows are 64 bytes
-// (four 16-byte chunks); chunk c of row r sits at c ^ f(r) with
+// BM x BN outputs per 256-thread workgroup (BM, BN in {64, 128, 256}, BM >=
+// 128): 2x2 wavefronts, each owning (BM/2) x (BN/2) = TM x TN MFMA 32x32
+// blocks.  K advances in 64-byte stages (32 bf16 or 64 fp8 elements) held in
+// four LDS buffers; each stage is fetched with global_load_lds three stages
+// ahead of its use, so about three stages of MFMA work cover the load
+// latency.  The wait before a stage is `s_waitcnt vmcnt(2 L)` (this
+// wavefront's L loads per stage for the two later stages may still be in
+// flight) followed by a plain s_barrier: the workgroup barrier of the
+// language would also drain those later loads.  LDS rows are 64 bytes (four
+// 16-byte chunks); chunk c of row r sits at c ^ f(r) with
 // f(r) = ((r >> 1) ^ (r >> 3)) & 3, which puts the rows one fragment read
 // touches on distinct banks for 32- and 64-bank LDS alike.
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -253,12 +256,14 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
-template <bool FP8, int EPI>
+template <int BM, int BN, bool FP8, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
-    constexpr int BM = 256, BN = 256, TM = 4, TN = 4;
+    constexpr int TM = BM / 64, TN = BN / 64;
     constexpr int SB = 64, DIST = 3;                 // stage bytes per row, prefetch distance (4 buffers)
     constexpr int KS = FP8 ? 1 : 2;                  // MFMA k-steps per stage
-    constexpr int LI = 4;                            // 16-row load instructions per wavefront per operand
+    constexpr int LIA = BM / 64, LIW = BN / 64;      // 16-row load instructions per wavefront per operand
+    constexpr int VM = 2 * (LIA + LIW);              // loads of the two stages after the one awaited
+    static_assert(BM >= 128 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
     // Four buffers per operand as separate arrays, used with compile-time
     // indices (the k loop is unrolled by four): the compiler can then tell the
     // buffer a load fills from the one being read, and does not stall every
@@ -273,13 +278,17 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     const size_t rowA = (size_t)g.K * (FP8 ? 1 : 2);
     const unsigned char* A0 = (const unsigned char*)g.a + (size_t)m0 * rowA;
     const unsigned char* W0 = (const unsigned char*)g.w + (size_t)n0 * rowA;
-    uint32_t offA[LI], offW[LI];
+    // Rows past M or N re-read the last row (finite data); their outputs are not stored.
+    uint32_t offA[LIA], offW[LIW];
 #pragma unroll
-    for (int i = 0; i < LI; ++i) {
-        const int r = (wave * LI + i) * 16 + lane / 4;
-        const uint32_t c = (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
-        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + c;
-        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + c;
+    for (int i = 0; i < LIA; ++i) {
+        const int r = (wave * LIA + i) * 16 + lane / 4;
+        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < LIW; ++i) {
+        const int r = (wave * LIW + i) * 16 + lane / 4;
+        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
     }
     auto abuf = [&](auto b) -> unsigned char* {
         if constexpr (decltype(b)::value == 0) return A_0;
@@ -297,14 +306,14 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
         unsigned char* ad = abuf(b);
         unsigned char* wd = wbuf(b);
 #pragma unroll
-        for (int i = 0; i < LI; ++i)
+        for (int i = 0; i < LIA; ++i)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A0 + offA[i] + kb),
-                                             (__attribute__((address_space(3))) void*)(ad + (wave * LI + i) * 16 * SB),
+                                             (__attribute__((address_space(3))) void*)(ad + (wave * LIA + i) * 16 * SB),
                                              16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < LI; ++i)
+        for (int i = 0; i < LIW; ++i)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W0 + offW[i] + kb),
-                                             (__attribute__((address_space(3))) void*)(wd + (wave * LI + i) * 16 * SB),
+                                             (__attribute__((address_space(3))) void*)(wd + (wave * LIW + i) * 16 * SB),
                                              16, 0, 0);
     };
 
@@ -318,13 +327,12 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
 
     // Fragments: bf16 one 16-byte read per operand block and k-step, fp8 two.
     constexpr int RP = FP8 ? 2 : 1;                  // reads per fragment
-    constexpr int NR = (TM + TN) * RP;               // reads per k-step (8 bf16, 16 fp8)
-    static_assert(FP8 || NR == 8, "lds_wait encodes 8 outstanding reads");
+    constexpr int NR = (TM + TN) * RP;               // reads per k-step
     intx4 fa[2][TM][RP], fb[2][TN][RP];
     auto reads = [&](int slot, const unsigned char* as, const unsigned char* ws, int ks) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * 128 + i * 32 + l32, sw = swz64(row);
+            const int row = wm * (BM / 2) + i * 32 + l32, sw = swz64(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
                 const int c = FP8 ? half * 2 + q : ks * 2 + half;
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn * 128 + j * 32 + l32, sw = swz64(row);
+            const int row = wn * (BN / 2) + j * 32 + l32, sw = swz64(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
                 const int c = FP8 ? half * 2 + q : ks * 2 + half;
@@ -341,11 +349,12 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
             }
         }
     };
-    // Wait until at most `pending` LDS reads are outstanding; the fragments of
-    // `slot` pass through the wait so the MFMAs that use them cannot move above it.
-    auto lds_wait = [&](int slot, int pending) {   // pending: 0 or 8 (a literal after inlining)
+    // Wait until at most `pending` LDS reads are outstanding (0 or NR, a literal after
+    // inlining); the fragments of `slot` pass through the wait so the MFMAs that use
+    // them cannot move above it.
+    auto lds_wait = [&](int slot, int pending) {
         if (pending == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[slot][0][0]));
-        else asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fa[slot][0][0]));
+        else asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fa[slot][0][0]) : "i"(NR));
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -379,10 +388,10 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     // (three stages ahead), multiply; the reads for k-step ks+1 are in flight
     // while the MFMAs of k-step ks run.  B is read, (B + 3) % 4 filled.
     auto stage = [&](auto b, int kt) {
-        // This wavefront's loads for stage kt are done (the 2 x 8 of the two later
+        // This wavefront's loads for stage kt are done (those of the two later
         // stages may be outstanding); the barrier makes every wavefront's loads
         // visible and guarantees the buffer refilled below is no longer read.
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM) : "memory");
         issue(std::integral_constant<int, (decltype(b)::value + DIST) % 4>{}, min(kt + DIST, nk - 1) * SB);
         const unsigned char* as = abuf(b);
         const unsigned char* ws = wbuf(b);
@@ -411,14 +420,17 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing re-loads before the workgroup ends
     __syncthreads();                                    // every wavefront is done with the stage buffers
 
-    // Epilogue through LDS.  Per 32-row slice of its 128x128 block, a
-    // wavefront writes the fp32 accumulators into its own 16 KB buffer (row
-    // stride 128 floats), reads them back as row-contiguous float4s and applies
-    // the epilogue with 8- or 16-byte global accesses; for the residual forms
-    // all loads of a half-slice are issued before any store.
+    // Epilogue through LDS.  Per 32-row slice of its block, a wavefront writes
+    // the fp32 accumulators into its own buffer (row stride CW floats), reads
+    // them back as row-contiguous float4s (CH lanes per row, RPP rows per
+    // pass) and applies the epilogue with 8- or 16-byte global accesses; for
+    // the residual forms the loads of up to eight passes are issued before
+    // any store.
+    constexpr int CW = 32 * TN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
+    static_assert(32 * CW * 4 <= BM * SB, "epilogue staging fits one A buffer");
     float* lds = (float*)(wave == 0 ? A_0 : wave == 1 ? A_1 : wave == 2 ? A_2 : A_3);
-    const int c4 = lane % 32;                           // float4 column chunk of this lane
-    const int nb = n0 + wn * 128 + 4 * c4;              // its first output column
+    const int c4 = lane % CH, rr = lane / CH;           // float4 column chunk and row-in-pass of this lane
+    const int nb = n0 + wn * CW + 4 * c4;               // its first output column
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
     if (ncol && g.bias) {
@@ -434,17 +446,17 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                lds[(8 * (r / 4) + 4 * half + (r % 4)) * 128 + j * 32 + l32] = acc[i][j][r];
+                lds[(8 * (r / 4) + 4 * half + (r % 4)) * CW + j * 32 + l32] = acc[i][j][r];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {                       // two half-slices of 8 row pairs
-            float4 v[8], xo[8], gt[8];
-            int mrow[8];
+        for (int h = 0; h < NP / PB; ++h) {
+            float4 v[PB], xo[PB], gt[PB];
+            int mrow[PB];
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int row = (h * 8 + it) * 2 + half;
-                mrow[it] = m0 + wm * 128 + i * 32 + row;
-                float4 a4 = *(const float4*)&lds[row * 128 + 4 * c4];
+            for (int it = 0; it < PB; ++it) {
+                const int row = (h * PB + it) * RPP + rr;
+                mrow[it] = m0 + wm * (BM / 2) + i * 32 + row;
+                float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
                 if (FP8) {
                     const float as = mrow[it] < g.M ? g.a_scale[mrow[it]] : 0.0f;
                     a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
                 }
             }
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
+            for (int it = 0; it < PB; ++it) {
                 if (!ncol || mrow[it] >= g.M) continue;
                 const float4 y = v[it];
                 if (EPI <= EPI_GELU) {
@@ -497,16 +509,30 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
         k_gemm_f32<EPI><<<grid, 256, 0, st>>>(g);
         return hipGetLastError();
     }
-    const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const size_t row_bytes = (size_t)g.K * (g.dtype == LWO_BF16 ? 2 : 1);
-    // Large products: 256x256 tiles with deep prefetch, when they give at least one
-    // workgroup per CU and the k loop unrolls by four 64-byte stages; otherwise
-    // 128x128 tiles.
-    if (big_tiles >= 256 && row_bytes % 256 == 0) {
-        if (g.dtype == LWO_BF16) k_gemm_deep<false, EPI><<<(int)big_tiles, 256, 0, st>>>(g);
-        else k_gemm_deep<true, EPI><<<(int)big_tiles, 256, 0, st>>>(g);
-    } else {
+    if (row_bytes % 256) {   // the deep kernels unroll the k loop by four 64-byte stages
         launch_mfma<128, 128, EPI>(g, st);
+        return hipGetLastError();
+    }
+    auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+    const bool f8 = g.dtype != LWO_BF16;
+    // Tile choice (measured on the block shapes): the largest tile that still
+    // gives most CUs a workgroup.  256x256 and 256x128 hold one workgroup per
+    // CU (LDS), 128x128 two, 128x64 three.
+    const int t256 = tiles(256, 256), t256x128 = tiles(256, 128), t128 = tiles(128, 128);
+    if (t256 >= 256) {
+        if (f8) k_gemm_deep<256, 256, true, EPI><<<t256, 256, 0, st>>>(g);
+        else k_gemm_deep<256, 256, false, EPI><<<t256, 256, 0, st>>>(g);
+    } else if (t256x128 >= 192 && t256x128 <= 256) {
+        if (f8) k_gemm_deep<256, 128, true, EPI><<<t256x128, 256, 0, st>>>(g);
+        else k_gemm_deep<256, 128, false, EPI><<<t256x128, 256, 0, st>>>(g);
+    } else if (t128 >= 128) {
+        if (f8) k_gemm_deep<128, 128, true, EPI><<<t128, 256, 0, st>>>(g);
+        else k_gemm_deep<128, 128, false, EPI><<<t128, 256, 0, st>>>(g);
+    } else {
+        const int t = tiles(128, 64);
+        if (f8) k_gemm_deep<128, 64, true, EPI><<<t, 256, 0, st>>>(g);
+        else k_gemm_deep<128, 64, false, EPI><<<t, 256, 0, st>>>(g);
     }
     return hipGetLastError();
 }

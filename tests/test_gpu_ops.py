@@ -66,6 +66,10 @@ def _sample(rng, M, N, n):
     (32760, 5120, 5120, 3),      # video cross output projection, plain residual
     (2048, 1152, 4608, 2),       # DiT-XL FFN down, gated
     (2048, 3456, 1152, 0),       # DiT-XL QKV
+    (2048, 1152, 1152, 2),       # DiT-XL attention output, gated
+    (2048, 4608, 1152, 1),       # DiT-XL FFN up, GELU
+    (256, 15360, 5120, 0),       # video at 256 tokens: QKV
+    (256, 5120, 13824, 2),       # video at 256 tokens: FFN down, gated
     (200, 576, 2304, 1),         # ragged M and N
 ])
 def test_linear_bf16_sampled(lib, M, N, K, epi):
