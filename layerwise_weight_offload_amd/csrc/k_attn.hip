@@ -2,20 +2,19 @@
 // block): O = softmax(Q K^T / sqrt(d)) V per (batch, head), streamed over key
 // tiles with an online softmax so the T x T score matrix never exists.
 //
-// k_attn_bf16 (gfx950 MFMA): a 256-thread workgroup owns 128 queries of one
-// (batch, head), 32 per wavefront.  Per 64-key tile:
-//   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
-//          wavefront's Q fragments kept in registers for the whole kernel;
-//          the accumulator layout puts one query in each lane (column), so
-//          the row max and row sum are in-lane reductions plus one swap
-//          between the two 32-lane halves;
+// k_attn_tr (bf16, gfx950 MFMA v_mfma_f32_32x32x16_bf16), per wavefront 32
+// queries, per 64-key tile:
+//   S^T = K Q^T: A = K rows from LDS, B = the wavefront's Q fragments kept in
+//          registers for the whole kernel; the accumulator layout puts one
+//          query in each lane (column), so the row max and row sum are
+//          in-lane reductions plus one swap between the two 32-lane halves;
 //   O^T += V^T P^T: B = the probabilities straight from the S^T registers
-//          (rounded to bf16), A = V^T read from an LDS tile stored
-//          transposed; the key order inside each MFMA k-step follows the
-//          accumulator layout, identically on both operands.
-// Head dims 64, 72 and 128: the QK^T contraction is padded with zeros to a
-// multiple of 16 and the PV output to a multiple of 32 columns (72 -> 80 and
-// 96); padded columns are never stored.  Key and query tails are masked.
+//          (rounded to bf16), A = V^T fragments read transposed from the
+//          row-major V tile; the key order inside each MFMA k-step follows
+//          the accumulator layout, identically on both operands.
+// Head dims 64, 72 and 128: QK^T is padded with zeros to a multiple of 16
+// and the PV output to a multiple of 32 columns (72 -> 80 and 96); padded
+// columns are never stored.  Key and query tails are masked.
 //
 // k_attn_f32: one query per lane with fp32 FMA, for the fp32 workloads.
 #include <math.h>
@@ -28,145 +27,21 @@
 
 namespace lwo {
 
-template <int DH>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-    constexpr int DK = (DH + 15) / 16 * 16;
-    constexpr int DN = (DH + 31) / 32 * 32;
-    constexpr int KS = DK / 16, NT = DN / 32;
-    constexpr int BN = 64;
-    constexpr int KST = DK + 8;     // K tile row stride (elements): 16-byte pad
-    constexpr int VST = BN + 8;     // V^T tile row stride (elements)
-    __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KST];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[DN * VST];
+// ------------------------------------------------------------------ direct-to-LDS tiles, transpose reads
 
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int l32 = lane % 32, half = lane / 32;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int Tq = a.Tq, Tk = a.Tk;
-    const int qi = blockIdx.x * 128 + wave * 32 + l32;
-    const bf16* Q = (const bf16*)a.q;
-    const bf16* K = (const bf16*)a.k;
-    const bf16* V = (const bf16*)a.v;
-    const intx4 z = {0, 0, 0, 0};
-
-    intx4 qf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int d0 = s * 16 + half * 8;
-        qf[s] = (qi < Tq && d0 < DH) ? *(const intx4*)(Q + (size_t)(b * Tq + qi) * a.ldq + h * DH + d0) : z;
-    }
-    floatx16 oacc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] = 0.0f;
-    float m_i = -INFINITY, l_i = 0.0f;
-    const float sl2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d)
-
-    for (int key0 = 0; key0 < Tk; key0 += BN) {
-        __syncthreads();
-        for (int c = tid; c < BN * (DK / 8); c += 256) {
-            const int key = c / (DK / 8), d0 = (c % (DK / 8)) * 8;
-            const intx4 v = (key0 + key < Tk && d0 < DH)
-                                ? *(const intx4*)(K + (size_t)(b * Tk + key0 + key) * a.ldk + h * DH + d0) : z;
-            *(intx4*)&Ks[key * KST + d0] = v;
-        }
-        for (int c = tid; c < BN * (DN / 8); c += 256) {
-            const int key = c % BN, d0 = (c / BN) * 8;
-            const intx4 v = (key0 + key < Tk && d0 < DH)
-                                ? *(const intx4*)(V + (size_t)(b * Tk + key0 + key) * a.ldv + h * DH + d0) : z;
-            const bf16x8 vv = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[(d0 + e) * VST + key] = vv[e];
-        }
-        __syncthreads();
-
-        floatx16 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-#pragma unroll
-            for (int st = 0; st < KS; ++st) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const intx4*)&Ks[(t * 32 + l32) * KST + st * 16 + half * 8]);
-                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[st]), s[t], 0, 0, 0);
-            }
-        }
-        // s[t][r]: key key0 + 32t + 8(r/4) + 4*half + r%4, query qi
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = key0 + t * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                const float v = key < Tk ? s[t][r] * sl2 : -INFINITY;
-                s[t][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_i, mx);
-        const float corr = exp2f(m_i - m_new);
-        float rs = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(s[t][r] - m_new);
-                s[t][r] = p;
-                rs += p;
-            }
-        rs += __shfl_xor(rs, 32);
-        l_i = l_i * corr + rs;
-        m_i = m_new;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[nt][r] *= corr;
-
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const bf16* vr = &Vt[(nt * 32 + l32) * VST + t * 32 + ks * 16 + half * 4];
-                    const bf16x4 lo = *(const bf16x4*)vr, hi = *(const bf16x4*)(vr + 8);
-                    const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[nt], 0, 0, 0);
-                }
-            }
-    }
-
-    if (qi >= Tq) return;
-    const float inv = 1.0f / l_i;
-    bf16* O = (bf16*)a.o + (size_t)(b * Tq + qi) * a.ldo + h * DH;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = nt * 32 + 8 * g + 4 * half;
-            if (d0 < DH) {
-                bf16x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[nt][4 * g + e] * inv);
-                *(bf16x4*)(O + d0) = o;
-            }
-        }
-}
-
-// ------------------------------------------------------------------ head dim 128
-
-// k_attn_d128: 512-thread workgroups own 256 queries of one (batch, head),
-// 32 per wavefront, with the same S^T = K Q^T / O^T += V^T P^T formulation
-// as k_attn_bf16.  Per 64-key tile:
+// k_attn_tr<DH, NW>: NW wavefronts own 32 NW queries of one (batch, head),
+// 32 per wavefront, with the S^T = K Q^T / O^T += V^T P^T formulation above.
+// Per 64-key tile:
 //  * K and V land in LDS with global_load_lds (16 bytes per lane, no
 //    register round trip), double-buffered: the tile after the current one
-//    is in flight while the current one is multiplied.  Rows are 256 bytes;
-//    the 16-byte chunk c of row r sits at c ^ (r % 16) for K (a fragment
-//    read touches 16 rows in one chunk column) and at c ^ 4 (r % 4) for V.
+//    is in flight while the current one is multiplied.  A row is NC 16-byte
+//    chunks (NC = 16, 12, 8 for d = 128, 72, 64: d 72 is read as 80 columns
+//    by QK and 96 by PV); chunks past the head's data hold a copy of its last
+//    chunk, so every value read is finite: padded K columns meet zero Q
+//    columns and padded V columns only feed outputs that are not stored.
+//    Chunk c of row r sits at c ^ fK(r) in K and c ^ fV(r) in V, chosen per
+//    row pitch so that the rows one fragment read touches fall on distinct
+//    banks.
 //  * V^T fragments come from ds_read_b64_tr_b16: within each group of 16
 //    lanes, lane 4y + c addresses four consecutive 16-bit values and lane j
 //    receives value j % 4 of lanes j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4.
@@ -176,16 +51,39 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
 //  * The softmax reference point moves only when a score exceeds it by more
 //    than 2^8 (base-2 exponent 8); until then the probabilities and the row
 //    sum keep the older reference, which changes no result (both share it)
-//    and skips most rescales of the 64 output accumulators.
+//    and skips most rescales of the output accumulators.
+
 // LDS reads issued as instructions the compiler does not track (their
 // completion is awaited with explicit lgkmcnt waits, so loads still in flight
 // into the other buffer do not stall them); `off` must fold to a constant.
 #define LDS_RD128(v, addr, off) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(off))
 #define LDS_RD64_TR16(v, addr, off) asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(off))
 
-__global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
-    constexpr int DH = 128, BN = 64, QW = 32, NW = 8, RB = DH * 2, KS = DH / 16, NT = DH / 32;
-    constexpr int TB = BN * RB;                      // bytes per K or V tile (16 KB)
+template <int DH> struct TrGeom;
+template <> struct TrGeom<128> {   // 256-byte rows: every row starts on bank 0
+    static constexpr int NC = 16;
+    static __device__ int fk(int r) { return r & 15; }
+    static __device__ int fv(int r) { return 4 * (r & 3); }
+};
+template <> struct TrGeom<72> {    // 192-byte rows: rows r, r+4, r+8, r+12 share banks
+    static constexpr int NC = 12;
+    static __device__ int fk(int r) { return (r >> 2) & 3; }   // permutes within aligned groups of 4: stays < 12
+    static __device__ int fv(int) { return 0; }               // four consecutive rows already disjoint
+};
+template <> struct TrGeom<64> {    // 128-byte rows: rows r, r+2 share banks
+    static constexpr int NC = 8;
+    static __device__ int fk(int r) { return (r >> 1) & 7; }
+    static __device__ int fv(int r) { return 4 * ((r >> 1) & 1); }
+};
+
+template <int DH, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void k_attn_tr(AttnArgs a) {
+    using G = TrGeom<DH>;
+    constexpr int BN = 64, QW = 32, NC = G::NC, PITCH = NC * 16, NVALID = DH / 8;
+    constexpr int KS = (DH + 15) / 16, NT = (DH + 31) / 32;   // QK k-steps, PV output tiles of 32 columns
+    constexpr int LI = NC / NW;                      // load instructions per wavefront per operand and tile
+    static_assert(NC % NW == 0 && 2 * KS <= NC && 4 * NT <= NC, "geometry");
+    constexpr int TB = BN * PITCH;                   // bytes per K or V tile
     constexpr int KOFF = 0, VOFF = 2 * TB;           // K buffers at 0, TB; V buffers at 2 TB, 3 TB
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
 
@@ -197,25 +95,27 @@ __global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
     const unsigned char* Kg = (const unsigned char*)a.k + ((size_t)b * Tk * a.ldk + h * DH) * 2;
     const unsigned char* Vg = (const unsigned char*)a.v + ((size_t)b * Tk * a.ldv + h * DH) * 2;
 
-    // Loads: wavefront w fills rows 8w .. 8w + 7 of each tile, four rows per instruction.
-    int lrow[2], kcol[2], vcol[2];
+    // Loads: instruction q = wave LI + i fills chunk positions 64 q .. 64 q + 63 of
+    // the tile (row p / NC, position p % NC), one per lane.
+    int lrow[LI], kcol[LI], vcol[LI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        lrow[i] = (wave * 2 + i) * 4 + lane / 16;
-        const int p = lane % 16;
-        kcol[i] = (p ^ (lrow[i] % 16)) * 16;
-        vcol[i] = (p ^ (4 * (lrow[i] % 4))) * 16;
+    for (int i = 0; i < LI; ++i) {
+        const int p = (wave * LI + i) * 64 + lane;
+        const int r = p / NC, cp = p % NC;
+        lrow[i] = r;
+        kcol[i] = min(cp ^ G::fk(r), NVALID - 1) * 16;
+        vcol[i] = min(cp ^ G::fv(r), NVALID - 1) * 16;
     }
     auto issue = [&](auto buf, int key0) {
         constexpr int B = decltype(buf)::value;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < LI; ++i) {
             const size_t key = (size_t)min(key0 + lrow[i], Tk - 1);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kg + key * a.ldk * 2 + kcol[i]),
-                                             (__attribute__((address_space(3))) void*)(smem + KOFF + B * TB + (wave * 2 + i) * 1024),
+                                             (__attribute__((address_space(3))) void*)(smem + KOFF + B * TB + (wave * LI + i) * 1024),
                                              16, 0, 0);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vg + key * a.ldv * 2 + vcol[i]),
-                                             (__attribute__((address_space(3))) void*)(smem + VOFF + B * TB + (wave * 2 + i) * 1024),
+                                             (__attribute__((address_space(3))) void*)(smem + VOFF + B * TB + (wave * LI + i) * 1024),
                                              16, 0, 0);
         }
     };
@@ -223,8 +123,10 @@ __global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
     const intx4 z = {0, 0, 0, 0};
     intx4 qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        qf[s] = qi < Tq ? *(const intx4*)((const bf16*)a.q + (size_t)(b * Tq + qi) * a.ldq + h * DH + s * 16 + half * 8) : z;
+    for (int s = 0; s < KS; ++s) {
+        const int d0 = s * 16 + half * 8;
+        qf[s] = (qi < Tq && d0 < DH) ? *(const intx4*)((const bf16*)a.q + (size_t)(b * Tq + qi) * a.ldq + h * DH + d0) : z;
+    }
 
     floatx16 oacc[NT];
 #pragma unroll
@@ -238,46 +140,68 @@ __global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
     const uint32_t sbase = (uint32_t)(uintptr_t)smem;
     uint32_t kaddr[KS], vaddr[NT];
 #pragma unroll
-    for (int st = 0; st < KS; ++st)   // K row t*32 + l32 (row % 16 == l32 % 16), chunk 2 st + half
-        kaddr[st] = sbase + KOFF + l32 * RB + (((2 * st + half) ^ (l32 % 16)) * 16);
+    for (int st = 0; st < KS; ++st)   // K row t*32 + l32 (fk(row) == fk(l32)), chunk 2 st + half
+        kaddr[st] = sbase + KOFF + l32 * PITCH + (((2 * st + half) ^ G::fk(l32)) * 16);
     {
         const int j16 = lane % 16, ty = j16 / 4, tc = j16 % 4, g2 = (lane / 16) % 2;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)   // V row t*32 + 16 ks + 4 half + ty (+ 8): row % 4 == ty
-            vaddr[nt] = sbase + VOFF + (4 * half + ty) * RB + ((4 * nt + 2 * g2 + tc / 2) ^ (4 * ty)) * 16 + 8 * (tc % 2);
+        for (int nt = 0; nt < NT; ++nt)   // V row t*32 + 16 ks + 4 half + ty (+ 8): fv(row) == fv(ty)
+            vaddr[nt] = sbase + VOFF + (4 * half + ty) * PITCH + ((4 * nt + 2 * g2 + tc / 2) ^ G::fv(ty)) * 16 +
+                        8 * (tc % 2);
     }
 
     auto tile = [&](auto buf, int key0) {
         constexpr int BO = decltype(buf)::value * TB;
-        // ---- S^T = K Q^T for 64 keys, in four batches of four k-steps (batch
-        // u: 32-key half u / 2, k-steps 4 (u % 2) .. + 3); two batches in flight.
         floatx16 s[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-        intx4 kf[2][4];
+        // ---- S^T = K Q^T for 64 keys
+        if constexpr (KS == 8) {
+            // four batches of four k-steps (batch u: 32-key half u / 2, k-steps
+            // 4 (u % 2) .. + 3); two batches in flight
+            intx4 kf[2][4];
 #define KREAD(u)                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
-        LDS_RD128(kf[(u) % 2][i], kaddr[4 * ((u) % 2) + i], BO + ((u) / 2) * 32 * RB);
-        KREAD(0);
-        KREAD(1);
+        LDS_RD128(kf[(u) % 2][i], kaddr[4 * ((u) % 2) + i], BO + ((u) / 2) * 32 * PITCH);
+            KREAD(0);
+            KREAD(1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u < 3) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            for (int u = 0; u < 4; ++u) {
+                if (u < 3) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+                else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asm volatile("" : "+v"(kf[u % 2][i]));
-                s[u / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[u % 2][i]),
-                                                                   __builtin_bit_cast(bf16x8, qf[4 * (u % 2) + i]),
-                                                                   s[u / 2], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    asm volatile("" : "+v"(kf[u % 2][i]));
+                    s[u / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[u % 2][i]),
+                                                                       __builtin_bit_cast(bf16x8, qf[4 * (u % 2) + i]),
+                                                                       s[u / 2], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep batch u's MFMAs ahead of the reads that reuse its registers
+                if (u == 0) { KREAD(2); }
+                if (u == 1) { KREAD(3); }
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep batch u's MFMAs ahead of the reads that reuse its registers
-            if (u == 0) { KREAD(2); }
-            if (u == 1) { KREAD(3); }
-        }
 #undef KREAD
+        } else {
+            // both 32-key halves in flight, then the MFMAs of each
+            intx4 kf[2][KS];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int st = 0; st < KS; ++st) LDS_RD128(kf[t][st], kaddr[st], BO + t * 32 * PITCH);
+            asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(KS) : "memory");
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (t == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    asm volatile("" : "+v"(kf[t][st]));
+                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t][st]),
+                                                                   __builtin_bit_cast(bf16x8, qf[st]), s[t], 0, 0, 0);
+                }
+            }
+        }
         // s[t][r]: key key0 + 32t + 8(r/4) + 4 half + r%4, query qi
         if (key0 + BN > Tk) {
 #pragma unroll
@@ -325,12 +249,12 @@ __global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    LDS_RD64_TR16(vf[ks][nt][0], vaddr[nt], BO + (t * 32 + 16 * ks) * RB);
-                    LDS_RD64_TR16(vf[ks][nt][1], vaddr[nt], BO + (t * 32 + 16 * ks + 8) * RB);
+                    LDS_RD64_TR16(vf[ks][nt][0], vaddr[nt], BO + (t * 32 + 16 * ks) * PITCH);
+                    LDS_RD64_TR16(vf[ks][nt][1], vaddr[nt], BO + (t * 32 + 16 * ks + 8) * PITCH);
                 }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (ks == 0) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+                if (ks == 0) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(2 * NT) : "memory");
                 else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 bf16x8 pf;
 #pragma unroll
@@ -367,10 +291,13 @@ __global__ __launch_bounds__(512) void k_attn_d128(AttnArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            bf16x4 o;
+            const int d0 = nt * 32 + 8 * g + 4 * half;
+            if (d0 < DH) {
+                bf16x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[nt][4 * g + e] * inv);
-            *(bf16x4*)(O + nt * 32 + 8 * g + 4 * half) = o;
+                for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[nt][4 * g + e] * inv);
+                *(bf16x4*)(O + d0) = o;
+            }
         }
 }
 
@@ -424,15 +351,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if (a.Tq <= 0 || a.B <= 0) return hipSuccess;
     if (a.Tk <= 0) return hipErrorInvalidValue;
     if (a.dtype == LWO_BF16) {
-        dim3 grid((a.Tq + 127) / 128, a.H, a.B);
         switch (a.dh) {
-            case 64: k_attn_bf16<64><<<grid, 256, 0, st>>>(a); break;
-            case 72: k_attn_bf16<72><<<grid, 256, 0, st>>>(a); break;
-            case 128: {
-                dim3 g128((a.Tq + 255) / 256, a.H, a.B);
-                k_attn_d128<<<g128, 512, 0, st>>>(a);
-                break;
-            }
+            case 64: k_attn_tr<64, 4><<<dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st>>>(a); break;
+            case 72: k_attn_tr<72, 4><<<dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st>>>(a); break;
+            case 128: k_attn_tr<128, 8><<<dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st>>>(a); break;
             default: return hipErrorInvalidValue;
         }
     } else {
