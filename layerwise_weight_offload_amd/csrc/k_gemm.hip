@@ -1,19 +1,14 @@
 // Linear layers of the DiT block, Y = A W^T with a fused epilogue (bias,
 // GELU-tanh, gated or plain residual add into the fp32 residual stream).
 //
-// Both kernels below take bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
+// k_gemm_deep takes bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) operands and
-// accumulate in fp32.  Both operands are K-contiguous ([M,K] activations,
+// accumulates in fp32.  Both operands are K-contiguous ([M,K] activations,
 // [N,K] weights), so each lane's MFMA fragment is one or two 16-byte LDS
 // reads from a row.  No split-K: every output is produced by one lane in a
-// fixed order, so results are deterministic run to run.
-// * k_gemm_deep: K rows a multiple of 256 bytes (every block product);
-//   256x256, 256x128, 128x128 or 128x64 tiles by problem size, direct-to-LDS
-//   loads three stages ahead, LDS-staged vector epilogue (details at the
-//   kernel).
-// * k_gemm_mfma: other K; 128x128 tiles (2x2 wavefronts of 64x64), 128
-//   bytes of K per stage, register-staged double-buffered LDS with a 16-byte
-//   row pad.
+// fixed order, so results are deterministic run to run.  Tiles of 256x256,
+// 256x128, 128x128 or 128x64 by problem size; direct-to-LDS loads three
+// stages ahead; LDS-staged vector epilogue (details at the kernel).
 // * k_gemm_f32: fp32 FMA tiles (64x64, 4x4 per thread) for the fp32
 //   workloads, where bf16 rounding would exceed a 1e-4 tolerance.
 #include <type_traits>
@@ -86,9 +81,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 
 // ------------------------------------------------------------------ MFMA tiles (bf16 / fp8)
 
-constexpr int kBKB = 128;             // K bytes per LDS stage: 64 bf16 or 128 fp8 elements
-constexpr int kRowB = kBKB + 16;      // LDS row stride in bytes (16-byte pad)
-
 // Tile index -> (tile row, tile col).  Workgroups are handed to the 8 XCDs
 // round-robin, so consecutive ids land on different L2s; the remap gives each
 // XCD a contiguous run of tiles, and inside that run tiles go in groups of
@@ -107,127 +99,6 @@ __device__ __forceinline__ void tile_of(int pid, int nt_m, int nt_n, int& tm, in
     const int r = t % per_group;
     tm = first_m + r % gsz;
     tn = r / gsz;
-}
-
-// BM x BN output tile per 256-thread workgroup: 2x2 wavefronts, each owning
-// (BM/2) x (BN/2) = TM x TN MFMA 32x32 blocks.
-template <int BM, int BN, bool FP8, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
-    constexpr int TM = BM / 64, TN = BN / 64;        // MFMA blocks per wavefront along M and N
-    constexpr int LA = BM / 32, LW = BN / 32;        // 16-byte global loads per thread per stage
-    constexpr int KS = FP8 ? 2 : 4;                  // MFMA k-steps per stage
-    __shared__ __attribute__((aligned(16))) unsigned char As[2][BM * kRowB];
-    __shared__ __attribute__((aligned(16))) unsigned char Ws[2][BN * kRowB];
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2, l32 = lane % 32, half = lane / 32;
-    int tmi, tni;
-    tile_of(blockIdx.x, (g.M + BM - 1) / BM, (g.N + BN - 1) / BN, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
-    const int esz = FP8 ? 1 : 2;
-    const size_t rowA = (size_t)g.K * esz;          // bytes per row of A and W
-    const unsigned char* A = (const unsigned char*)g.a;
-    const unsigned char* W = (const unsigned char*)g.w;
-    const int ch = tid % 8;                          // 16-byte chunk within the 128-byte stage row
-    intx4 ra[LA], rw[LW];
-    const intx4 z = {0, 0, 0, 0};
-
-    auto gload = [&](int kb) {   // kb: byte offset along K
-#pragma unroll
-        for (int i = 0; i < LA; ++i) {
-            const int r = tid / 8 + 32 * i;
-            ra[i] = (m0 + r < g.M) ? *(const intx4*)(A + (size_t)(m0 + r) * rowA + kb + ch * 16) : z;
-        }
-#pragma unroll
-        for (int i = 0; i < LW; ++i) {
-            const int r = tid / 8 + 32 * i;
-            rw[i] = (n0 + r < g.N) ? *(const intx4*)(W + (size_t)(n0 + r) * rowA + kb + ch * 16) : z;
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i) *(intx4*)&As[buf][(tid / 8 + 32 * i) * kRowB + ch * 16] = ra[i];
-#pragma unroll
-        for (int i = 0; i < LW; ++i) *(intx4*)&Ws[buf][(tid / 8 + 32 * i) * kRowB + ch * 16] = rw[i];
-    };
-
-    floatx16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Fragment of k-step ks: bf16 = one 16-byte read (8 elements), fp8 = two (32 elements).
-    typedef typename std::conditional<FP8, intx8, bf16x8>::type frag_t;
-    auto frag = [&](const unsigned char* base, int row, int ks) -> frag_t {
-        if constexpr (FP8) {
-            const unsigned char* p = base + row * kRowB + ks * 64 + half * 32;
-            const intx4 lo = *(const intx4*)p, hi = *(const intx4*)(p + 16);
-            return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-            return __builtin_bit_cast(bf16x8, *(const intx4*)(base + row * kRowB + ks * 32 + half * 16));
-        }
-    };
-
-    const int nk = (int)(rowA / kBKB);
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * kBKB);
-        const unsigned char* as = As[buf];
-        const unsigned char* ws = Ws[buf];
-        frag_t af[2][TM], bfr[2][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[0][i] = frag(as, wm * (BM / 2) + i * 32 + l32, 0);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[0][j] = frag(ws, wn * (BN / 2) + j * 32 + l32, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int cb = ks & 1, nb = cb ^ 1;
-            if (ks + 1 < KS) {   // read the next k-step's fragments while this one multiplies
-#pragma unroll
-                for (int i = 0; i < TM; ++i) af[nb][i] = frag(as, wm * (BM / 2) + i * 32 + l32, ks + 1);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) bfr[nb][j] = frag(ws, wn * (BN / 2) + j * 32 + l32, ks + 1);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    if constexpr (FP8)   // formats 0/0: e4m3 x e4m3; scale exponents 127 = 2^0
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[cb][i], bfr[cb][j], acc[i][j],
-                                                                                    0, 0, 0, 127, 0, 127);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // Accumulator layout of a 32x32 MFMA block: register r of lane l holds
-    // row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * (BN / 2) + j * 32 + l32;
-            if (n >= g.N) continue;
-            float wsc = 1.0f;
-            if (FP8) wsc = g.w_scale[n / g.w_seg];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (m < g.M) {
-                    float v = acc[i][j][r];
-                    if (FP8) v = v * wsc * g.a_scale[m];
-                    epilogue<EPI, bf16>(g, m, n, v);
-                }
-            }
-        }
 }
 
 // ------------------------------------------------------------------ deep prefetch, direct-to-LDS
@@ -256,20 +127,30 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
-template <int BM, int BN, bool FP8, int EPI>
+template <int BM, int BN, int SB, bool FP8, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     constexpr int TM = BM / 64, TN = BN / 64;
-    constexpr int SB = 64, DIST = 3;                 // stage bytes per row, prefetch distance (4 buffers)
-    constexpr int KS = FP8 ? 1 : 2;                  // MFMA k-steps per stage
-    constexpr int LIA = BM / 64, LIW = BN / 64;      // 16-row load instructions per wavefront per operand
+    constexpr int DIST = 3;                          // prefetch distance (4 buffers); SB = stage bytes per row
+    constexpr int KS = FP8 ? SB / 64 : SB / 32;      // MFMA k-steps per stage
+    constexpr int CPR = SB / 16, RPI = kWave / CPR;  // 16-byte chunks per row, rows per load instruction
+    constexpr int LIA = BM / (4 * RPI), LIW = BN / (4 * RPI);   // load instructions per wavefront per operand
     constexpr int VM = 2 * (LIA + LIW);              // loads of the two stages after the one awaited
+    // Tail stages (a stage count that is not a multiple of four) cost registers
+    // in the large-tile kernels, so only the small-tile ones carry them.
+    constexpr bool TAIL = BM == 128;
     static_assert(BM >= 128 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
+    static_assert(SB == 64 || SB == 128, "stage depth");
+    constexpr int AB = BM * SB, WB = BN * SB;        // bytes of one stage buffer per operand
+    static_assert(4 * (AB + WB) <= 160 * 1024, "LDS");
+    // Chunk c of row r sits at c ^ swz(r): 64-byte rows as described above;
+    // 128-byte rows (r >> 1) & 7 (rows r and r + 1 are half the banks apart).
+    auto swz = [](int r) { return SB == 64 ? swz64(r) : (r >> 1) & 7; };
     // Four buffers per operand as separate arrays, used with compile-time
     // indices (the k loop is unrolled by four): the compiler can then tell the
     // buffer a load fills from the one being read, and does not stall every
     // LDS read on the loads still in flight.
-    __shared__ __attribute__((aligned(1024))) unsigned char A_0[BM * SB], A_1[BM * SB], A_2[BM * SB], A_3[BM * SB];
-    __shared__ __attribute__((aligned(1024))) unsigned char W_0[BN * SB], W_1[BN * SB], W_2[BN * SB], W_3[BN * SB];
+    __shared__ __attribute__((aligned(1024))) unsigned char A_0[AB], A_1[AB], A_2[AB], A_3[AB];
+    __shared__ __attribute__((aligned(1024))) unsigned char W_0[WB], W_1[WB], W_2[WB], W_3[WB];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / 2, wn = wave % 2, l32 = lane % 32, half = lane / 32;
     int tmi, tni;
@@ -282,13 +163,13 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     uint32_t offA[LIA], offW[LIW];
 #pragma unroll
     for (int i = 0; i < LIA; ++i) {
-        const int r = (wave * LIA + i) * 16 + lane / 4;
-        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
+        const int r = (wave * LIA + i) * RPI + lane / CPR;
+        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + (uint32_t)(((lane % CPR) ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < LIW; ++i) {
-        const int r = (wave * LIW + i) * 16 + lane / 4;
-        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + (uint32_t)(((lane % 4) ^ swz64(r)) * 16);
+        const int r = (wave * LIW + i) * RPI + lane / CPR;
+        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + (uint32_t)(((lane % CPR) ^ swz(r)) * 16);
     }
     auto abuf = [&](auto b) -> unsigned char* {
         if constexpr (decltype(b)::value == 0) return A_0;
@@ -308,12 +189,12 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < LIA; ++i)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A0 + offA[i] + kb),
-                                             (__attribute__((address_space(3))) void*)(ad + (wave * LIA + i) * 16 * SB),
+                                             (__attribute__((address_space(3))) void*)(ad + (wave * LIA + i) * RPI * SB),
                                              16, 0, 0);
 #pragma unroll
         for (int i = 0; i < LIW; ++i)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W0 + offW[i] + kb),
-                                             (__attribute__((address_space(3))) void*)(wd + (wave * LIW + i) * 16 * SB),
+                                             (__attribute__((address_space(3))) void*)(wd + (wave * LIW + i) * RPI * SB),
                                              16, 0, 0);
     };
 
@@ -332,19 +213,19 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     auto reads = [&](int slot, const unsigned char* as, const unsigned char* ws, int ks) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * (BM / 2) + i * 32 + l32, sw = swz64(row);
+            const int row = wm * (BM / 2) + i * 32 + l32, sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
-                const int c = FP8 ? half * 2 + q : ks * 2 + half;
+                const int c = FP8 ? ks * 4 + half * 2 + q : ks * 2 + half;
                 fa[slot][i][q] = lds_read16(as + row * SB + ((c ^ sw) * 16));
             }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn * (BN / 2) + j * 32 + l32, sw = swz64(row);
+            const int row = wn * (BN / 2) + j * 32 + l32, sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
-                const int c = FP8 ? half * 2 + q : ks * 2 + half;
+                const int c = FP8 ? ks * 4 + half * 2 + q : ks * 2 + half;
                 fb[slot][j][q] = lds_read16(ws + row * SB + ((c ^ sw) * 16));
             }
         }
@@ -400,7 +281,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) {
                 reads((ks + 1) & 1, as, ws, ks + 1);
-                lds_wait(ks & 1, NR);   // bf16 only (fp8 has one k-step per stage)
+                lds_wait(ks & 1, NR);
             } else {
                 lds_wait(ks & 1, 0);
             }
@@ -411,11 +292,20 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, min(1, nk - 1) * SB);
     issue(std::integral_constant<int, 2>{}, min(2, nk - 1) * SB);
-    for (int kt = 0; kt < nk; kt += 4) {   // nk % 4 == 0 (launcher); past the end issue() re-loads the last stage
+    // Stage kt uses buffer kt % 4; past the end issue() re-loads the last stage
+    // into a buffer no later stage reads.
+    // Without TAIL the launcher guarantees nk % 4 == 0.
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
         stage(std::integral_constant<int, 0>{}, kt);
         stage(std::integral_constant<int, 1>{}, kt + 1);
         stage(std::integral_constant<int, 2>{}, kt + 2);
         stage(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    if constexpr (TAIL) {
+        if (kt < nk) stage(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) stage(std::integral_constant<int, 1>{}, kt + 1);
+        if (kt + 2 < nk) stage(std::integral_constant<int, 2>{}, kt + 2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing re-loads before the workgroup ends
     __syncthreads();                                    // every wavefront is done with the stage buffers
@@ -427,7 +317,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     // the residual forms the loads of up to eight passes are issued before
     // any store.
     constexpr int CW = 32 * TN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
-    static_assert(32 * CW * 4 <= BM * SB, "epilogue staging fits one A buffer");
+    static_assert(32 * CW * 4 <= AB, "epilogue staging fits one A buffer");
     float* lds = (float*)(wave == 0 ? A_0 : wave == 1 ? A_1 : wave == 2 ? A_2 : A_3);
     const int c4 = lane % CH, rr = lane / CH;           // float4 column chunk and row-in-pass of this lane
     const int nb = n0 + wn * CW + 4 * c4;               // its first output column
@@ -495,13 +385,6 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
 
 // ------------------------------------------------------------------ launch
 
-template <int BM, int BN, int EPI>
-static void launch_mfma(const GemmArgs& g, hipStream_t st) {
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    if (g.dtype == LWO_BF16) k_gemm_mfma<BM, BN, false, EPI><<<tiles, 256, 0, st>>>(g);
-    else k_gemm_mfma<BM, BN, true, EPI><<<tiles, 256, 0, st>>>(g);
-}
-
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     if (g.dtype == LWO_F32) {
@@ -509,30 +392,31 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
         k_gemm_f32<EPI><<<grid, 256, 0, st>>>(g);
         return hipGetLastError();
     }
-    const size_t row_bytes = (size_t)g.K * (g.dtype == LWO_BF16 ? 2 : 1);
-    if (row_bytes % 256) {   // the deep kernels unroll the k loop by four 64-byte stages
-        launch_mfma<128, 128, EPI>(g, st);
-        return hipGetLastError();
-    }
+    // K rows are a multiple of 128 bytes (argument checks); the 256-row tiles
+    // unroll the k loop by four 64-byte stages without a tail.
+    const bool rows256 = (size_t)g.K * (g.dtype == LWO_BF16 ? 2 : 1) % 256 == 0;
     auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
     const bool f8 = g.dtype != LWO_BF16;
     // Tile choice (measured on the block shapes): the largest tile that still
     // gives most CUs a workgroup.  256x256 and 256x128 hold one workgroup per
-    // CU (LDS), 128x128 two, 128x64 three.
+    // CU (LDS), 128x128 two (64-byte stages) or one (128-byte stages), 128x64 one.
     const int t256 = tiles(256, 256), t256x128 = tiles(256, 128), t128 = tiles(128, 128);
-    if (t256 >= 256) {
-        if (f8) k_gemm_deep<256, 256, true, EPI><<<t256, 256, 0, st>>>(g);
-        else k_gemm_deep<256, 256, false, EPI><<<t256, 256, 0, st>>>(g);
-    } else if (t256x128 >= 192 && t256x128 <= 256) {
-        if (f8) k_gemm_deep<256, 128, true, EPI><<<t256x128, 256, 0, st>>>(g);
-        else k_gemm_deep<256, 128, false, EPI><<<t256x128, 256, 0, st>>>(g);
-    } else if (t128 >= 128) {
-        if (f8) k_gemm_deep<128, 128, true, EPI><<<t128, 256, 0, st>>>(g);
-        else k_gemm_deep<128, 128, false, EPI><<<t128, 256, 0, st>>>(g);
+    if (rows256 && t256 >= 256) {
+        if (f8) k_gemm_deep<256, 256, 64, true, EPI><<<t256, 256, 0, st>>>(g);
+        else k_gemm_deep<256, 256, 64, false, EPI><<<t256, 256, 0, st>>>(g);
+    } else if (rows256 && t256x128 >= 192 && t256x128 <= 256) {
+        if (f8) k_gemm_deep<256, 128, 64, true, EPI><<<t256x128, 256, 0, st>>>(g);
+        else k_gemm_deep<256, 128, 64, false, EPI><<<t256x128, 256, 0, st>>>(g);
+    } else if (t128 > 256) {   // two 64 KB workgroups per CU
+        if (f8) k_gemm_deep<128, 128, 64, true, EPI><<<t128, 256, 0, st>>>(g);
+        else k_gemm_deep<128, 128, 64, false, EPI><<<t128, 256, 0, st>>>(g);
+    } else if (t128 >= 128) {  // one workgroup per CU: 128-byte stages keep more bytes in flight
+        if (f8) k_gemm_deep<128, 128, 128, true, EPI><<<t128, 256, 0, st>>>(g);
+        else k_gemm_deep<128, 128, 128, false, EPI><<<t128, 256, 0, st>>>(g);
     } else {
         const int t = tiles(128, 64);
-        if (f8) k_gemm_deep<128, 64, true, EPI><<<t, 256, 0, st>>>(g);
-        else k_gemm_deep<128, 64, false, EPI><<<t, 256, 0, st>>>(g);
+        if (f8) k_gemm_deep<128, 64, 128, true, EPI><<<t, 256, 0, st>>>(g);
+        else k_gemm_deep<128, 64, 128, false, EPI><<<t, 256, 0, st>>>(g);
     }
     return hipGetLastError();
 }
