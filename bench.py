@@ -55,6 +55,47 @@ def pinned_peak(torch, nbytes: int, stream, reps: int = 10) -> float:
     return best
 
 
+def copy_calibration(torch) -> int:
+    """Three dispatches of a plain streaming kernel (y = 1.0 * x over 2^28 fp32):
+    each reads and writes exactly 1 GiB, so what FETCH_SIZE / WRITE_SIZE report
+    for it gives the scale from those counters to HBM bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise y = 1.0 * x", "dispatches": 3, "read_bytes": 4 * n,
+                      "write_bytes": 4 * n}), flush=True)
+    return 0
+
+
+def committed_traffic(label: str, workload: str):
+    """HBM bytes per launch of `label` on `workload` from a committed rocprofv3
+    counter summary (profiles/*.md, a fenced json block), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for blk in re.findall(r"```json\n(.*?)\n```", open(path).read(), re.S):
+            try:
+                rec = json.loads(blk)
+            except ValueError:
+                continue
+            if rec.get("label") != label or rec.get("workload") != workload:
+                continue
+            h = hashlib.sha256()
+            for src in rec.get("sources", []):
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    h.update(f.read())
+            if h.hexdigest() != rec.get("sources_sha256"):
+                return None
+            return rec.get("hbm_bytes_per_launch")
+    return None
+
+
 def block_flops(w) -> float:
     """Algorithmic FLOPs of one block: 2MNK per linear, 4 B H Tq Tk d per attention."""
     B, T, D, F, Tc = w.batch, w.tokens, w.hidden, w.ffn, w.ctx_tokens
@@ -118,6 +159,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of known size (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -133,6 +176,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(torch)
     w = lwo_synth.get(args.workload)
     k = w.resident_prefix if args.resident_prefix is None else args.resident_prefix
     L = w.n_blocks
@@ -233,7 +278,8 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof.update({"kernel": dom["name"], "avg_launch_ms": round(avg_ms, 4), "launches_per_step": dom["launches"] // steps_timed,
-                 "traffic": None})
+                 "algorithmic_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
+                 "traffic": committed_traffic(dom["name"], w.name)})
 
     kernels = {kk["name"]: {"ms_per_step": round(kk["total_ms"] / steps_timed, 4),
                             "launches_per_step": kk["launches"] // steps_timed,

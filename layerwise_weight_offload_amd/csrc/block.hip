@@ -62,6 +62,11 @@ void workspace_free(Workspace* ws) {
 
 // ------------------------------------------------------------------ kernel timing
 
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
 hipEvent_t KernelTimer::get() {
     hipEvent_t e = nullptr;
     if (!pool.empty()) { e = pool.back(); pool.pop_back(); return e; }
@@ -81,7 +86,12 @@ lwo_status KernelTimer::collect() {
     for (Rec& r : pending) {
         LWO_HIP_TRY(hipEventSynchronize(r.b));
         float ms = 0.0f;
-        LWO_HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {   // the operation launched nothing (empty shape)
+            (void)hipGetLastError();
+            pool.push_back(r.a);
+            pool.push_back(r.b);
+            continue;
+        }
         Agg& a = agg[r.cls];
         a.launches++;
         a.ms += ms;
@@ -162,14 +172,15 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
         g.w_seg = fused ? D : g.N;
         g.a_scale = a_scale;
     };
-    // Timing wrapper: events around one launch, attributed to the kernel symbol `name`.
+    // Timing wrapper: the one kernel `launch` enqueues records its own start and
+    // end into two events, attributed to the kernel class `name`.
     auto timed = [&](const char* name, double flops, double bytes, auto&& launch) -> hipError_t {
         if (!kt || !kt->on) return launch();
         KernelTimer::Rec r{kt->cls(name), kt->get(), kt->get(), flops, bytes};
         if (!r.a || !r.b) return hipErrorOutOfMemory;
-        hipError_t e = hipEventRecord(r.a, st);
-        if (e == hipSuccess) e = launch();
-        if (e == hipSuccess) e = hipEventRecord(r.b, st);
+        launch_events() = LaunchEvents{r.a, r.b};
+        const hipError_t e = launch();
+        launch_events() = LaunchEvents{};
         kt->pending.push_back(r);
         return e;
     };

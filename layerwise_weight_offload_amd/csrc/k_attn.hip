@@ -352,17 +352,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if (a.Tk <= 0) return hipErrorInvalidValue;
     if (a.dtype == LWO_BF16) {
         switch (a.dh) {
-            case 64: k_attn_tr<64, 4><<<dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st>>>(a); break;
-            case 72: k_attn_tr<72, 4><<<dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st>>>(a); break;
-            case 128: k_attn_tr<128, 8><<<dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st>>>(a); break;
+            case 64: LWO_KL((k_attn_tr<64, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a); break;
+            case 72: LWO_KL((k_attn_tr<72, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a); break;
+            case 128: LWO_KL((k_attn_tr<128, 8>), dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     } else {
         dim3 grid((a.Tq + 63) / 64, a.H, a.B);
         switch (a.dh) {
-            case 64: k_attn_f32<64><<<grid, 64, 0, st>>>(a); break;
-            case 72: k_attn_f32<72><<<grid, 64, 0, st>>>(a); break;
-            case 128: k_attn_f32<128><<<grid, 64, 0, st>>>(a); break;
+            case 64: LWO_KL((k_attn_f32<64>), grid, 64, 0, st, a); break;
+            case 72: LWO_KL((k_attn_f32<72>), grid, 64, 0, st, a); break;
+            case 128: LWO_KL((k_attn_f32<128>), grid, 64, 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     }

@@ -389,7 +389,7 @@ template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     if (g.dtype == LWO_F32) {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
-        k_gemm_f32<EPI><<<grid, 256, 0, st>>>(g);
+        LWO_KL((k_gemm_f32<EPI>), grid, 256, 0, st, g);
         return hipGetLastError();
     }
     // K rows are a multiple of 128 bytes (argument checks); the 256-row tiles
@@ -402,21 +402,21 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     // CU (LDS), 128x128 two (64-byte stages) or one (128-byte stages), 128x64 one.
     const int t256 = tiles(256, 256), t256x128 = tiles(256, 128), t128 = tiles(128, 128);
     if (rows256 && t256 >= 256) {
-        if (f8) k_gemm_deep<256, 256, 64, true, EPI><<<t256, 256, 0, st>>>(g);
-        else k_gemm_deep<256, 256, 64, false, EPI><<<t256, 256, 0, st>>>(g);
+        if (f8) LWO_KL((k_gemm_deep<256, 256, 64, true, EPI>), t256, 256, 0, st, g);
+        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI>), t256, 256, 0, st, g);
     } else if (rows256 && t256x128 >= 192 && t256x128 <= 256) {
-        if (f8) k_gemm_deep<256, 128, 64, true, EPI><<<t256x128, 256, 0, st>>>(g);
-        else k_gemm_deep<256, 128, 64, false, EPI><<<t256x128, 256, 0, st>>>(g);
+        if (f8) LWO_KL((k_gemm_deep<256, 128, 64, true, EPI>), t256x128, 256, 0, st, g);
+        else LWO_KL((k_gemm_deep<256, 128, 64, false, EPI>), t256x128, 256, 0, st, g);
     } else if (t128 > 256) {   // two 64 KB workgroups per CU
-        if (f8) k_gemm_deep<128, 128, 64, true, EPI><<<t128, 256, 0, st>>>(g);
-        else k_gemm_deep<128, 128, 64, false, EPI><<<t128, 256, 0, st>>>(g);
+        if (f8) LWO_KL((k_gemm_deep<128, 128, 64, true, EPI>), t128, 256, 0, st, g);
+        else LWO_KL((k_gemm_deep<128, 128, 64, false, EPI>), t128, 256, 0, st, g);
     } else if (t128 >= 128) {  // one workgroup per CU: 128-byte stages keep more bytes in flight
-        if (f8) k_gemm_deep<128, 128, 128, true, EPI><<<t128, 256, 0, st>>>(g);
-        else k_gemm_deep<128, 128, 128, false, EPI><<<t128, 256, 0, st>>>(g);
+        if (f8) LWO_KL((k_gemm_deep<128, 128, 128, true, EPI>), t128, 256, 0, st, g);
+        else LWO_KL((k_gemm_deep<128, 128, 128, false, EPI>), t128, 256, 0, st, g);
     } else {
         const int t = tiles(128, 64);
-        if (f8) k_gemm_deep<128, 64, 128, true, EPI><<<t, 256, 0, st>>>(g);
-        else k_gemm_deep<128, 64, 128, false, EPI><<<t, 256, 0, st>>>(g);
+        if (f8) LWO_KL((k_gemm_deep<128, 64, 128, true, EPI>), t, 256, 0, st, g);
+        else LWO_KL((k_gemm_deep<128, 64, 128, false, EPI>), t, 256, 0, st, g);
     }
     return hipGetLastError();
 }

@@ -44,15 +44,15 @@ static int grid_for(size_t n, int per_block) {
 
 hipError_t launch_to_f32(const void* x, int dt, float* xr, size_t n, hipStream_t st) {
     size_t n4 = n / 4;
-    if (dt == LWO_F32) k_to_f32<float><<<grid_for(n4, 256), 256, 0, st>>>((const float*)x, xr, n4);
-    else k_to_f32<bf16><<<grid_for(n4, 256), 256, 0, st>>>((const bf16*)x, xr, n4);
+    if (dt == LWO_F32) LWO_KL((k_to_f32<float>), grid_for(n4, 256), 256, 0, st, (const float*)x, xr, n4);
+    else LWO_KL((k_to_f32<bf16>), grid_for(n4, 256), 256, 0, st, (const bf16*)x, xr, n4);
     return hipGetLastError();
 }
 
 hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream_t st) {
     size_t n4 = n / 4;
-    if (dt == LWO_F32) k_from_f32<float><<<grid_for(n4, 256), 256, 0, st>>>(xr, (float*)x, n4);
-    else k_from_f32<bf16><<<grid_for(n4, 256), 256, 0, st>>>(xr, (bf16*)x, n4);
+    if (dt == LWO_F32) LWO_KL((k_from_f32<float>), grid_for(n4, 256), 256, 0, st, xr, (float*)x, n4);
+    else LWO_KL((k_from_f32<bf16>), grid_for(n4, 256), 256, 0, st, xr, (bf16*)x, n4);
     return hipGetLastError();
 }
 
@@ -90,15 +90,15 @@ __global__ void k_mod_video(const T* __restrict__ cond, const T* __restrict__ ta
 hipError_t launch_mod_dit(const void* cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st) {
     dim3 grid((6 * D + 3) / 4);
-    if (dt == LWO_F32) k_mod_dit<float><<<grid, 256, 0, st>>>((const float*)cond, (const float*)w, (const float*)b, mod, B, D);
-    else k_mod_dit<bf16><<<grid, 256, 0, st>>>((const bf16*)cond, (const bf16*)w, (const bf16*)b, mod, B, D);
+    if (dt == LWO_F32) LWO_KL((k_mod_dit<float>), grid, 256, 0, st, (const float*)cond, (const float*)w, (const float*)b, mod, B, D);
+    else LWO_KL((k_mod_dit<bf16>), grid, 256, 0, st, (const bf16*)cond, (const bf16*)w, (const bf16*)b, mod, B, D);
     return hipGetLastError();
 }
 
 hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* mod, int B, int D, hipStream_t st) {
     int g = grid_for((size_t)B * 6 * D, 256);
-    if (dt == LWO_F32) k_mod_video<float><<<g, 256, 0, st>>>((const float*)cond, (const float*)table, mod, B, D);
-    else k_mod_video<bf16><<<g, 256, 0, st>>>((const bf16*)cond, (const bf16*)table, mod, B, D);
+    if (dt == LWO_F32) LWO_KL((k_mod_video<float>), g, 256, 0, st, (const float*)cond, (const float*)table, mod, B, D);
+    else LWO_KL((k_mod_video<bf16>), g, 256, 0, st, (const bf16*)cond, (const bf16*)table, mod, B, D);
     return hipGetLastError();
 }
 
@@ -180,7 +180,7 @@ static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float*
     dim3 grid((M + 3) / 4);
 #define LWO_LN_CASE(NV)                                                                                     \
     if (need <= NV) {                                                                                       \
-        k_ln<OUT, MOD, NV><<<grid, 256, 0, st>>>(xr, M, D, T, mod, shc, scc, out, out_scale);              \
+        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, 0, st, xr, M, D, T, mod, shc, scc, out, out_scale);              \
         return hipGetLastError();                                                                           \
     }
     LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(5) LWO_LN_CASE(8)
@@ -237,7 +237,7 @@ static hipError_t rms_dispatch(T* qkv, int M, int D, const T* gq, const T* gk, h
     dim3 grid((2 * M + 3) / 4);
 #define LWO_RMS_CASE(NV)                                                          \
     if (need <= NV) {                                                             \
-        k_rmsnorm_qk<T, NV><<<grid, 256, 0, st>>>(qkv, M, D, gq, gk);             \
+        LWO_KL((k_rmsnorm_qk<T, NV>), grid, 256, 0, st, qkv, M, D, gq, gk);             \
         return hipGetLastError();                                                 \
     }
     LWO_RMS_CASE(1) LWO_RMS_CASE(2) LWO_RMS_CASE(4) LWO_RMS_CASE(8) LWO_RMS_CASE(12) LWO_RMS_CASE(16)
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
 }
 
 hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st) {
-    k_quant_rows<<<(M + 3) / 4, 256, 0, st>>>((const bf16*)in, M, N, codes, scales);
+    LWO_KL((k_quant_rows), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales);
     return hipGetLastError();
 }
 
@@ -316,17 +316,17 @@ hipError_t launch_checksum(const void* dev, uint64_t bytes, uint64_t* acc, hipSt
     const uint64_t n = bytes / 8;
     int g = (int)((n + 256 * 16 - 1) / (256 * 16));
     g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
-    k_checksum<<<g, 256, 0, st>>>((const uint64_t*)dev, n, (unsigned long long*)acc);
+    LWO_KL((k_checksum), g, 256, 0, st, (const uint64_t*)dev, n, (unsigned long long*)acc);
     return hipGetLastError();
 }
 
 hipError_t launch_checksum_compare(uint64_t* acc, uint64_t expect, hipStream_t st) {
-    k_checksum_compare<<<1, 64, 0, st>>>((unsigned long long*)acc, (unsigned long long)expect);
+    LWO_KL((k_checksum_compare), 1, 64, 0, st, (unsigned long long*)acc, (unsigned long long)expect);
     return hipGetLastError();
 }
 
 hipError_t launch_zero_u64(uint64_t* p, int n, hipStream_t st) {
-    k_zero_u64<<<(n + 63) / 64, 64, 0, st>>>((unsigned long long*)p, n);
+    LWO_KL((k_zero_u64), (n + 63) / 64, 64, 0, st, (unsigned long long*)p, n);
     return hipGetLastError();
 }
 

@@ -2,10 +2,22 @@
 // the launch status; shapes are checked by the callers in block.hip).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lwo {
+
+// Events the next kernel launch records at its own start and end (the
+// dispatch's timestamps, so no gap between launches is counted).  The kernel
+// timer sets them around exactly one launch; null otherwise (plain launch).
+struct LaunchEvents { hipEvent_t start = nullptr, stop = nullptr; };
+LaunchEvents& launch_events();   // per host thread
+
+// kern<<<grid, block, shmem, st>>>(args...), with the launch events above.
+#define LWO_KL(kern, grid, block, shmem, st, ...)                                                  \
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), (shmem), (st), ::lwo::launch_events().start, \
+                          ::lwo::launch_events().stop, 0u, __VA_ARGS__)
 
 // Epilogue of a linear layer Y = A W^T: v = acc (* w_scale[n / seg] * a_scale[m]) + bias[n], then
 //   EPI_STORE  out[m, n] = v                       (act dtype)
