@@ -58,23 +58,64 @@ hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream
 
 // ------------------------------------------------------------------ adaLN modulation
 
-// DiT kind: mod[b, n] = sum_k SiLU(cond[b, k]) W[n, k] + bias[n], n < 6D (one wavefront per n).
+// DiT kind: mod[b, n] = sum_k SiLU(cond[b, k]) W[n, k] + bias[n], n < 6D.
+// A GEMV over the [6D, D] weight, bound by reading it once: 16 lanes own one
+// row, a workgroup owns 16 rows.  K goes in windows of 16 16-byte loads per
+// lane; each window's loads are issued before SiLU(cond) of the window is
+// computed into LDS (for up to four batches), so the two overlap.
 template <typename T>
 __global__ __launch_bounds__(256) void k_mod_dit(const T* __restrict__ cond, const T* __restrict__ w,
                                                  const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
-    const int n = blockIdx.x * 4 + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    if (n >= 6 * D) return;
-    const T* wr = w + (size_t)n * D;
-    for (int b = 0; b < B; ++b) {
-        const T* c = cond + (size_t)b * D;
-        float s = 0.0f;
-        for (int k = 4 * lane; k < D; k += 4 * kWave) {
-            float4 wv = load4(wr + k), cv = load4(c + k);
-            s += silu(cv.x) * wv.x + silu(cv.y) * wv.y + silu(cv.z) * wv.z + silu(cv.w) * wv.w;
+    constexpr int EV = 16 / sizeof(T);                  // elements per 16-byte load (8 bf16, 4 f32)
+    constexpr int CL = 16, WIN = CL * 16 * EV;          // loads per lane per window, window elements
+    __shared__ float sc[4][WIN];
+    const int n = blockIdx.x * 16 + threadIdx.x / 16, l16 = threadIdx.x % 16;
+    const T* wr = w + (size_t)min(n, 6 * D - 1) * D;
+    for (int b0 = 0; b0 < B; b0 += 4) {
+        const int nb = min(4, B - b0);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < D; k0 += WIN) {
+            intx4 raw[CL];
+#pragma unroll
+            for (int i = 0; i < CL; ++i) {
+                const int k = k0 + (i * 16 + l16) * EV;
+                raw[i] = k < D ? *(const intx4*)(wr + k) : intx4{0, 0, 0, 0};
+            }
+            const int wn = min(WIN, D - k0);
+            __syncthreads();                            // the previous window's reads are done
+            for (int i = threadIdx.x; i < nb * WIN; i += 256) {
+                const int j = i / WIN, kk = i % WIN;
+                if (kk < wn) sc[j][kk] = silu(to_f(cond[(size_t)(b0 + j) * D + k0 + kk]));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < CL; ++i) {
+                const int kk = (i * 16 + l16) * EV;
+                if (k0 + kk >= D) break;
+                float wv[EV];
+                if constexpr (EV == 8) {
+                    const bf16x8 v = __builtin_bit_cast(bf16x8, raw[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) wv[e] = (float)v[e];
+                } else {
+                    const float4 v = __builtin_bit_cast(float4, raw[i]);
+                    wv[0] = v.x; wv[1] = v.y; wv[2] = v.z; wv[3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j >= nb) break;
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) acc[j] = fmaf(wv[e], sc[j][kk + e], acc[j]);
+                }
+            }
         }
-        s = wave_sum(s);
-        if (lane == 0) mod[(size_t)b * 6 * D + n] = s + to_f(bias[n]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = acc[j];
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            if (l16 == 0 && n < 6 * D && j < nb) mod[(size_t)(b0 + j) * 6 * D + n] = v + to_f(bias[n]);
+        }
     }
 }
 
@@ -89,7 +130,8 @@ __global__ void k_mod_video(const T* __restrict__ cond, const T* __restrict__ ta
 
 hipError_t launch_mod_dit(const void* cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st) {
-    dim3 grid((6 * D + 3) / 4);
+    if (D < 8 || D % 8) return hipErrorInvalidValue;
+    const dim3 grid((6 * D + 15) / 16);
     if (dt == LWO_F32) LWO_KL((k_mod_dit<float>), grid, 256, 0, st, (const float*)cond, (const float*)w, (const float*)b, mod, B, D);
     else LWO_KL((k_mod_dit<bf16>), grid, 256, 0, st, (const bf16*)cond, (const bf16*)w, (const bf16*)b, mod, B, D);
     return hipGetLastError();
