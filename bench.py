@@ -159,6 +159,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--host-mode", choices=("pin_copy", "staged"), default="pin_copy",
+                    help="pin_copy: pinned host extents; staged: pageable extents packed through two pinned "
+                         "staging slots")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -195,8 +198,16 @@ def main() -> int:
             log(f"packed block {b + 1}/{L}")
 
     t0 = time.perf_counter()
-    store = lwo.build_block_store(desc, fill=fill)
-    log(f"built {L} x {ext / 1e6:.2f} MB extents in {time.perf_counter() - t0:.1f} s")
+    if args.host_mode == "staged":
+        pageable = []
+        for b in range(L):
+            buf = np.empty(ext, np.uint8)   # ordinary pageable host memory
+            fill(b, buf.ctypes.data, ext)
+            pageable.append(buf)
+        store = lwo.build_block_store(desc, extents=pageable, host_mode=lwo.HOST_STAGED)
+    else:
+        store = lwo.build_block_store(desc, fill=fill)
+    log(f"built {L} x {ext / 1e6:.2f} MB extents ({args.host_mode}) in {time.perf_counter() - t0:.1f} s")
 
     dt = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     xs, cs, cxs = lwo_synth.step_inputs(w)
@@ -300,7 +311,7 @@ def main() -> int:
         "config": {"workload": w.name, "kind": w.kind, "blocks": L, "hidden": w.hidden, "heads": w.heads,
                    "ffn": w.ffn, "batch": w.batch, "tokens": w.tokens, "ctx_tokens": w.ctx_tokens,
                    "act_dtype": w.act_dtype, "linear_dtype": w.linear_dtype, "resident_prefix": k,
-                   "streamed_blocks": m, "host_mode": "pin_copy", "extent_bytes": ext},
+                   "streamed_blocks": m, "host_mode": args.host_mode, "extent_bytes": ext},
         "resident_ms": round(t_res, 3),
         "streamed_over_resident": round(t_str / t_res, 4),
         "h2d_gbps": round(h2d_gbps, 2),
@@ -313,6 +324,8 @@ def main() -> int:
         "block_tflops": round(block_tflops, 2),
         "block_mfma_frac": round(block_tflops / MFMA_PEAK_TFLOPS[lin_dt if lin_dt != "fp8" else "bf16"], 4),
         "h2d_copies_total": st.h2d_copies,
+        "pack_gbps": round(st.pack_bytes / (st.pack_ms * 1e-3) / 1e9, 2) if st.pack_ms > 0 else None,
+        "pack_threads": st.pack_threads or None,
         "build_s": round(st.build_ms / 1e3, 2),
         "roofline": roof,
         "kernels": kernels,

@@ -73,7 +73,7 @@ typedef enum lwo_status {
 
 typedef enum lwo_dtype { LWO_F32 = 0, LWO_BF16 = 1, LWO_FP8_E4M3 = 2 } lwo_dtype;
 typedef enum lwo_block_kind { LWO_KIND_DIT = 0, LWO_KIND_VIDEO = 1 } lwo_block_kind;
-typedef enum lwo_host_mode { LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1 } lwo_host_mode;
+typedef enum lwo_host_mode { LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1, LWO_HOST_STAGED = 2 } lwo_host_mode;
 
 /* Shape of the block stack and of one denoise step's activations.
  * Constraints (LWO_EINVAL otherwise): n_blocks >= 1; hidden = heads * head
@@ -106,8 +106,8 @@ typedef struct lwo_tensor_info {
 /* Where build takes each block's flat extent from.
  *   extents != NULL: extents[b] points to extent_bytes of host memory in the
  *     layout above.  PIN_COPY reads them during the call only.  REGISTER
- *     borrows them until destroy (they must be page-aligned, immutable and
- *     stay mapped until lwo_destroy_block_store returns).
+ *     and STAGED borrow them until destroy (immutable, mapped until
+ *     lwo_destroy_block_store returns; REGISTER needs them page-aligned).
  *   extents == NULL (PIN_COPY only): fill(user, b, dst, extent_bytes) is
  *     called once per block, in order, to write block b's extent into the
  *     store's pinned host memory dst (e.g. with lwo_pack_block); a non-zero
@@ -135,6 +135,11 @@ typedef struct lwo_stats {
     int32_t host_mode;           /* lwo_host_mode in effect */
     int32_t validation;          /* 1 if per-block checksums run before each block */
     double build_ms;             /* wall time of lwo_build_block_store */
+    uint64_t staging_bytes;      /* STAGED: the two pinned staging slots */
+    uint64_t pack_bytes;         /* STAGED: bytes packed host -> staging (total) */
+    double pack_ms;              /* STAGED: host wall time spent packing (total) */
+    int32_t pack_threads;        /* STAGED: threads that pack one extent */
+    int32_t reserved;
 } lwo_stats;
 
 /* --- layout and packing (host only, no GPU needed) ---------------------- */
@@ -191,12 +196,23 @@ typedef struct lwo_store lwo_store;   /* opaque */
 /* [LW], [DLO] "Startup and runtime sequence": set up the host weight store
  * (PIN_COPY: one hipHostMalloc extent per block filled from src; REGISTER:
  * the caller's extents registered read-only through lwo_register_ranges with
- * hipHostRegister, all-or-nothing within register_budget bytes), the device
+ * hipHostRegister, all-or-nothing within register_budget bytes; STAGED, see
+ * below), the device
  * arena (two slots of extent_bytes; no resident prefix), the activation
  * workspace, a non-blocking copy stream at default priority and the
  * readiness events, then prime block 0 into slot 0.  On `device` (HIP
  * ordinal).  On any failure everything allocated so far is released and
- * *out is NULL. */
+ * *out is NULL.
+ * [DLO] "Host backing and transfer composition", "Runtime cache": STAGED
+ * borrows the caller's pageable extents (e.g. an mmap of a flat block file)
+ * and allocates two pinned staging slots of extent_bytes; every block copy
+ * first waits until the device copy last issued from the next staging slot
+ * has finished, packs the extent into it on the host (split over
+ * pack_threads threads; the calling thread blocks meanwhile) and then copies
+ * it to the device on the copy stream.  REGISTER with register_budget == 0,
+ * or whose registration fails and is rolled back (LWO_EBUDGET,
+ * LWO_EREGISTER), continues as STAGED; lwo_stats.host_mode reports the mode
+ * in effect.  A failed rollback (LWO_EROLLBACK) still fails the build. */
 lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src,
                                  int32_t host_mode, uint64_t register_budget, int32_t device,
                                  lwo_store** out);

@@ -18,7 +18,7 @@ _lib = C.CDLL(LIB_PATH)
 # enums (include/lwo.h)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KIND_DIT, KIND_VIDEO = 0, 1
-HOST_PIN_COPY, HOST_REGISTER = 0, 1
+HOST_PIN_COPY, HOST_REGISTER, HOST_STAGED = 0, 1, 2
 STATUS = {0: "LWO_OK", 1: "LWO_EINVAL", 2: "LWO_ENOMEM", 3: "LWO_EHIP", 4: "LWO_EBUDGET",
           5: "LWO_EREGISTER", 6: "LWO_EROLLBACK", 7: "LWO_ESTATE", 8: "LWO_ECHECKSUM"}
 
@@ -56,7 +56,8 @@ class _Stats(C.Structure):
                                           "host_bytes", "h2d_copies", "h2d_bytes", "steps", "checksum_mismatches",
                                           "registered_ranges", "registered_bytes")] + \
                [(n, C.c_int32) for n in ("resident_prefix", "head_slot", "host_mode", "validation")] + \
-               [("build_ms", C.c_double)]
+               [("build_ms", C.c_double), ("staging_bytes", C.c_uint64), ("pack_bytes", C.c_uint64),
+                ("pack_ms", C.c_double), ("pack_threads", C.c_int32), ("reserved", C.c_int32)]
 
 
 class _KStat(C.Structure):
@@ -250,6 +251,11 @@ class Stats:
     host_mode: int
     validation: int
     build_ms: float
+    staging_bytes: int
+    pack_bytes: int
+    pack_ms: float
+    pack_threads: int
+    reserved: int
 
 
 class Store:
@@ -340,7 +346,8 @@ class Store:
 def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,
                       register_budget: int = 0, device: int = 0) -> Store:
     """extents: list of host buffers/addresses (one per block), or fill(b, dst_addr, nbytes) -> None
-    writing block b's flat extent into the store's pinned memory."""
+    writing block b's flat extent into the store's pinned memory.  REGISTER and STAGED borrow the
+    extents: the returned store keeps the Python objects alive until it is destroyed."""
     src = _Source()
     keep = []
     if extents is not None:
@@ -364,4 +371,4 @@ def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int =
         src.fill = cb
     h = C.c_void_p()
     _check(_lib_build(C.byref(desc._c()), C.byref(src), host_mode, register_budget, device, C.byref(h)))
-    return Store(h, desc, keepalive=keep if host_mode == HOST_REGISTER else None)
+    return Store(h, desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)

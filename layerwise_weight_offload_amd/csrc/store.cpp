@@ -18,22 +18,99 @@
 //  * "CPU Offloading", "Cross-strategy invariants": device storage is not
 //    reused until dependent compute or transfer work is complete; "Shared
 //    lifecycle": a failed enable leaves no partial state.
+//  * "Distributed Layerwise Offload", "Host backing and transfer
+//    composition" and "Runtime cache": with pageable (e.g. mmap) host
+//    storage and no registration, every streamed block is packed into one of
+//    two bounded pinned host staging slots and copied from there; a zero
+//    registration budget or a failed (rolled back) registration keeps that
+//    staging path.
 #include <algorithm>
 #include <chrono>
+#include <condition_variable>
 #include <cstring>
+#include <mutex>
 #include <thread>
 
 #include "lwo_internal.h"
 
 using namespace lwo;
 
+// Host copy workers for STAGED mode: one extent copy is split into equal
+// parts, one per worker plus the calling thread, which waits for all of them.
+struct PackPool {
+    std::vector<std::thread> th;
+    std::mutex mu;
+    std::condition_variable go, done;
+    uint64_t gen = 0;
+    int left = 0;
+    bool stop = false;
+    char* dst = nullptr;
+    const char* src = nullptr;
+    uint64_t bytes = 0;
+
+    void part(int i) {
+        const int parts = (int)th.size() + 1;
+        const uint64_t a = bytes * (uint64_t)i / parts / 64 * 64;
+        const uint64_t b = (i + 1 == parts) ? bytes : bytes * (uint64_t)(i + 1) / parts / 64 * 64;
+        if (b > a) std::memcpy(dst + a, src + a, b - a);
+    }
+    void start(int workers) {
+        for (int i = 0; i < workers; ++i)
+            th.emplace_back([this, i] {
+                uint64_t seen = 0;
+                for (;;) {
+                    std::unique_lock<std::mutex> lk(mu);
+                    go.wait(lk, [&] { return stop || gen != seen; });
+                    if (stop) return;
+                    seen = gen;
+                    lk.unlock();
+                    part(i + 1);
+                    lk.lock();
+                    if (--left == 0) done.notify_one();
+                }
+            });
+    }
+    void copy(char* d, const char* s_, uint64_t n) {
+        {
+            std::lock_guard<std::mutex> lk(mu);
+            dst = d;
+            src = s_;
+            bytes = n;
+            left = (int)th.size();
+            ++gen;
+        }
+        go.notify_all();
+        part(0);
+        std::unique_lock<std::mutex> lk(mu);
+        done.wait(lk, [&] { return left == 0; });
+    }
+    void shutdown() {
+        {
+            std::lock_guard<std::mutex> lk(mu);
+            stop = true;
+        }
+        go.notify_all();
+        for (auto& t : th) t.join();
+        th.clear();
+        stop = false;
+    }
+};
+
 struct lwo_store {
     lwo_model_desc d{};
     Layout L;
     int device = 0;
-    int host_mode = LWO_HOST_PIN_COPY;
+    int host_mode = LWO_HOST_PIN_COPY;    // mode in effect
     std::vector<void*> host;              // per-block host extent
     bool host_owned = false;              // PIN_COPY: allocated with hipHostMalloc
+    char* stage[2] = {nullptr, nullptr};  // STAGED: two pinned staging slots of extent_bytes
+    hipEvent_t stage_done[2] = {nullptr, nullptr};   // end of the last device copy out of each
+    bool stage_busy[2] = {false, false};
+    int stage_next = 0;
+    PackPool pool;
+    int pack_threads = 0;                 // workers besides the calling thread
+    uint64_t pack_bytes = 0;
+    double pack_ms = 0;
     std::vector<uint64_t> reg_base, reg_len;
     std::vector<uint64_t> host_sums;      // lazily computed host checksums
     bool sums_ready = false;
@@ -137,6 +214,11 @@ static void release(lwo_store* s) {
         for (void* p : s->host)
             if (p) (void)hipHostFree(p);
     s->host.clear();
+    s->pool.shutdown();
+    for (int i = 0; i < 2; ++i) {
+        if (s->stage[i]) (void)hipHostFree(s->stage[i]);
+        if (s->stage_done[i]) (void)hipEventDestroy(s->stage_done[i]);
+    }
     for (int i = 0; i < 2; ++i) {
         if (s->slot[i]) (void)hipFree(s->slot[i]);
         if (s->copy_done[i]) (void)hipEventDestroy(s->copy_done[i]);
@@ -154,16 +236,44 @@ static void release(lwo_store* s) {
 
 // ------------------------------------------------------------------ helpers
 
+// Enqueue the host -> device copy of block b's extent into dst on the copy
+// stream (optional timing events around the device copy only).  STAGED: wait
+// until the device copy last issued from the next staging slot is done (the
+// host is about to overwrite it), pack the pageable extent into it, then copy.
+static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
+    const uint64_t ext = s->L.extent_bytes;
+    const char* src = (const char*)s->host[b];
+    int q = -1;
+    if (s->host_mode == LWO_HOST_STAGED) {
+        q = s->stage_next;
+        s->stage_next ^= 1;
+        if (s->stage_busy[q]) LWO_HIP_TRY(hipEventSynchronize(s->stage_done[q]));
+        const auto c0 = std::chrono::steady_clock::now();
+        s->pool.copy(s->stage[q], src, ext);
+        s->pack_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - c0).count();
+        s->pack_bytes += ext;
+        src = s->stage[q];
+    }
+    if (t0) LWO_HIP_TRY(hipEventRecord(t0, s->copy));
+    LWO_HIP_TRY(hipMemcpyAsync(dst, src, ext, hipMemcpyHostToDevice, s->copy));
+    if (t1) LWO_HIP_TRY(hipEventRecord(t1, s->copy));
+    if (q >= 0) {
+        LWO_HIP_TRY(hipEventRecord(s->stage_done[q], s->copy));
+        s->stage_busy[q] = true;
+    }
+    s->h2d_copies++;
+    s->h2d_bytes += ext;
+    return LWO_OK;
+}
+
 static lwo_status prime_head(lwo_store* s) {
     // Block k goes to slot 0 on the copy stream ([DLO] prime the first block).
     s->head_slot = 0;
     s->slot_block[0] = s->slot_block[1] = -1;
     if (s->k >= s->d.n_blocks) return LWO_OK;
-    LWO_HIP_TRY(hipMemcpyAsync(s->slot[0], s->host[s->k], s->L.extent_bytes, hipMemcpyHostToDevice, s->copy));
+    LWO_TRY(h2d_block(s, s->slot[0], s->k));
     LWO_HIP_TRY(hipEventRecord(s->copy_done[0], s->copy));
     s->slot_block[0] = s->k;
-    s->h2d_copies++;
-    s->h2d_bytes += s->L.extent_bytes;
     return LWO_OK;
 }
 
@@ -189,6 +299,9 @@ static lwo_status check_store(lwo_store* s) {
 
 // ------------------------------------------------------------------ build
 
+static lwo_status build_staged(lwo_store* s, const lwo_block_source* src);
+static lwo_status build_device(lwo_store* s);
+
 static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uint64_t budget) {
     const uint64_t ext = s->L.extent_bytes;
     const int n = s->d.n_blocks;
@@ -211,7 +324,7 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
                 return LWO_EINVAL;
             }
         }
-    } else {
+    } else if (mode == LWO_HOST_REGISTER && budget > 0) {
         if (!src->extents) { set_error("REGISTER mode needs caller extents"); return LWO_EINVAL; }
         const uint64_t page = 4096;
         std::vector<uint64_t> lens(n, ext);
@@ -226,7 +339,12 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
         int32_t nr = 0;
         lwo_status st = lwo_register_ranges(src->extents, lens.data(), n, page, budget, hip_register_cb,
                                             hip_unregister_cb, nullptr, base.data(), len.data(), n, &nr);
-        if (st != LWO_OK) return st;
+        if (st == LWO_EBUDGET || st == LWO_EREGISTER) {   // nothing stays registered: keep the staging path
+            (void)hipGetLastError();
+            s->host_mode = LWO_HOST_STAGED;
+            return build_staged(s, src);
+        }
+        if (st != LWO_OK) return st;   // LWO_EROLLBACK: a range may still be registered
         s->reg_base.assign(base.begin(), base.begin() + nr);
         s->reg_len.assign(len.begin(), len.begin() + nr);
         for (int b = 0; b < n; ++b) {   // every extent must now be known to HIP as registered host memory
@@ -236,7 +354,37 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
                 return LWO_EREGISTER;
             }
         }
+    } else {   // STAGED, or REGISTER with a zero budget
+        s->host_mode = LWO_HOST_STAGED;
+        return build_staged(s, src);
     }
+    return build_device(s);
+}
+
+// STAGED: borrow the caller's pageable extents, allocate the two pinned staging slots.
+static lwo_status build_staged(lwo_store* s, const lwo_block_source* src) {
+    const uint64_t ext = s->L.extent_bytes;
+    if (!src->extents) { set_error("STAGED mode needs caller extents"); return LWO_EINVAL; }
+    for (int b = 0; b < s->d.n_blocks; ++b) {
+        if (!src->extents[b]) { set_error("extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
+        s->host[b] = const_cast<void*>(src->extents[b]);
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (hipHostMalloc((void**)&s->stage[i], ext, hipHostMallocDefault) != hipSuccess || !s->stage[i]) {
+            s->stage[i] = nullptr;
+            set_error("hipHostMalloc of a staging slot failed");
+            return LWO_ENOMEM;
+        }
+        LWO_HIP_TRY(hipEventCreateWithFlags(&s->stage_done[i], hipEventDisableTiming));
+    }
+    s->pack_threads = (int)std::max(0u, std::min(7u, std::thread::hardware_concurrency() / 2));
+    s->pool.start(s->pack_threads);
+    return build_device(s);
+}
+
+// Device arena, workspace, copy stream and events; prime the head block.
+static lwo_status build_device(lwo_store* s) {
+    const uint64_t ext = s->L.extent_bytes;
     for (int i = 0; i < 2; ++i) {
         if (hipMalloc(&s->slot[i], ext) != hipSuccess) { s->slot[i] = nullptr; set_error("hipMalloc of a slot failed"); return LWO_ENOMEM; }
         LWO_HIP_TRY(hipEventCreateWithFlags(&s->copy_done[i], hipEventDisableTiming));
@@ -257,7 +405,10 @@ extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lw
     *out = nullptr;
     LWO_TRY(validate_desc(desc));
     if (!src || (!src->extents && !src->fill)) { set_error("block source has neither extents nor fill"); return LWO_EINVAL; }
-    if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER) { set_error("host_mode"); return LWO_EINVAL; }
+    if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER && host_mode != LWO_HOST_STAGED) {
+        set_error("host_mode");
+        return LWO_EINVAL;
+    }
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
         set_error("device " + std::to_string(device) + " is not available");
@@ -305,7 +456,8 @@ extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
             return LWO_ENOMEM;   // previous prefix stays in effect
         }
         for (int b = 0; b < k; ++b) {
-            if (hipMemcpyAsync(region + ext * (uint64_t)b, s->host[b], ext, hipMemcpyHostToDevice, s->copy) != hipSuccess) {
+            if (h2d_block(s, region + ext * (uint64_t)b, b) != LWO_OK) {
+                (void)hipStreamSynchronize(s->copy);
                 (void)hipFree(region);
                 set_error("copy of resident block " + std::to_string(b) + " failed");
                 return LWO_EHIP;
@@ -336,6 +488,7 @@ static lwo_status validate_slot(lwo_store* s, const char* base, int block, hipSt
 static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* ctx, hipStream_t st) {
     const lwo_model_desc& d = s->d;
     const uint64_t ext = s->L.extent_bytes;
+    (void)ext;
     const int n = d.n_blocks, k = s->k, m = n - k;
     LWO_TRY(enqueue_step_begin(d, s->ws, x, ctx, st));
     for (int b = 0; b < k; ++b) {
@@ -370,14 +523,11 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
                         LWO_HIP_TRY(hipEventCreate(&e1));
                         s->tev.push_back(e0);
                         s->tev.push_back(e1);
-                        LWO_HIP_TRY(hipEventRecord(e0, s->copy));
+                        s->n_timed++;
                     }
-                    LWO_HIP_TRY(hipMemcpyAsync(s->slot[nxt], s->host[nb], ext, hipMemcpyHostToDevice, s->copy));
-                    if (s->timing) { LWO_HIP_TRY(hipEventRecord(e1, s->copy)); s->n_timed++; }
+                    LWO_TRY(h2d_block(s, s->slot[nxt], nb, e0, e1));
                     LWO_HIP_TRY(hipEventRecord(s->copy_done[nxt], s->copy));
                     s->slot_block[nxt] = nb;
-                    s->h2d_copies++;
-                    s->h2d_bytes += ext;
                 }
             }
             cur = nxt;
@@ -458,7 +608,7 @@ extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* 
     } else {
         // borrow the slot the ring is not about to read
         int sl = 1 - s->head_slot;
-        LWO_HIP_TRY(hipMemcpyAsync(s->slot[sl], s->host[block], ext, hipMemcpyHostToDevice, s->copy));
+        LWO_TRY(h2d_block(s, s->slot[sl], block));
         LWO_HIP_TRY(hipEventRecord(s->copy_done[sl], s->copy));
         s->slot_block[sl] = block;
         base = s->slot[sl];
@@ -516,7 +666,11 @@ extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
     o->slot_bytes = ext;
     o->device_weight_bytes = ext * (uint64_t)(2 + s->k);
     o->workspace_bytes = s->ws.bytes;
-    o->host_bytes = ext * (uint64_t)s->d.n_blocks;
+    o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : ext * (uint64_t)s->d.n_blocks;
+    o->staging_bytes = s->host_mode == LWO_HOST_STAGED ? 2 * ext : 0;
+    o->pack_bytes = s->pack_bytes;
+    o->pack_ms = s->pack_ms;
+    o->pack_threads = s->host_mode == LWO_HOST_STAGED ? s->pack_threads + 1 : 0;
     o->h2d_copies = s->h2d_copies;
     o->h2d_bytes = s->h2d_bytes;
     o->steps = s->steps;

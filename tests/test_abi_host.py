@@ -200,3 +200,29 @@ def test_register_rollback_failure_is_reported(lib):
     assert e.value.name == "LWO_EROLLBACK"
     assert set(f.live) == {ptrs[1]}      # the range that could not be unregistered stays registered
     assert [x[1] for x in f.log if x[0] == "unreg"] == [ptrs[2], ptrs[1], ptrs[0]]
+
+
+def test_struct_layouts_match_header(lib, tmp_path):
+    """The binding's ctypes mirrors have the C header's sizes and field offsets
+    (compiled with the host C compiler against include/lwo.h)."""
+    import ctypes as C
+    from layerwise_weight_offload_amd import _binding as B
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    structs = {"lwo_model_desc": B._Desc, "lwo_tensor_info": B._TensorInfo, "lwo_block_source": B._Source,
+               "lwo_stats": B._Stats, "lwo_kernel_stat": B._KStat}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "lwo.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in py._fields_:
+            lines.append(f'  printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "sizes.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {(ln.split()[0], ln.split()[1]): int(ln.split()[2]) for ln in out if ln.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f in py._fields_:
+            assert got[(cname, f[0])] == getattr(py, f[0]).offset, (cname, f[0])
