@@ -162,6 +162,9 @@ def main() -> int:
     ap.add_argument("--host-mode", choices=("pin_copy", "staged"), default="pin_copy",
                     help="pin_copy: pinned host extents; staged: pageable extents packed through two pinned "
                          "staging slots")
+    ap.add_argument("--cache-dir", default=None,
+                    help="with --host-mode staged: publish the stack as a flat-block file under this directory, "
+                         "map it back (verified) and stream from the mapping")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -204,6 +207,15 @@ def main() -> int:
             buf = np.empty(ext, np.uint8)   # ordinary pageable host memory
             fill(b, buf.ctypes.data, ext)
             pageable.append(buf)
+        cache_entry = None
+        if args.cache_dir:
+            t1 = time.perf_counter()
+            key, created = lwo.cache_publish(args.cache_dir, desc, extents=pageable)
+            del pageable
+            cache_entry = lwo.cache_open(args.cache_dir, key, desc, verify=True)
+            pageable = cache_entry.extents()
+            log(f"flat-block file {key[:12]}... ({'published' if created else 'joined'}) and verified mapping in "
+                f"{time.perf_counter() - t1:.1f} s")
         store = lwo.build_block_store(desc, extents=pageable, host_mode=lwo.HOST_STAGED)
     else:
         store = lwo.build_block_store(desc, fill=fill)
@@ -311,7 +323,8 @@ def main() -> int:
         "config": {"workload": w.name, "kind": w.kind, "blocks": L, "hidden": w.hidden, "heads": w.heads,
                    "ffn": w.ffn, "batch": w.batch, "tokens": w.tokens, "ctx_tokens": w.ctx_tokens,
                    "act_dtype": w.act_dtype, "linear_dtype": w.linear_dtype, "resident_prefix": k,
-                   "streamed_blocks": m, "host_mode": args.host_mode, "extent_bytes": ext},
+                   "streamed_blocks": m, "host_mode": args.host_mode + ("+file" if args.cache_dir else ""),
+                   "extent_bytes": ext},
         "resident_ms": round(t_res, 3),
         "streamed_over_resident": round(t_str / t_res, 4),
         "h2d_gbps": round(h2d_gbps, 2),

@@ -68,7 +68,9 @@ typedef enum lwo_status {
     LWO_EREGISTER = 5,   /* a range failed to register; earlier ranges were rolled back */
     LWO_EROLLBACK = 6,   /* a rollback unregister failed: the process must not unmap the range */
     LWO_ESTATE = 7,      /* call not valid in the store's current state */
-    LWO_ECHECKSUM = 8    /* slot bytes differ from the host extent */
+    LWO_ECHECKSUM = 8,   /* slot bytes differ from the host extent, or a cache entry from its digests */
+    LWO_ETIMEOUT = 9,    /* a bounded wait ran out (another writer holds a cache lock) */
+    LWO_EIO = 10         /* a file, lock or mapping operation failed (message names it) */
 } lwo_status;
 
 typedef enum lwo_dtype { LWO_F32 = 0, LWO_BF16 = 1, LWO_FP8_E4M3 = 2 } lwo_dtype;
@@ -188,6 +190,46 @@ typedef int32_t (*lwo_unregister_fn)(void* user, void* base);                /* 
 lwo_status lwo_register_ranges(const void* const* ptrs, const uint64_t* bytes, int32_t n, uint64_t page,
                                uint64_t budget, lwo_register_fn reg, lwo_unregister_fn unreg, void* user,
                                uint64_t* out_base, uint64_t* out_len, int32_t cap, int32_t* n_out);
+
+/* --- persisted flat-block files (host only, no GPU needed) --------------
+ * [DLO] "Runtime cache": one content-addressed entry per block stack,
+ * published atomically, mapped read-only as the host backing of a store.
+ * Entry <dir>/<key>/ holds blocks.bin (block b's extent at b * stride, stride
+ * = extent_bytes rounded up to 4096, zero padded, so every extent is
+ * page-aligned in the mapping) and manifest.json (format, descriptor, tensor
+ * table, per-block SHA-256 digests, content digest).  The key is the
+ * lower-case hex SHA-256 of the canonical layout text followed by the 32-byte
+ * block digests in order. */
+
+typedef struct lwo_cache lwo_cache;   /* an open, validated, mapped entry */
+
+/* FIPS 180-4 SHA-256 of bytes at data into out32[32]. */
+lwo_status lwo_sha256(const void* data, uint64_t bytes, uint8_t* out32);
+
+/* Publish the stack read from src (extents, or fill called twice per block:
+ * once to hash, once to write) under dir, creating dir if needed.  Takes an
+ * exclusive flock on <dir>/<key>.lock, polling up to wait_ms
+ * (LWO_ETIMEOUT).  If the entry exists it is joined (*created = 0).
+ * Otherwise temporaries <dir>/.tmp-<key>-* left by dead writers are removed,
+ * the files are written and fsynced in a fresh temporary directory, which is
+ * renamed to <dir>/<key> (*created = 1).  key_out receives the key
+ * (65 bytes with the terminating NUL).  On error nothing is published. */
+lwo_status lwo_cache_publish(const char* dir, const lwo_model_desc* desc, const lwo_block_source* src,
+                             uint32_t wait_ms, char* key_out, int32_t* created);
+
+/* Open <dir>/<key>: the manifest must describe desc's layout (LWO_EINVAL
+ * otherwise) and its digests must give the key (LWO_ECHECKSUM);
+ * blocks.bin is mapped read-only and shared; with verify != 0 every block's
+ * SHA-256 is recomputed from the mapping (LWO_ECHECKSUM on a mismatch). */
+lwo_status lwo_cache_open(const char* dir, const char* key, const lwo_model_desc* desc, int32_t verify,
+                          lwo_cache** out);
+
+/* The n_blocks extent pointers inside the mapping (page-aligned, valid until
+ * lwo_cache_close); out == NULL and cap == 0 only sets *n. */
+lwo_status lwo_cache_extents(const lwo_cache* cache, const void** out, int32_t cap, int32_t* n);
+
+/* Unmap and close.  A store built on the extents must be destroyed first. */
+lwo_status lwo_cache_close(lwo_cache* cache);
 
 /* --- the store ----------------------------------------------------------- */
 

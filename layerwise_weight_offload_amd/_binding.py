@@ -20,7 +20,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 KIND_DIT, KIND_VIDEO = 0, 1
 HOST_PIN_COPY, HOST_REGISTER, HOST_STAGED = 0, 1, 2
 STATUS = {0: "LWO_OK", 1: "LWO_EINVAL", 2: "LWO_ENOMEM", 3: "LWO_EHIP", 4: "LWO_EBUDGET",
-          5: "LWO_EREGISTER", 6: "LWO_EROLLBACK", 7: "LWO_ESTATE", 8: "LWO_ECHECKSUM"}
+          5: "LWO_EREGISTER", 6: "LWO_EROLLBACK", 7: "LWO_ESTATE", 8: "LWO_ECHECKSUM", 9: "LWO_ETIMEOUT",
+          10: "LWO_EIO"}
 
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 
@@ -94,6 +95,12 @@ _lib_set_kernel_timing = _sig("lwo_set_kernel_timing", C.c_int, _P, C.c_int32)
 _lib_kernel_stats = _sig("lwo_kernel_stats", C.c_int, _P, C.POINTER(_KStat), C.c_int32, C.POINTER(C.c_int32))
 _lib_destroy = _sig("lwo_destroy_block_store", C.c_int, _P)
 _lib_last_error = _sig("lwo_last_error", C.c_char_p)
+_lib_sha256 = _sig("lwo_sha256", C.c_int, _P, C.c_uint64, C.c_char_p)
+_lib_cache_publish = _sig("lwo_cache_publish", C.c_int, C.c_char_p, C.POINTER(_Desc), C.POINTER(_Source), C.c_uint32,
+                          C.c_char_p, C.POINTER(C.c_int32))
+_lib_cache_open = _sig("lwo_cache_open", C.c_int, C.c_char_p, C.c_char_p, C.POINTER(_Desc), C.c_int32, C.POINTER(_P))
+_lib_cache_extents = _sig("lwo_cache_extents", C.c_int, _P, C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_int32))
+_lib_cache_close = _sig("lwo_cache_close", C.c_int, _P)
 _I = C.c_int32
 _lib_op_linear = _sig("lwo_op_linear", C.c_int, _I, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _I, _P)
 _lib_op_attention = _sig("lwo_op_attention", C.c_int, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P)
@@ -107,7 +114,8 @@ EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_re
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
             "lwo_op_quantize_rows", "lwo_op_rmsnorm_qk",
-            "lwo_destroy_block_store", "lwo_last_error"]
+            "lwo_destroy_block_store", "lwo_last_error", "lwo_sha256", "lwo_cache_publish", "lwo_cache_open",
+            "lwo_cache_extents", "lwo_cache_close"]
 
 
 def exported_symbols() -> list[str]:
@@ -343,11 +351,9 @@ class Store:
             pass
 
 
-def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,
-                      register_budget: int = 0, device: int = 0) -> Store:
-    """extents: list of host buffers/addresses (one per block), or fill(b, dst_addr, nbytes) -> None
-    writing block b's flat extent into the store's pinned memory.  REGISTER and STAGED borrow the
-    extents: the returned store keeps the Python objects alive until it is destroyed."""
+def _source(extents=None, fill=None):
+    """A lwo_block_source over host buffers/addresses or a fill(b, dst_addr, nbytes) callback, and the
+    Python objects it points into (keep them alive while the library may use the source)."""
     src = _Source()
     keep = []
     if extents is not None:
@@ -361,7 +367,7 @@ def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int =
             try:
                 fill(int(b), int(dst), int(nbytes))
                 return 0
-            except Exception as e:   # reported through the library's status
+            except Exception:   # reported through the library's status
                 import traceback
                 traceback.print_exc()
                 return 1
@@ -369,6 +375,65 @@ def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int =
         keep.append(cb)
         src.extents = C.POINTER(C.c_void_p)()
         src.fill = cb
+    return src, keep
+
+
+def sha256(buf) -> bytes:
+    """The library's SHA-256 of a bytes-like object."""
+    a = np.frombuffer(buf, dtype=np.uint8)
+    out = C.create_string_buffer(32)
+    _check(_lib_sha256(a.ctypes.data if a.size else None, a.size, out))
+    return out.raw
+
+
+def cache_publish(directory: str, desc: ModelDesc, extents=None, fill=None, wait_ms: int = 10000):
+    """Publish the block stack under directory; returns (key, created)."""
+    src, keep = _source(extents, fill)
+    key = C.create_string_buffer(65)
+    created = C.c_int32()
+    _check(_lib_cache_publish(os.fsencode(directory), C.byref(desc._c()), C.byref(src), wait_ms, key,
+                              C.byref(created)))
+    del keep
+    return key.value.decode(), bool(created.value)
+
+
+class CacheEntry:
+    """An open, validated entry mapped read-only; extents() are page-aligned addresses in the mapping."""
+
+    def __init__(self, handle, n):
+        self._h = handle
+        self.n_blocks = n
+
+    def extents(self) -> list[int]:
+        arr = (C.c_void_p * self.n_blocks)()
+        n = C.c_int32()
+        _check(_lib_cache_extents(self._h, arr, self.n_blocks, C.byref(n)))
+        return [int(arr[i]) for i in range(n.value)]
+
+    def close(self) -> None:
+        if self._h:
+            _check(_lib_cache_close(self._h))
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def cache_open(directory: str, key: str, desc: ModelDesc, verify: bool = True) -> CacheEntry:
+    h = C.c_void_p()
+    _check(_lib_cache_open(os.fsencode(directory), key.encode(), C.byref(desc._c()), int(verify), C.byref(h)))
+    return CacheEntry(h, desc.n_blocks)
+
+
+def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,
+                      register_budget: int = 0, device: int = 0) -> Store:
+    """extents: list of host buffers/addresses (one per block), or fill(b, dst_addr, nbytes) -> None
+    writing block b's flat extent into the store's pinned memory.  REGISTER and STAGED borrow the
+    extents: the returned store keeps the Python objects alive until it is destroyed."""
+    src, keep = _source(extents, fill)
     h = C.c_void_p()
     _check(_lib_build(C.byref(desc._c()), C.byref(src), host_mode, register_budget, device, C.byref(h)))
     return Store(h, desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)

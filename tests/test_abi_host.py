@@ -21,7 +21,7 @@ DT = {"f32": 0, "bf16": 1, "fp8": 2}
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lwo_[a-z_]+)\s*\(", src)) - {"lwo_register_fn", "lwo_unregister_fn"})
+    return sorted(set(re.findall(r"\b(lwo_[a-z0-9_]+)\s*\(", src)) - {"lwo_register_fn", "lwo_unregister_fn"})
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -106,3 +106,25 @@ def test_staged_needs_extents(lib):
     desc = lib.ModelDesc.from_workload(w)
     with pytest.raises(lib.LwoError):
         lib.build_block_store(desc, fill=lambda b, d, n: None, host_mode=lib.HOST_STAGED)
+
+
+def test_cache_backed_staged_store(lib, tmp_path):
+    """Publish the stack as a flat-block file, map it back (verified) and stream
+    from the mapping through the staging slots: same bits as PIN_COPY."""
+    w = lwo_synth.get("video_t_bf16")
+    desc, exts = _pageable_extents(lib, w)
+    key, created = lib.cache_publish(str(tmp_path), desc, extents=exts)
+    assert created
+    del exts
+    with lib.cache_open(str(tmp_path), key, desc, verify=True) as entry:
+        with lib.build_block_store(desc, extents=entry.extents(), host_mode=lib.HOST_STAGED) as st:
+            x, c, cx = device_inputs(w)
+            run_steps(st, x, c, cx, steps=2)
+            for b in range(w.n_blocks):
+                hs, ss = st.block_checksum(b)
+                assert hs == ss == o_ck.extent_checksum(o_layout.pack_block(w, lwo_synth.block_tensors(w, b)))
+    desc2, exts2 = _pageable_extents(lib, w)
+    with lib.build_block_store(desc2, extents=exts2, host_mode=lib.HOST_PIN_COPY) as ref:
+        xr, c, cx = device_inputs(w)
+        run_steps(ref, xr, c, cx, steps=2)
+    assert np.array_equal(_bits(w, x), _bits(w, xr))
