@@ -121,7 +121,7 @@ typedef struct lwo_block_source {
 } lwo_block_source;
 
 typedef struct lwo_stats {
-    uint64_t extent_bytes;       /* bytes of one block extent */
+    uint64_t extent_bytes;       /* bytes of one block extent (the largest, for a mixed stack) */
     uint64_t slot_bytes;         /* bytes of each of the two device slots */
     uint64_t device_weight_bytes;/* resident prefix + two slots */
     uint64_t workspace_bytes;    /* activation workspace on the device */
@@ -258,6 +258,21 @@ typedef struct lwo_store lwo_store;   /* opaque */
 lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src,
                                  int32_t host_mode, uint64_t register_budget, int32_t device,
                                  lwo_store** out);
+
+/* [LW] "How It Works" (models with several block types, streamed through
+ * the same slots) and [DLO] "Startup and runtime sequence" (slots sized for
+ * the largest streamed block): a stack of n_blocks blocks where block b has
+ * descriptor types[block_type[b]] (its n_blocks field is ignored).  All types
+ * share kind, hidden, batch, tokens, ctx_tokens and act_dtype (LWO_EINVAL
+ * otherwise, checked before any device call); heads, ffn and linear_dtype
+ * may differ.  Each block's extent has its own type's layout and size
+ * (lwo_block_layout of the type); extents[b] / fill(.., b, .., bytes) use
+ * that size.  The slots and staging slots hold the largest extent, the
+ * resident region the sum of the prefix's extents, the workspace the largest
+ * ffn.  Otherwise as lwo_build_block_store, which is the one-type case. */
+lwo_status lwo_build_mixed_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type,
+                                 int32_t n_blocks, const lwo_block_source* src, int32_t host_mode,
+                                 uint64_t register_budget, int32_t device, lwo_store** out);
 
 /* [DLO] "Feature compatibility" (resident leading layers): keep blocks
  * 0..k-1 in a device-resident region and stream blocks k..n_blocks-1

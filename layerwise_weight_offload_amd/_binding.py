@@ -83,6 +83,8 @@ _lib_register_ranges = _sig("lwo_register_ranges", C.c_int, C.POINTER(C.c_void_p
                             C.POINTER(C.c_uint64), C.c_int32, C.POINTER(C.c_int32))
 _lib_build = _sig("lwo_build_block_store", C.c_int, C.POINTER(_Desc), C.POINTER(_Source), C.c_int32, C.c_uint64,
                   C.c_int32, C.POINTER(_P))
+_lib_build_mixed = _sig("lwo_build_mixed_store", C.c_int, C.POINTER(_Desc), C.c_int32, C.POINTER(C.c_int32), C.c_int32,
+                        C.POINTER(_Source), C.c_int32, C.c_uint64, C.c_int32, C.POINTER(_P))
 _lib_set_prefix = _sig("lwo_set_resident_prefix", C.c_int, _P, C.c_int32)
 _lib_run = _sig("lwo_run_denoise_step", C.c_int, _P, _P, _P, _P, _P)
 _lib_set_validation = _sig("lwo_set_validation", C.c_int, _P, C.c_int32)
@@ -109,7 +111,7 @@ _lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P
 _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
-            "lwo_build_block_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
+            "lwo_build_block_store", "lwo_build_mixed_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
             "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
@@ -437,3 +439,18 @@ def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int =
     h = C.c_void_p()
     _check(_lib_build(C.byref(desc._c()), C.byref(src), host_mode, register_budget, device, C.byref(h)))
     return Store(h, desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)
+
+
+def build_mixed_store(types, block_type, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,
+                      register_budget: int = 0, device: int = 0) -> Store:
+    """A stack whose block b has descriptor types[block_type[b]]; extents[b] / fill use that type's extent size."""
+    types = list(types)
+    bt = list(block_type)
+    src, keep = _source(extents, fill)
+    arr = (_Desc * len(types))(*[t._c() for t in types])
+    tarr = (C.c_int32 * len(bt))(*bt)
+    h = C.c_void_p()
+    _check(_lib_build_mixed(arr, len(types), tarr, len(bt), C.byref(src), host_mode, register_budget, device,
+                            C.byref(h)))
+    n_desc = dataclasses.replace(types[0], n_blocks=len(bt))
+    return Store(h, n_desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)

@@ -97,8 +97,13 @@ struct PackPool {
 };
 
 struct lwo_store {
-    lwo_model_desc d{};
-    Layout L;
+    lwo_model_desc d{};                   // the stack: shared shapes, largest ffn, fp8 if any block type is
+    std::vector<lwo_model_desc> tdesc;    // per block type
+    std::vector<Layout> tlay;             // per block type
+    std::vector<int> btype;               // per block: its type
+    std::vector<uint64_t> bext;           // per block: extent bytes of its type
+    std::vector<uint64_t> roff;           // per block: offset in the resident region (prefix sums of bext)
+    uint64_t max_ext = 0;                 // slot and staging size
     int device = 0;
     int host_mode = LWO_HOST_PIN_COPY;    // mode in effect
     std::vector<void*> host;              // per-block host extent
@@ -241,7 +246,7 @@ static void release(lwo_store* s) {
 // until the device copy last issued from the next staging slot is done (the
 // host is about to overwrite it), pack the pageable extent into it, then copy.
 static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
-    const uint64_t ext = s->L.extent_bytes;
+    const uint64_t ext = s->bext[b];
     const char* src = (const char*)s->host[b];
     int q = -1;
     if (s->host_mode == LWO_HOST_STAGED) {
@@ -285,7 +290,7 @@ static void compute_host_sums(lwo_store* s) {
     std::vector<std::thread> th;
     for (unsigned t = 0; t < nt; ++t)
         th.emplace_back([s, t, nt, n] {
-            for (int b = (int)t; b < n; b += (int)nt) s->host_sums[b] = extent_checksum_host(s->host[b], s->L.extent_bytes);
+            for (int b = (int)t; b < n; b += (int)nt) s->host_sums[b] = extent_checksum_host(s->host[b], s->bext[b]);
         });
     for (auto& x : th) x.join();
     s->sums_ready = true;
@@ -303,13 +308,13 @@ static lwo_status build_staged(lwo_store* s, const lwo_block_source* src);
 static lwo_status build_device(lwo_store* s);
 
 static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uint64_t budget) {
-    const uint64_t ext = s->L.extent_bytes;
     const int n = s->d.n_blocks;
     LWO_HIP_TRY(hipSetDevice(s->device));
     s->host.assign(n, nullptr);
     if (mode == LWO_HOST_PIN_COPY) {
         s->host_owned = true;
         for (int b = 0; b < n; ++b) {
+            const uint64_t ext = s->bext[b];
             void* p = nullptr;
             if (hipHostMalloc(&p, ext, hipHostMallocDefault) != hipSuccess || !p) {
                 set_error("hipHostMalloc of block " + std::to_string(b) + " (" + std::to_string(ext) + " bytes) failed");
@@ -327,7 +332,7 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
     } else if (mode == LWO_HOST_REGISTER && budget > 0) {
         if (!src->extents) { set_error("REGISTER mode needs caller extents"); return LWO_EINVAL; }
         const uint64_t page = 4096;
-        std::vector<uint64_t> lens(n, ext);
+        std::vector<uint64_t> lens(s->bext);
         for (int b = 0; b < n; ++b) {
             if (!src->extents[b] || ((uintptr_t)src->extents[b] % page)) {
                 set_error("REGISTER mode needs page-aligned extents (block " + std::to_string(b) + ")");
@@ -363,7 +368,7 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
 
 // STAGED: borrow the caller's pageable extents, allocate the two pinned staging slots.
 static lwo_status build_staged(lwo_store* s, const lwo_block_source* src) {
-    const uint64_t ext = s->L.extent_bytes;
+    const uint64_t ext = s->max_ext;
     if (!src->extents) { set_error("STAGED mode needs caller extents"); return LWO_EINVAL; }
     for (int b = 0; b < s->d.n_blocks; ++b) {
         if (!src->extents[b]) { set_error("extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
@@ -384,7 +389,7 @@ static lwo_status build_staged(lwo_store* s, const lwo_block_source* src) {
 
 // Device arena, workspace, copy stream and events; prime the head block.
 static lwo_status build_device(lwo_store* s) {
-    const uint64_t ext = s->L.extent_bytes;
+    const uint64_t ext = s->max_ext;
     for (int i = 0; i < 2; ++i) {
         if (hipMalloc(&s->slot[i], ext) != hipSuccess) { s->slot[i] = nullptr; set_error("hipMalloc of a slot failed"); return LWO_ENOMEM; }
         LWO_HIP_TRY(hipEventCreateWithFlags(&s->copy_done[i], hipEventDisableTiming));
@@ -398,12 +403,27 @@ static lwo_status build_device(lwo_store* s) {
     return LWO_OK;
 }
 
-extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t host_mode,
-                                            uint64_t register_budget, int32_t device, lwo_store** out) {
-    clear_error();
+// Shared by both build calls: block b has descriptor types[block_type[b]].
+static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type, int32_t n_blocks,
+                              const lwo_block_source* src, int32_t host_mode, uint64_t register_budget,
+                              int32_t device, lwo_store** out) {
     if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
     *out = nullptr;
-    LWO_TRY(validate_desc(desc));
+    if (!types || n_types < 1 || !block_type || n_blocks < 1) { set_error("stack: types, block_type and n_blocks >= 1 required"); return LWO_EINVAL; }
+    std::vector<lwo_model_desc> td(types, types + n_types);
+    for (int t = 0; t < n_types; ++t) {
+        td[t].n_blocks = n_blocks;
+        LWO_TRY(validate_desc(&td[t]));
+        const lwo_model_desc& a = td[0], &c = td[t];
+        if (c.kind != a.kind || c.hidden != a.hidden || c.batch != a.batch || c.tokens != a.tokens ||
+            c.ctx_tokens != a.ctx_tokens || c.act_dtype != a.act_dtype) {
+            set_error("block type " + std::to_string(t) + " differs from type 0 in kind, hidden, batch, tokens, "
+                      "ctx_tokens or act_dtype");
+            return LWO_EINVAL;
+        }
+    }
+    for (int b = 0; b < n_blocks; ++b)
+        if (block_type[b] < 0 || block_type[b] >= n_types) { set_error("block_type[" + std::to_string(b) + "] out of range"); return LWO_EINVAL; }
     if (!src || (!src->extents && !src->fill)) { set_error("block source has neither extents nor fill"); return LWO_EINVAL; }
     if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER && host_mode != LWO_HOST_STAGED) {
         set_error("host_mode");
@@ -417,8 +437,21 @@ extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lw
     auto t0 = std::chrono::steady_clock::now();
     lwo_store* s = new (std::nothrow) lwo_store();
     if (!s) { set_error("out of host memory"); return LWO_ENOMEM; }
-    s->d = *desc;
-    s->L = make_layout(*desc);
+    s->tdesc = td;
+    for (const lwo_model_desc& t : td) s->tlay.push_back(make_layout(t));
+    s->btype.assign(block_type, block_type + n_blocks);
+    s->d = td[0];
+    for (const lwo_model_desc& t : td) {
+        s->d.ffn = std::max(s->d.ffn, t.ffn);
+        if (t.linear_dtype == LWO_FP8_E4M3) s->d.linear_dtype = LWO_FP8_E4M3;
+    }
+    uint64_t off = 0;
+    for (int b = 0; b < n_blocks; ++b) {
+        s->bext.push_back(s->tlay[block_type[b]].extent_bytes);
+        s->roff.push_back(off);
+        off += s->bext[b];
+        s->max_ext = std::max(s->max_ext, s->bext[b]);
+    }
     s->device = device;
     s->host_mode = host_mode;
     lwo_status st = build(s, src, host_mode, register_budget);
@@ -431,6 +464,23 @@ extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lw
     s->build_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     *out = s;
     return LWO_OK;
+}
+
+extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t host_mode,
+                                            uint64_t register_budget, int32_t device, lwo_store** out) {
+    clear_error();
+    if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
+    *out = nullptr;
+    LWO_TRY(validate_desc(desc));
+    std::vector<int32_t> bt(desc->n_blocks, 0);
+    return build_store(desc, 1, bt.data(), desc->n_blocks, src, host_mode, register_budget, device, out);
+}
+
+extern "C" lwo_status lwo_build_mixed_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type,
+                                            int32_t n_blocks, const lwo_block_source* src, int32_t host_mode,
+                                            uint64_t register_budget, int32_t device, lwo_store** out) {
+    clear_error();
+    return build_store(types, n_types, block_type, n_blocks, src, host_mode, register_budget, device, out);
 }
 
 extern "C" lwo_status lwo_destroy_block_store(lwo_store* s) {
@@ -448,15 +498,15 @@ extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
     LWO_HIP_TRY(hipSetDevice(s->device));
     LWO_HIP_TRY(hipStreamSynchronize(s->copy));
     LWO_HIP_TRY(hipDeviceSynchronize());
-    const uint64_t ext = s->L.extent_bytes;
     char* region = nullptr;
     if (k > 0) {
-        if (hipMalloc(&region, ext * (uint64_t)k) != hipSuccess) {
-            set_error("hipMalloc of the resident region (" + std::to_string(ext * (uint64_t)k) + " bytes) failed");
+        const uint64_t bytes = s->roff[k - 1] + s->bext[k - 1];
+        if (hipMalloc(&region, bytes) != hipSuccess) {
+            set_error("hipMalloc of the resident region (" + std::to_string(bytes) + " bytes) failed");
             return LWO_ENOMEM;   // previous prefix stays in effect
         }
         for (int b = 0; b < k; ++b) {
-            if (h2d_block(s, region + ext * (uint64_t)b, b) != LWO_OK) {
+            if (h2d_block(s, region + s->roff[b], b) != LWO_OK) {
                 (void)hipStreamSynchronize(s->copy);
                 (void)hipFree(region);
                 set_error("copy of resident block " + std::to_string(b) + " failed");
@@ -481,19 +531,20 @@ extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
 
 static lwo_status validate_slot(lwo_store* s, const char* base, int block, hipStream_t st) {
     LWO_TRY(enqueue_zero_u64(s->ws.sums, 1, st));
-    LWO_TRY(enqueue_checksum(base, s->L.extent_bytes, s->ws.sums, st));
+    LWO_TRY(enqueue_checksum(base, s->bext[block], s->ws.sums, st));
     return enqueue_checksum_compare(s->ws.sums, s->host_sums[block], st);
 }
 
 static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* ctx, hipStream_t st) {
     const lwo_model_desc& d = s->d;
-    const uint64_t ext = s->L.extent_bytes;
-    (void)ext;
     const int n = d.n_blocks, k = s->k, m = n - k;
+    auto run_block = [&](int b, const char* base) {
+        const lwo_model_desc& bd = s->tdesc[s->btype[b]];
+        return enqueue_block(bd, block_ptrs(s->tlay[s->btype[b]], bd, base), s->ws, cond, ctx, st, &s->kt);
+    };
     LWO_TRY(enqueue_step_begin(d, s->ws, x, ctx, st));
     for (int b = 0; b < k; ++b) {
-        const char* base = s->resident + ext * (uint64_t)b;
-        LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, base), s->ws, cond, ctx, st, &s->kt));
+        LWO_TRY(run_block(b, s->resident + s->roff[b]));
     }
     if (m > 0) {
         for (hipEvent_t e : s->tev) (void)hipEventDestroy(e);
@@ -508,7 +559,7 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
             // The block's kernels go in before the prefetch call: the runtime may
             // block the host inside hipMemcpyAsync when many copies are queued,
             // and the compute queue must not starve meanwhile.
-            LWO_TRY(enqueue_block(d, block_ptrs(s->L, d, s->slot[cur]), s->ws, cond, ctx, st, &s->kt));
+            LWO_TRY(run_block(j, s->slot[cur]));
             LWO_HIP_TRY(hipEventRecord(s->compute_done[cur], st));
             int nxt = cur;
             if (m > 1) {
@@ -599,10 +650,10 @@ extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* 
     LWO_HIP_TRY(hipSetDevice(s->device));
     LWO_HIP_TRY(hipDeviceSynchronize());
     compute_host_sums(s);
-    const uint64_t ext = s->L.extent_bytes;
+    const uint64_t ext = s->bext[block];
     const char* base = nullptr;
     if (block < s->k) {
-        base = s->resident + ext * (uint64_t)block;
+        base = s->resident + s->roff[block];
     } else if (s->slot_block[0] == block || s->slot_block[1] == block) {
         base = s->slot[s->slot_block[0] == block ? 0 : 1];
     } else {
@@ -661,12 +712,14 @@ extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
     LWO_HIP_TRY(hipSetDevice(s->device));
     LWO_HIP_TRY(hipDeviceSynchronize());
     std::memset(o, 0, sizeof(*o));
-    const uint64_t ext = s->L.extent_bytes;
+    const uint64_t ext = s->max_ext;
+    uint64_t all = 0;
+    for (uint64_t e : s->bext) all += e;
     o->extent_bytes = ext;
     o->slot_bytes = ext;
-    o->device_weight_bytes = ext * (uint64_t)(2 + s->k);
+    o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->bext[s->k - 1] : 0);
     o->workspace_bytes = s->ws.bytes;
-    o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : ext * (uint64_t)s->d.n_blocks;
+    o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : all;
     o->staging_bytes = s->host_mode == LWO_HOST_STAGED ? 2 * ext : 0;
     o->pack_bytes = s->pack_bytes;
     o->pack_ms = s->pack_ms;

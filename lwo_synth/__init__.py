@@ -16,7 +16,8 @@ transformer: a tiny DiT, a DiT-XL-shaped stack, and a 14B-class video DiT):
 * ``video14b_fp8``    the same stack with per-tensor fp8 e4m3 linear weights
 
 plus small variants (suffix ``_t``) whose shapes span several kernel tiles
-with ragged tails, used by the parity tests.
+with ragged tails, used by the parity tests, and small mixed stacks of two
+block types (``MixedStack``).
 
 Draw recipe (one stream per block, one for the step inputs):
 
@@ -98,6 +99,55 @@ _add(Workload("video_t_fp8", KIND_VIDEO, 3, 256, 2, 1024, 1, 300, 40, "bf16", "f
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+# Mixed stacks: several block types streamed through one ring.  Block b of a
+# stack draws its tensors as block b of its type's workload (all types share
+# the stack's seed), so the recipe above is unchanged.
+@dataclasses.dataclass(frozen=True)
+class MixedStack:
+    name: str
+    types: tuple          # Workload per block type; they share kind, hidden, batch, tokens, ctx, act dtype, seed
+    block_type: tuple     # type index of each block, in stack order
+
+    @property
+    def n_blocks(self) -> int:
+        return len(self.block_type)
+
+    def type_of(self, b: int) -> Workload:
+        return self.types[self.block_type[b]].with_(n_blocks=self.n_blocks)
+
+    @property
+    def inputs(self) -> Workload:
+        """The workload whose step inputs the stack takes (shared by every type)."""
+        return self.types[0].with_(n_blocks=self.n_blocks)
+
+
+MIXED: dict[str, MixedStack] = {}
+
+
+def _mix(name: str, types, block_type) -> None:
+    MIXED[name] = MixedStack(name, tuple(types), tuple(block_type))
+
+
+# two DiT block types of different sizes (head dims 64 and 128, FFN 1024 and 512), fp32
+_mix("dit_mixed_fp32", [Workload("dit_mixed_fp32.a", KIND_DIT, 1, 256, 4, 1024, 1, 96, 0, "f32", "f32", 401),
+                        Workload("dit_mixed_fp32.b", KIND_DIT, 1, 256, 2, 512, 1, 96, 0, "f32", "f32", 401)],
+     [0, 1, 1, 0, 1])
+# two DiT block types (head dims 72 and 64, FFN 2304 and 1152), bf16, ragged tokens
+_mix("dit_mixed_bf16", [Workload("dit_mixed_bf16.a", KIND_DIT, 1, 576, 8, 2304, 2, 200, 0, "bf16", "bf16", 402),
+                        Workload("dit_mixed_bf16.b", KIND_DIT, 1, 576, 9, 1152, 2, 200, 0, "bf16", "bf16", 402)],
+     [1, 0, 0, 1, 0])
+# video blocks with bf16 and with fp8 linears (extents of different sizes)
+_mix("video_mixed_fp8", [Workload("video_mixed_fp8.a", KIND_VIDEO, 1, 256, 2, 1024, 1, 300, 40, "bf16", "bf16", 403,
+                                  gamma_jitter=True),
+                         Workload("video_mixed_fp8.b", KIND_VIDEO, 1, 256, 2, 512, 1, 300, 40, "bf16", "fp8", 403,
+                                  gamma_jitter=True)],
+     [0, 1, 0, 1])
+
+
+def get_mixed(name: str) -> MixedStack:
+    return MIXED[name]
 
 
 def tensor_inventory(w: Workload) -> list[tuple[str, tuple[int, ...]]]:

@@ -208,6 +208,19 @@ def stack_forward(w, extents, x, cond, ctx, blocks=None, fp8_act: bool = False) 
     return x
 
 
+def stack_forward_mixed(m, extents, x, cond, ctx, fp8_act: bool = False) -> np.ndarray:
+    """A stack of several block types applied in order: block b is decoded and
+    run with its own type's workload ``m.type_of(b)`` (the per-block reading of
+    a model with several block types streamed through one ring).  ``fp8_act``
+    applies to the blocks whose linears are fp8."""
+    for b in range(m.n_blocks):
+        wb = m.type_of(b)
+        ext = extents(b) if callable(extents) else extents[b]
+        params = layout.unpack_block(wb, ext)
+        x = block_forward(wb, x, cond, ctx, params, fp8_act=fp8_act and wb.linear_dtype == "fp8")
+    return x
+
+
 def rel_l2(y: np.ndarray, ref: np.ndarray) -> float:
     y = np.asarray(y, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

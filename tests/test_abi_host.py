@@ -226,3 +226,26 @@ def test_struct_layouts_match_header(lib, tmp_path):
         assert got[(cname, "size")] == C.sizeof(py), cname
         for f in py._fields_:
             assert got[(cname, f[0])] == getattr(py, f[0]).offset, (cname, f[0])
+
+
+def test_mixed_build_validation_before_device(lib):
+    """Mixed stacks: inconsistent types or bad indices fail with LWO_EINVAL before
+    any device call (so the checks run on a host without a GPU); a consistent
+    stack gets as far as the device check."""
+    m = lwo_synth.get_mixed("dit_mixed_bf16")
+    a, b = (lib.ModelDesc.from_workload(t) for t in m.types)
+    src = [np.zeros(8, np.uint8)] * 5
+    import dataclasses
+    for types, bt in [([a, dataclasses.replace(b, hidden=512)], [0, 1]),      # hidden differs
+                      ([a, dataclasses.replace(b, tokens=100)], [0, 1]),      # tokens differ
+                      ([a, dataclasses.replace(b, kind=1, ctx_tokens=8)], [0, 1]),
+                      ([a, b], [0, 2]),                                       # type index out of range
+                      ([a, b], []),                                           # no blocks
+                      ([a, dataclasses.replace(b, heads=7)], [0, 1])]:        # invalid head dim
+        with pytest.raises(lib.LwoError) as e:
+            lib.build_mixed_store(types, bt, extents=src[:max(len(bt), 1)])
+        assert e.value.status == 1, (types, bt, str(e.value))
+    if not os.path.exists("/dev/kfd"):
+        with pytest.raises(lib.LwoError) as e:
+            lib.build_mixed_store([a, b], list(m.block_type), extents=src)
+        assert "device" in str(e.value)

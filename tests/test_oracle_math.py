@@ -250,3 +250,50 @@ def test_stack_is_blocks_in_order():
     # order matters
     z2 = dit.stack_forward(w, ext, x, c, ctx, blocks=[1, 0, 2])
     assert np.abs(z2 - y).max() > 0
+
+
+def _mixed_small(name, tokens=12):
+    m = lwo_synth.get_mixed(name)
+    return lwo_synth.MixedStack(m.name, tuple(t.with_(tokens=tokens) for t in m.types), m.block_type)
+
+
+def test_mixed_stack_reduces_to_uniform_stack():
+    """A mixed stack whose types are all the same workload is the uniform stack."""
+    w = lwo_synth.get("dit_t_fp32").with_(tokens=12, n_blocks=3)
+    m = lwo_synth.MixedStack("same", (w, w), (0, 1, 0))
+    ext = [layout.pack_block(w, lwo_synth.block_tensors(w, b)) for b in range(3)]
+    x, c, ctx = dit.decode_inputs(w, *lwo_synth.step_inputs(w))
+    assert np.array_equal(dit.stack_forward_mixed(m, ext, x, c, ctx), dit.stack_forward(w, ext, x, c, ctx))
+
+
+@pytest.mark.parametrize("name", ["dit_mixed_fp32", "video_mixed_fp8"])
+def test_mixed_stack_uses_each_blocks_type_and_order(name):
+    m = _mixed_small(name)
+    ext = [layout.pack_block(m.type_of(b), lwo_synth.block_tensors(m.type_of(b), b)) for b in range(m.n_blocks)]
+    assert len({len(e) for e in ext}) == 2   # two extent sizes in one stack
+    x, c, ctx = dit.decode_inputs(m.inputs, *lwo_synth.step_inputs(m.inputs))
+    y = dit.stack_forward_mixed(m, ext, x, c, ctx)
+    assert np.isfinite(y).all() and np.abs(y - x).max() > 0
+    # order matters
+    rev = lwo_synth.MixedStack(m.name, m.types, tuple(reversed(m.block_type)))
+    y2 = dit.stack_forward_mixed(rev, [ext[b] for b in reversed(range(m.n_blocks))], x, c, ctx)
+    assert np.abs(y2 - y).max() > 0
+    # a zero-gated block of either type is the identity, in a stack of the other type's blocks
+    for t in (0, 1):
+        wb = m.type_of(list(m.block_type).index(t))
+        tens = lwo_synth.block_tensors(wb, 0)
+        p = layout.unpack_block(wb, layout.pack_block(wb, tens))
+        D = wb.hidden
+        if wb.kind == "dit":
+            for g in (2, 5):
+                p["ada.w"][g * D:(g + 1) * D] = 0
+                p["ada.b"][g * D:(g + 1) * D] = 0
+            cz = c
+        else:
+            cz = c.copy()
+            for g in (2, 5):
+                cz[:, g] = 0
+                p["mod.table"][g] = 0
+            p["cross.o.w"][:] = 0
+            p["cross.o.b"][:] = 0
+        assert np.array_equal(dit.block_forward(wb, y, cz, ctx, p), y)
