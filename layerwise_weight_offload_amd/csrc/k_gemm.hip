@@ -112,10 +112,12 @@ __device__ __forceinline__ void tile_of(int pid, int nt_m, int nt_n, int& tm, in
 // wavefront's L loads per stage for the two later stages may still be in
 // flight) followed by a plain s_barrier: the workgroup barrier of the
 // language would also drain those later loads.  LDS rows are 64 bytes (four
-// 16-byte chunks); chunk c of row r sits at c ^ f(r) with
-// f(r) = ((r >> 1) ^ (r >> 3)) & 3, which puts the rows one fragment read
-// touches on distinct banks for 32- and 64-bank LDS alike.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 16-byte chunks); chunk c of row r sits at c ^ f(r) with f(r) = (r >> 2) & 3:
+// rows r, r + 4, r + 8, r + 12 of one fragment read would otherwise share
+// banks (measured on gfx950 with the LDS bank-conflict counter: this choice
+// gives none for the fragment reads, XOR with bits 1 or 0 of r leaves half
+// the LDS cycles in conflicts).
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
 
 // 16-byte LDS read issued as an instruction the compiler does not track: its
 // completion is awaited explicitly (lds_wait), so the compiler's own waits,
