@@ -129,18 +129,20 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
-template <int BM, int BN, int SB, bool FP8, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
-    constexpr int TM = BM / 64, TN = BN / 64;
+template <int BM, int BN, int SB, bool FP8, int EPI, int NWN = 2>
+__global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
+    // 2 x NWN wavefronts, each owning (BM/2) x (BN/NWN) outputs = TM x TN MFMA blocks.
+    constexpr int NW = 2 * NWN;
+    constexpr int TM = BM / 64, TN = BN / (32 * NWN);
     constexpr int DIST = 3;                          // prefetch distance (4 buffers); SB = stage bytes per row
     constexpr int KS = FP8 ? SB / 64 : SB / 32;      // MFMA k-steps per stage
     constexpr int CPR = SB / 16, RPI = kWave / CPR;  // 16-byte chunks per row, rows per load instruction
-    constexpr int LIA = BM / (4 * RPI), LIW = BN / (4 * RPI);   // load instructions per wavefront per operand
+    constexpr int LIA = BM / (NW * RPI), LIW = BN / (NW * RPI);   // load instructions per wavefront per operand
     constexpr int VM = 2 * (LIA + LIW);              // loads of the two stages after the one awaited
     // Tail stages (a stage count that is not a multiple of four) cost registers
     // in the large-tile kernels, so only the small-tile ones carry them.
     constexpr bool TAIL = BM == 128;
-    static_assert(BM >= 128 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
+    static_assert(BM >= 128 && BN >= 64 && BM <= 256 && BN <= 256 && TN >= 1 && LIA >= 1 && LIW >= 1, "tile");
     static_assert(SB == 64 || SB == 128, "stage depth");
     constexpr int AB = BM * SB, WB = BN * SB;        // bytes of one stage buffer per operand
     static_assert(4 * (AB + WB) <= 160 * 1024, "LDS");
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned char A_0[AB], A_1[AB], A_2[AB], A_3[AB];
     __shared__ __attribute__((aligned(1024))) unsigned char W_0[WB], W_1[WB], W_2[WB], W_3[WB];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2, l32 = lane % 32, half = lane / 32;
+    const int wm = wave / NWN, wn = wave % NWN, l32 = lane % 32, half = lane / 32;
     int tmi, tni;
     tile_of(blockIdx.x, (g.M + BM - 1) / BM, (g.N + BN - 1) / BN, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn * (BN / 2) + j * 32 + l32, sw = swz(row);
+            const int row = wn * (BN / NWN) + j * 32 + l32, sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
                 const int c = FP8 ? ks * 4 + half * 2 + q : ks * 2 + half;
@@ -319,10 +321,11 @@ __global__ __launch_bounds__(256) void k_gemm_deep(GemmArgs g) {
     // the residual forms the loads of up to eight passes are issued before
     // any store.
     constexpr int CW = 32 * TN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
-    static_assert(32 * CW * 4 <= AB, "epilogue staging fits one A buffer");
-    float* lds = (float*)(wave == 0 ? A_0 : wave == 1 ? A_1 : wave == 2 ? A_2 : A_3);
+    static_assert((NW / 4) * 32 * CW * 4 <= AB, "epilogue staging fits the A buffers");
+    float* lds = (float*)((wave % 4 == 0 ? A_0 : wave % 4 == 1 ? A_1 : wave % 4 == 2 ? A_2 : A_3) +
+                          (wave / 4) * 32 * CW * 4);
     const int c4 = lane % CH, rr = lane / CH;           // float4 column chunk and row-in-pass of this lane
-    const int nb = n0 + wn * CW + 4 * c4;               // its first output column
+    const int nb = n0 + wn * CW + 4 * c4;               // its first output column (CW = BN / NWN)
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
     if (ncol && g.bias) {
@@ -403,9 +406,9 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     // gives most CUs a workgroup.  256x256 and 256x128 hold one workgroup per
     // CU (LDS), 128x128 two (64-byte stages) or one (128-byte stages), 128x64 one.
     const int t256 = tiles(256, 256), t256x128 = tiles(256, 128), t128 = tiles(128, 128);
-    if (rows256 && t256 >= 256) {
-        if (f8) LWO_KL((k_gemm_deep<256, 256, 64, true, EPI>), t256, 256, 0, st, g);
-        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI>), t256, 256, 0, st, g);
+    if (rows256 && t256 >= 256) {   // eight wavefronts: two per SIMD
+        if (f8) LWO_KL((k_gemm_deep<256, 256, 64, true, EPI, 4>), t256, 512, 0, st, g);
+        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI, 4>), t256, 512, 0, st, g);
     } else if (rows256 && t256x128 >= 192 && t256x128 <= 256) {
         if (f8) LWO_KL((k_gemm_deep<256, 128, 64, true, EPI>), t256x128, 256, 0, st, g);
         else LWO_KL((k_gemm_deep<256, 128, 64, false, EPI>), t256x128, 256, 0, st, g);
@@ -413,8 +416,8 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
         if (f8) LWO_KL((k_gemm_deep<128, 128, 64, true, EPI>), t128, 256, 0, st, g);
         else LWO_KL((k_gemm_deep<128, 128, 64, false, EPI>), t128, 256, 0, st, g);
     } else if (t128 >= 128) {  // one workgroup per CU: 128-byte stages keep more bytes in flight
-        if (f8) LWO_KL((k_gemm_deep<128, 128, 128, true, EPI>), t128, 256, 0, st, g);
-        else LWO_KL((k_gemm_deep<128, 128, 128, false, EPI>), t128, 256, 0, st, g);
+        if (f8) LWO_KL((k_gemm_deep<128, 128, 128, true, EPI, 4>), t128, 512, 0, st, g);
+        else LWO_KL((k_gemm_deep<128, 128, 128, false, EPI, 4>), t128, 512, 0, st, g);
     } else {
         const int t = tiles(128, 64);
         if (f8) LWO_KL((k_gemm_deep<128, 64, 128, true, EPI>), t, 256, 0, st, g);
