@@ -149,6 +149,29 @@ def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12):
                       + note}
 
 
+def mfma_probe(torch, lwo, s, reps: int = 3) -> dict:
+    """Sustained dense MFMA rate of lwo_probe_mfma (bf16 and fp8, three
+    workgroups of four wavefronts per CU, the most its registers let one CU
+    hold at once, independent accumulator chains): what the matrix cores
+    deliver at the clock they hold under full load.  Best of `reps`."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 3 * cus
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    out = {"blocks": blocks}
+    for name, dt, iters in (("bf16", lwo.BF16, 20000), ("fp8", lwo.FP8_E4M3, 5000)):
+        lwo.probe_mfma(dt, blocks, iters, sink.data_ptr(), sink.numel(), s.cuda_stream)   # warm-up
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fl = lwo.probe_mfma(dt, blocks, iters, sink.data_ptr(), sink.numel(), s.cuda_stream)
+            e1.record(s)
+            e1.synchronize()
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[name + "_tflops"] = round(best, 1)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +297,8 @@ def main() -> int:
     peak_gib = pinned_peak(torch, 1 << 30, s, reps=5)
     peak = max(peak_block, peak_gib)
     log(f"pinned H2D peak: block-sized {peak_block:.1f} GB/s, 1 GiB {peak_gib:.1f} GB/s")
+    probe = mfma_probe(torch, lwo, s)
+    log(f"MFMA probe: bf16 {probe['bf16_tflops']} TFLOP/s, fp8 {probe['fp8_tflops']} TFLOP/s sustained")
 
     m = L - k
     copies_per_step = m if m >= 3 else 0
@@ -296,6 +321,8 @@ def main() -> int:
         ach = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[kdt], "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS[kdt], 4)}
+        if kdt in ("bf16", "fp8"):   # context: the sustained rate the probe measured on this GPU
+            roof.update({"probe_peak": probe[kdt + "_tflops"], "frac_of_probe": round(ach / probe[kdt + "_tflops"], 4)})
     else:
         ach = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -341,6 +368,7 @@ def main() -> int:
         "pack_threads": st.pack_threads or None,
         "build_s": round(st.build_ms / 1e3, 2),
         "roofline": roof,
+        "mfma_probe": probe,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }

@@ -404,6 +404,21 @@ lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* c
 lwo_status lwo_op_rmsnorm_qk(int32_t dtype, void* qkv, int32_t M, int32_t D, const void* gq, const void* gk,
                              void* stream);
 
+/* Dense MFMA throughput probe.  It is a measurement, not a step of the
+ * method: block kernels are set against the published dense peak and, for
+ * context, against what the matrix cores sustain at the clock they run at
+ * under full load.  It enqueues `blocks` workgroups of 256 threads (4 or more
+ * per CU fill every SIMD).  Each wavefront runs 4 * iters independent MFMAs
+ * on register operands: dtype BF16 uses v_mfma_f32_32x32x16_bf16 (32768
+ * flops each), FP8_E4M3 uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales
+ * (131072 flops each).  `sink` (device, caller-owned, at least blocks * 256
+ * floats) receives one float per thread.  *flops returns the launch's flop
+ * count; the caller divides it by the time it measures on `stream`.
+ * LWO_EINVAL for another dtype, blocks outside [1, 65536], iters outside
+ * [1, 10^6], a short or misaligned sink, or a NULL stream. */
+lwo_status lwo_probe_mfma(int32_t dtype, int32_t blocks, int32_t iters, float* sink, uint64_t sink_floats, void* stream,
+                          double* flops);
+
 /* Thread-local description of the last failure ("" if none). */
 const char* lwo_last_error(void);
 

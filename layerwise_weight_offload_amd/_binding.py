@@ -109,13 +109,14 @@ _lib_op_attention = _sig("lwo_op_attention", C.c_int, _I, _P, _I, _P, _I, _P, _I
 _lib_op_layernorm = _sig("lwo_op_layernorm", C.c_int, _P, _I, _I, _I, _P, _I, _I, _P, _I, _P, _P)
 _lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P, _P)
 _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
+_lib_probe_mfma = _sig("lwo_probe_mfma", C.c_int, _I, _I, _I, _P, C.c_uint64, _P, C.POINTER(C.c_double))
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
             "lwo_build_block_store", "lwo_build_mixed_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
             "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
-            "lwo_op_quantize_rows", "lwo_op_rmsnorm_qk",
+            "lwo_op_quantize_rows", "lwo_op_rmsnorm_qk", "lwo_probe_mfma",
             "lwo_destroy_block_store", "lwo_last_error", "lwo_sha256", "lwo_cache_publish", "lwo_cache_open",
             "lwo_cache_extents", "lwo_cache_close"]
 
@@ -152,6 +153,13 @@ def op_quantize_rows(inp, M, N, codes, scales, stream):
 
 def op_rmsnorm_qk(dtype, qkv, M, D, gq, gk, stream):
     _check(_lib_op_rmsnorm_qk(dtype, _v(qkv), M, D, _v(gq), _v(gk), _v(stream)))
+
+
+def probe_mfma(dtype, blocks, iters, sink, sink_floats, stream) -> float:
+    """Enqueue the MFMA throughput probe; returns the launch's flop count (see lwo_probe_mfma)."""
+    fl = C.c_double(0.0)
+    _check(_lib_probe_mfma(dtype, blocks, iters, _v(sink), sink_floats, _v(stream), C.byref(fl)))
+    return fl.value
 
 
 def last_error() -> str:

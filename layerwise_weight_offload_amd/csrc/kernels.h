@@ -70,5 +70,7 @@ hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float
 hipError_t launch_checksum(const void* dev, uint64_t bytes, uint64_t* acc, hipStream_t st);
 hipError_t launch_checksum_compare(uint64_t* acc, uint64_t expect, hipStream_t st);
 hipError_t launch_zero_u64(uint64_t* p, int n, hipStream_t st);
+// MFMA throughput probe: `blocks` x 256 threads, 4 * iters MFMAs per wavefront, one float per thread to sink.
+hipError_t launch_mfma_peak(bool fp8, int blocks, int iters, float* sink, hipStream_t st);
 
 }  // namespace lwo

@@ -107,3 +107,14 @@ extern "C" lwo_status lwo_op_rmsnorm_qk(int32_t dtype, void* qkv, int32_t M, int
     if (!stream) return bad("rmsnorm_qk: stream is NULL");
     return launched(launch_rmsnorm_qk(qkv, dtype, M, D, gq, gk, (hipStream_t)stream), "rmsnorm_qk");
 }
+
+extern "C" lwo_status lwo_probe_mfma(int32_t dtype, int32_t blocks, int32_t iters, float* sink, uint64_t sink_floats,
+                                     void* stream, double* flops) {
+    clear_error();
+    if (dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) return bad("probe_mfma: dtype must be BF16 or FP8_E4M3");
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000) return bad("probe_mfma: blocks or iters out of range");
+    if (!sink || ((uintptr_t)sink & 3u) || sink_floats < (uint64_t)blocks * 256) return bad("probe_mfma: sink");
+    if (!stream) return bad("probe_mfma: stream is NULL");
+    if (flops) *flops = (double)blocks * 4 /* wavefronts */ * 4.0 * iters * (dtype == LWO_BF16 ? 32768.0 : 131072.0);
+    return launched(launch_mfma_peak(dtype == LWO_FP8_E4M3, blocks, iters, sink, (hipStream_t)stream), "probe_mfma");
+}

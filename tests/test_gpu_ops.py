@@ -298,3 +298,20 @@ def test_op_argument_validation(lib):
     with pytest.raises(lib.LwoError):   # head dim 96
         lib.op_attention(BF16, a.data_ptr(), 96, a.data_ptr(), 96, a.data_ptr(), 96, a.data_ptr(), 96, 1, 1, 4, 4,
                          96, s.cuda_stream)
+
+
+# ------------------------------------------------------------------ MFMA throughput probe
+
+def test_probe_mfma_counts_and_rejects(lib):
+    torch = _torch()
+    s = _stream()
+    sink = torch.full((8 * 256,), float("nan"), dtype=torch.float32, device="cuda:0")
+    for dt, per in ((BF16, 32768), (FP8, 131072)):
+        fl = lib.probe_mfma(dt, 8, 10, sink.data_ptr(), sink.numel(), s.cuda_stream)
+        s.synchronize()
+        assert fl == 8 * 4 * 4 * 10 * per
+        assert bool(torch.isfinite(sink).all())
+    with pytest.raises(lib.LwoError):
+        lib.probe_mfma(F32, 8, 10, sink.data_ptr(), sink.numel(), s.cuda_stream)
+    with pytest.raises(lib.LwoError):   # sink shorter than blocks * 256 floats
+        lib.probe_mfma(BF16, 9, 10, sink.data_ptr(), sink.numel(), s.cuda_stream)
