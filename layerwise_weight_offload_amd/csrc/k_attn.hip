@@ -76,18 +76,27 @@ template <> struct TrGeom<64> {    // 128-byte rows: rows r, r+2 share banks
     static __device__ int fv(int r) { return 4 * ((r >> 1) & 1); }
 };
 
-template <int DH, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void k_attn_tr(AttnArgs a) {
+// KSP = 2 splits the key tiles of one query tile between two groups of NW
+// wavefronts (the first and the second half of the tiles, each group with its
+// own K/V buffers), so a grid of few query tiles still puts two wavefronts on
+// every SIMD; the groups' softmax states and accumulators merge through LDS at
+// the end (the merge is exact: O and the row sum share each group's reference
+// point, both rescaled to the larger one).
+template <int DH, int NW, int KSP = 1>
+__global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
     using G = TrGeom<DH>;
     constexpr int BN = 64, QW = 32, NC = G::NC, PITCH = NC * 16, NVALID = DH / 8;
     constexpr int KS = (DH + 15) / 16, NT = (DH + 31) / 32;   // QK k-steps, PV output tiles of 32 columns
     constexpr int LI = NC / NW;                      // load instructions per wavefront per operand and tile
     static_assert(NC % NW == 0 && 2 * KS <= NC && 4 * NT <= NC, "geometry");
     constexpr int TB = BN * PITCH;                   // bytes per K or V tile
-    constexpr int KOFF = 0, VOFF = 2 * TB;           // K buffers at 0, TB; V buffers at 2 TB, 3 TB
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+    constexpr int KOFF = 0, VOFF = 2 * TB;           // K buffers at 0, TB; V buffers at 2 TB, 3 TB (per group)
+    static_assert(KSP == 1 || KSP == 2, "key split");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[KSP * 4 * TB];
 
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tid = threadIdx.x, wave = (tid / kWave) % NW, lane = tid % kWave;
+    const int grp = tid / (kWave * NW);              // key group (0 unless KSP = 2)
+    unsigned char* const smem = lds_all + grp * 4 * TB;
     const int l32 = lane % 32, half = lane / 32;
     const int h = blockIdx.y, b = blockIdx.z;
     const int Tq = a.Tq, Tk = a.Tk;
@@ -270,18 +279,49 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_tr(AttnArgs a) {
         }
     };
 
-    const int ntile = (Tk + BN - 1) / BN;
-    issue(std::integral_constant<int, 0>{}, 0);
-    for (int j = 0; j < ntile; j += 2) {
+    // Group g takes tiles [g nt0, min((g + 1) nt0, ntile)); every wavefront runs the
+    // same nt0 iterations so that the barriers match, skipping tiles past its range.
+    const int ntile = (Tk + BN - 1) / BN, nt0 = (ntile + KSP - 1) / KSP;
+    const int t0 = grp * nt0, tend = min(t0 + nt0, ntile);
+    if (t0 < tend) issue(std::integral_constant<int, 0>{}, t0 * BN);
+    for (int j = 0; j < nt0; j += 2) {
         // Tile j in buffer 0: its loads are this wavefront's only outstanding ones; the
         // barrier publishes every wavefront's loads and frees buffer 1 for tile j + 1.
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (j + 1 < ntile) issue(std::integral_constant<int, 1>{}, (j + 1) * BN);
-        tile(std::integral_constant<int, 0>{}, j * BN);
-        if (j + 1 >= ntile) break;
+        if (t0 + j + 1 < tend) issue(std::integral_constant<int, 1>{}, (t0 + j + 1) * BN);
+        if (t0 + j < tend) tile(std::integral_constant<int, 0>{}, (t0 + j) * BN);
+        if (j + 1 >= nt0) break;
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (j + 2 < ntile) issue(std::integral_constant<int, 0>{}, (j + 2) * BN);
-        tile(std::integral_constant<int, 1>{}, (j + 1) * BN);
+        if (t0 + j + 2 < tend) issue(std::integral_constant<int, 0>{}, (t0 + j + 2) * BN);
+        if (t0 + j + 1 < tend) tile(std::integral_constant<int, 1>{}, (t0 + j + 1) * BN);
+    }
+
+    if constexpr (KSP == 2) {
+        // Group 1 leaves m, l and its accumulators in LDS (lane-contiguous per
+        // wavefront) and ends; group 0 merges them into its own.
+        constexpr int NF = NT * 16 + 2;
+        static_assert(NW * NF * kWave * 4 <= KSP * 4 * TB, "merge fits the tile buffers");
+        float* red = (float*)lds_all + wave * NF * kWave;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                             // every wavefront is done with the tile buffers
+        if (grp == 1) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[(nt * 16 + r) * kWave + lane] = oacc[nt][r];
+            red[(NT * 16) * kWave + lane] = m_i;
+            red[(NT * 16 + 1) * kWave + lane] = l_i;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = red[(NT * 16) * kWave + lane], l1 = red[(NT * 16 + 1) * kWave + lane];
+        const float m = fmaxf(m_i, m1);
+        const float c0 = __builtin_amdgcn_exp2f(m_i - m), c1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[nt][r] = oacc[nt][r] * c0 + red[(nt * 16 + r) * kWave + lane] * c1;
+        l_i = l_i * c0 + l1 * c1;
     }
 
     if (qi >= Tq) return;
@@ -351,9 +391,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if (a.Tq <= 0 || a.B <= 0) return hipSuccess;
     if (a.Tk <= 0) return hipErrorInvalidValue;
     if (a.dtype == LWO_BF16) {
+        // d 64 / 72: four wavefronts per 128 queries leave one wavefront per SIMD
+        // when there are at most as many query tiles as CUs; then the key tiles
+        // are split over two groups of wavefronts (at least two tiles each).
+        const long qtiles = (long)((a.Tq + 127) / 128) * a.H * a.B;
+        const bool ksplit = qtiles <= 256 && a.Tk > 2 * 64;
         switch (a.dh) {
-            case 64: LWO_KL((k_attn_tr<64, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a); break;
-            case 72: LWO_KL((k_attn_tr<72, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a); break;
+            case 64:
+                if (ksplit) LWO_KL((k_attn_tr<64, 4, 2>), dim3((a.Tq + 127) / 128, a.H, a.B), 512, 0, st, a);
+                else LWO_KL((k_attn_tr<64, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a);
+                break;
+            case 72:
+                if (ksplit) LWO_KL((k_attn_tr<72, 4, 2>), dim3((a.Tq + 127) / 128, a.H, a.B), 512, 0, st, a);
+                else LWO_KL((k_attn_tr<72, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a);
+                break;
             case 128: LWO_KL((k_attn_tr<128, 8>), dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
