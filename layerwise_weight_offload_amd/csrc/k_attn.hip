@@ -211,6 +211,22 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
                 }
             }
         }
+        // V^T fragments of keys 0..31 (16 keys per k-step): read now, in flight
+        // during the softmax below, whose two-half reductions use a lane swap
+        // (VALU) rather than an LDS permute so that nothing waits for them early.
+#define VREAD(T, KS, VF)                                                                  \
+    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                   \
+        LDS_RD64_TR16(VF[KS][nt][0], vaddr[nt], BO + ((T) * 32 + 16 * (KS)) * PITCH);     \
+        LDS_RD64_TR16(VF[KS][nt][1], vaddr[nt], BO + ((T) * 32 + 16 * (KS) + 8) * PITCH); \
+    }
+        intx2 va[2][NT][2], vb[2][NT][2];
+        VREAD(0, 0, va);
+        VREAD(0, 1, va);
+        auto swap_halves = [](float x, auto op) {
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        };
+
         // s[t][r]: key key0 + 32t + 8(r/4) + 4 half + r%4, query qi
         if (key0 + BN > Tk) {
 #pragma unroll
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        mx = swap_halves(mx, [](float u, float v) { return fmaxf(u, v); }) * sl2;
         const bool need = mx > m_i + 8.0f;
         if (__ballot(need)) {
             const float m_new = need ? mx : m_i;
@@ -246,37 +262,32 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
                 s[t][r] = p;
                 rs += p;
             }
-        rs += __shfl_xor(rs, 32);
-        l_i += rs;
+        l_i += swap_halves(rs, [](float u, float v) { return u + v; });
 
-        // ---- O^T += V^T P^T, 16 keys per k-step; the reads of one 32-key half in flight together
+        // ---- O^T += V^T P^T, one k-step (16 keys) at a time.  Keys 32..63's
+        // fragments are read while keys 0..31's MFMAs run; every wait leaves at
+        // most 2 NT reads outstanding (the counter holds 15).
+        auto pv = [&](int t, int ks, intx2 (&vf)[2][NT][2]) {
+            bf16x8 pf;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            __builtin_amdgcn_sched_barrier(0);   // one half's V fragments live at a time
-            intx2 vf[2][NT][2];
+            for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    LDS_RD64_TR16(vf[ks][nt][0], vaddr[nt], BO + (t * 32 + 16 * ks) * PITCH);
-                    LDS_RD64_TR16(vf[ks][nt][1], vaddr[nt], BO + (t * 32 + 16 * ks + 8) * PITCH);
-                }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks == 0) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(2 * NT) : "memory");
-                else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                bf16x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    asm volatile("" : "+v"(vf[ks][nt][0]), "+v"(vf[ks][nt][1]));
-                    const intx4 v4 = {vf[ks][nt][0][0], vf[ks][nt][0][1], vf[ks][nt][1][0], vf[ks][nt][1][1]};
-                    oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pf, oacc[nt],
-                                                                       0, 0, 0);
-                }
+            for (int nt = 0; nt < NT; ++nt) {
+                asm volatile("" : "+v"(vf[ks][nt][0]), "+v"(vf[ks][nt][1]));
+                const intx4 v4 = {vf[ks][nt][0][0], vf[ks][nt][0][1], vf[ks][nt][1][0], vf[ks][nt][1][1]};
+                oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pf, oacc[nt], 0, 0, 0);
             }
-        }
+        };
+        VREAD(1, 0, vb);
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(2 * NT) : "memory");   // keys 0..31 landed
+        VREAD(1, 1, vb);
+        pv(0, 0, va);
+        pv(0, 1, va);
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(2 * NT) : "memory");   // keys 32..47
+        pv(1, 0, vb);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        pv(1, 1, vb);
+#undef VREAD
     };
 
     // Group g takes tiles [g nt0, min((g + 1) nt0, ntile)); every wavefront runs the
