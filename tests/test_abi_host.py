@@ -249,3 +249,25 @@ def test_mixed_build_validation_before_device(lib):
         with pytest.raises(lib.LwoError) as e:
             lib.build_mixed_store([a, b], list(m.block_type), extents=src)
         assert "device" in str(e.value)
+
+
+def test_build_rejects_scratch_in_asm_read_kernels():
+    """The kernels that await inline-asm LDS reads by hand must not spill; the
+    build parses hipcc's resource-usage remarks and names any that do."""
+    import importlib.util
+    path = os.path.join(ROOT, "layerwise_weight_offload_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("lwo_build_under_test", path)
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    pre = "/x/k.hip:13:1: remark: "
+    tail = " [-Rpass-analysis=kernel-resource-usage]"
+    text = "\n".join([
+        pre + "Function Name: _ZN3lwo11k_gemm_deepILi256ELi256ELi64ELb0ELi0ELi4EEEvNS_8GemmArgsE" + tail,
+        pre + "    ScratchSize [bytes/lane]: 0" + tail,
+        pre + "Function Name: _ZN3lwo9k_attn_trILi128ELi8ELi1EEEvNS_8AttnArgsE" + tail,
+        pre + "    ScratchSize [bytes/lane]: 16" + tail,
+        pre + "Function Name: _ZN3lwo10k_attn_f32ILi128EEEvNS_8AttnArgsE" + tail,   # plain loads: allowed
+        pre + "    ScratchSize [bytes/lane]: 36" + tail,
+    ])
+    bad = b._scratch_users(text)
+    assert len(bad) == 1 and "k_attn_tr" in bad[0] and "16 bytes" in bad[0]
