@@ -26,6 +26,7 @@ lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     const size_t o_xr = take(M * D * 4), o_mod = take((size_t)d.batch * 6 * D * 4), o_h = take(M * D * ae);
+    const size_t o_silu = video ? 0 : take((size_t)d.batch * D * 4);
     const size_t o_big = take(M * std::max(3 * D, F) * ae), o_attn = take(M * D * ae);
     const size_t o_cq = video ? take(M * D * ae) : 0, o_ckv = video ? take(Mc * 2 * D * ae) : 0;
     const size_t o_q8 = fp8 ? take(M * std::max(D, F)) : 0, o_q8s = fp8 ? take(std::max(M, Mc) * 4) : 0;
@@ -41,6 +42,7 @@ lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
     ws->bytes = off;
     ws->xr = (float*)(b + o_xr);
     ws->mod = (float*)(b + o_mod);
+    ws->silu_cond = video ? nullptr : (float*)(b + o_silu);
     ws->h = b + o_h;
     ws->big = b + o_big;
     ws->attn = b + o_attn;
@@ -125,10 +127,12 @@ void KernelTimer::destroy() {
         }                                                                                 \
     } while (0)
 
-lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* ctx,
-                              hipStream_t st) {
+lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* cond,
+                              const void* ctx, hipStream_t st) {
     const size_t n = (size_t)d.batch * d.tokens * d.hidden;
     LWO_LAUNCH(launch_to_f32(x, d.act_dtype, ws.xr, n, st));
+    if (d.kind == LWO_KIND_DIT)   // SiLU(cond) feeds the adaLN linear of every block: once per step
+        LWO_LAUNCH(launch_silu(cond, d.act_dtype, ws.silu_cond, d.batch * d.hidden, st));
     if (d.linear_dtype == LWO_FP8_E4M3)   // the context feeds the cross K/V linears of every block: quantise once
         LWO_LAUNCH(launch_quant_rows(ctx, d.batch * d.ctx_tokens, d.hidden, ws.ctx8, ws.ctx8_scale, st));
     return LWO_OK;
@@ -216,7 +220,7 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
 
     if (d.kind == LWO_KIND_DIT) {
         LWO_LAUNCH(timed("adaln_modulation", 2.0 * B * 6 * D * D, 6.0 * D * D * ae,
-                         [&] { return launch_mod_dit(cond, p.ada_w, p.ada_b, act, ws.mod, B, D, st); }));
+                         [&] { return launch_mod_dit(ws.silu_cond, p.ada_w, p.ada_b, act, ws.mod, B, D, st); }));
         LWO_LAUNCH(ln(mod, 0, 1, ws.h, act, nullptr));
         GemmArgs g = gemm_args(d, ws.h, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
         g.out = big; g.ldo = 3 * D;

@@ -59,12 +59,18 @@ hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream
 // ------------------------------------------------------------------ adaLN modulation
 
 // DiT kind: mod[b, n] = sum_k SiLU(cond[b, k]) W[n, k] + bias[n], n < 6D.
+// SiLU(cond) [B, D] in fp32, once per step: every block's adaLN GEMV reads it.
+template <typename T>
+__global__ void k_silu(const T* __restrict__ in, float* __restrict__ out, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) out[i] = silu(to_f(in[i]));
+}
+
 // A GEMV over the [6D, D] weight, bound by reading it once: 16 lanes own one
 // row, a workgroup owns 16 rows.  K goes in windows of 16 16-byte loads per
-// lane; each window's loads are issued before SiLU(cond) of the window is
-// computed into LDS (for up to four batches), so the two overlap.
+// lane; each window's loads are issued before SiLU(cond) of the window (computed
+// once per step) is staged into LDS (for up to four batches), so the two overlap.
 template <typename T>
-__global__ __launch_bounds__(256) void k_mod_dit(const T* __restrict__ cond, const T* __restrict__ w,
+__global__ __launch_bounds__(256) void k_mod_dit(const float* __restrict__ sc_in, const T* __restrict__ w,
                                                  const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
     constexpr int EV = 16 / sizeof(T);                  // elements per 16-byte load (8 bf16, 4 f32)
     constexpr int CL = 16, WIN = CL * 16 * EV;          // loads per lane per window, window elements
@@ -83,10 +89,8 @@ __global__ __launch_bounds__(256) void k_mod_dit(const T* __restrict__ cond, con
             }
             const int wn = min(WIN, D - k0);
             __syncthreads();                            // the previous window's reads are done
-            for (int i = threadIdx.x; i < nb * WIN; i += 256) {
-                const int j = i / WIN, kk = i % WIN;
-                if (kk < wn) sc[j][kk] = silu(to_f(cond[(size_t)(b0 + j) * D + k0 + kk]));
-            }
+            for (int j = 0; j < nb; ++j)
+                for (int kk = threadIdx.x; kk < wn; kk += 256) sc[j][kk] = sc_in[(size_t)(b0 + j) * D + k0 + kk];
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < CL; ++i) {
@@ -111,9 +115,7 @@ __global__ __launch_bounds__(256) void k_mod_dit(const T* __restrict__ cond, con
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float v = acc[j];
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            const float v = row16_reduce(acc[j], [](float a, float b) { return a + b; });
             if (l16 == 0 && n < 6 * D && j < nb) mod[(size_t)(b0 + j) * 6 * D + n] = v + to_f(bias[n]);
         }
     }
@@ -128,12 +130,19 @@ __global__ void k_mod_video(const T* __restrict__ cond, const T* __restrict__ ta
         mod[i] = to_f(cond[i]) + to_f(table[i % n]);
 }
 
-hipError_t launch_mod_dit(const void* cond, const void* w, const void* b, int dt, float* mod, int B, int D,
+hipError_t launch_silu(const void* in, int dt, float* out, int n, hipStream_t st) {
+    const int g = grid_for((size_t)n, 256);
+    if (dt == LWO_F32) LWO_KL((k_silu<float>), g, 256, 0, st, (const float*)in, out, n);
+    else LWO_KL((k_silu<bf16>), g, 256, 0, st, (const bf16*)in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_mod_dit(const float* silu_cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st) {
     if (D < 8 || D % 8) return hipErrorInvalidValue;
     const dim3 grid((6 * D + 15) / 16);
-    if (dt == LWO_F32) LWO_KL((k_mod_dit<float>), grid, 256, 0, st, (const float*)cond, (const float*)w, (const float*)b, mod, B, D);
-    else LWO_KL((k_mod_dit<bf16>), grid, 256, 0, st, (const bf16*)cond, (const bf16*)w, (const bf16*)b, mod, B, D);
+    if (dt == LWO_F32) LWO_KL((k_mod_dit<float>), grid, 256, 0, st, silu_cond, (const float*)w, (const float*)b, mod, B, D);
+    else LWO_KL((k_mod_dit<bf16>), grid, 256, 0, st, silu_cond, (const bf16*)w, (const bf16*)b, mod, B, D);
     return hipGetLastError();
 }
 

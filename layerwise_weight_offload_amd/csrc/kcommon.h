@@ -24,16 +24,43 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }   // v_cvt_pk_bf16_f32: nearest-even
 
+// Cross-lane reductions with DPP moves (VALU, no LDS round trip).  dpp<C, R>
+// returns, in the lanes of the 16-lane rows enabled by R, the value of the
+// lane that DPP control C selects, and `old` in the other rows.
+template <int C, int R = 0xF>
+__device__ __forceinline__ float dpp(float v, float old) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), C, R, 0xF, false));
+}
+
+// op over each 16-lane row, left in every lane of the row: quad_perm [1,0,3,2]
+// and [2,3,0,1] combine the lanes of a quad, row_half_mirror the two quads of
+// an 8-lane half, row_mirror the two halves.
+template <typename Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+    v = op(v, dpp<0xB1>(v, 0.0f));
+    v = op(v, dpp<0x4E>(v, 0.0f));
+    v = op(v, dpp<0x141>(v, 0.0f));
+    return op(v, dpp<0x140>(v, 0.0f));
+}
+
+// op over the wavefront, returned as a wave-uniform value: row_bcast15 folds
+// row 0 into row 1 and row 2 into row 3, row_bcast31 rows 0-1 into rows 2-3,
+// and lane 63 then holds the result (`id`: op's identity, for the rows a
+// broadcast leaves unchanged).
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op, float id) {
+    v = row16_reduce(v, op);
+    v = op(v, dpp<0x142, 0xA>(v, id));
+    v = op(v, dpp<0x143, 0xC>(v, id));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; }, 0.0f);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, -INFINITY);
 }
 
 // tanh(t) = 1 - 2 / (exp(2t) + 1), with exp(2t) = 2^(2t log2 e) on v_exp_f32.

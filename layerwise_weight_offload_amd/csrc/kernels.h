@@ -56,7 +56,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_to_f32(const void* x, int dt, float* xr, size_t n, hipStream_t st);
 hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream_t st);
-hipError_t launch_mod_dit(const void* cond, const void* w, const void* b, int dt, float* mod, int B, int D,
+// SiLU of the conditioning vector [n], to fp32 (once per step, DiT kind).
+hipError_t launch_silu(const void* in, int dt, float* out, int n, hipStream_t st);
+// mod [B, 6D] = silu_cond [B, D] x w^T + b (the DiT adaLN linear; w [6D, D] and b in dtype dt).
+hipError_t launch_mod_dit(const float* silu_cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st);
 hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* mod, int B, int D, hipStream_t st);
 // LayerNorm of the fp32 rows xr [M, D]; with mod, y = LN(x)(1 + mod[b, scale_chunk]) + mod[b, shift_chunk]

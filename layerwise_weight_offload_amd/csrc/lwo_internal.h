@@ -82,6 +82,7 @@ BlockPtrs block_ptrs(const Layout& L, const lwo_model_desc& d, const char* base)
 struct Workspace {
     float* xr = nullptr;        // fp32 residual [M, D]
     float* mod = nullptr;       // fp32 modulation [B, 6, D]
+    float* silu_cond = nullptr; // DiT kind: SiLU(cond) [B, D] fp32, once per step
     void* h = nullptr;          // LN output [M, D] act dtype
     void* big = nullptr;        // [M, max(3D, F)] act dtype: qkv, then FFN hidden
     void* attn = nullptr;       // attention output [M, D] act dtype
@@ -118,9 +119,10 @@ struct KernelTimer {
 lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Workspace& ws,
                          const void* cond, const void* ctx, hipStream_t stream, KernelTimer* kt);
 
-// Step prologue/epilogue: x (act dtype) -> fp32 residual, and back.
-lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* ctx,
-                              hipStream_t stream);
+// Step prologue/epilogue: x (act dtype) -> fp32 residual (and, DiT kind, SiLU(cond)
+// for every block's adaLN linear; fp8 linears: the context's e4m3 codes), and back.
+lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, const void* x, const void* cond,
+                              const void* ctx, hipStream_t st);
 lwo_status enqueue_step_end(const lwo_model_desc& d, const Workspace& ws, void* x, hipStream_t stream);
 
 // Checksum of `bytes` (multiple of 8) device bytes; adds into acc[0].  When

@@ -542,7 +542,7 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
         const lwo_model_desc& bd = s->tdesc[s->btype[b]];
         return enqueue_block(bd, block_ptrs(s->tlay[s->btype[b]], bd, base), s->ws, cond, ctx, st, &s->kt);
     };
-    LWO_TRY(enqueue_step_begin(d, s->ws, x, ctx, st));
+    LWO_TRY(enqueue_step_begin(d, s->ws, x, cond, ctx, st));
     for (int b = 0; b < k; ++b) {
         LWO_TRY(run_block(b, s->resident + s->roff[b]));
     }
