@@ -13,6 +13,16 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python -m layerwise_weight_offload_amd.build "
                       f"or __graft_entry__.build()); there is no fallback implementation")
 
+# PyTorch ships its own HIP runtime library.  When it is installed, load it
+# before liblwo.so so that the library binds to that same runtime: a process
+# that uses both (tests, bench.py) then has one HIP runtime whichever package
+# it imports first.  Two runtimes in one process do not share devices.  The
+# binding uses nothing from PyTorch.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = C.CDLL(LIB_PATH)
 
 # enums (include/lwo.h)

