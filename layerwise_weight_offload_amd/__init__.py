@@ -4,8 +4,9 @@ Thin Python binding over the C ABI in ``include/lwo.h`` (``liblwo.so``,
 built in-tree by ``layerwise_weight_offload_amd.build``).  Every function
 here only marshals arguments; all work runs in the library's C++ host code
 and HIP kernels.  Device buffers and streams are passed as raw integers
-(``tensor.data_ptr()``, ``stream.cuda_stream``), so the binding itself does
-not depend on PyTorch.
+(``tensor.data_ptr()``, ``stream.cuda_stream``), so the binding uses nothing
+from PyTorch; when PyTorch is installed it is imported before the library is
+loaded, so that both bind to one HIP runtime in the process.
 
 Importing fails loudly if the library has not been built: there is no
 fallback implementation.
