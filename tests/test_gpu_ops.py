@@ -203,6 +203,9 @@ def _attn_case(lib, dtype, B, H, Tq, Tk, d, fused_qkv, n_rows, seed):
     (2, 2, 200, 40, 72, False, 200),          # cross with fewer keys than one tile
     (2, 3, 77, 40, 128, False, 77),           # d 128: one partial query block, one partial key tile
     (1, 2, 300, 130, 128, True, 300),         # d 128: ragged queries, three key tiles, the last partial
+    (1, 3, 129, 128, 128, False, 129),        # d 128: two full key tiles (even tile count)
+    (2, 2, 64, 64, 128, True, 64),            # d 128: one full key tile
+    (1, 2, 520, 700, 128, False, 520),        # d 128: eleven key tiles, three query blocks
     (2, 2, 100, 150, 72, False, 100),         # key tiles split over two groups: the second has one partial tile
     (1, 16, 2100, 300, 72, False, 48),        # d 72 with more query tiles than CUs: no key split
     (1, 64, 600, 200, 64, False, 48),         # d 64 with more query tiles than CUs: no key split
