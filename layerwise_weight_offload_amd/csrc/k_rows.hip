@@ -282,6 +282,46 @@ __global__ __launch_bounds__(256) void k_rmsnorm_qk(T* __restrict__ qkv, int M, 
     }
 }
 
+// bf16 rows with 16-byte accesses, kept as raw bf16 in registers (half the
+// registers of a float copy): the same arithmetic, in the same order, as above.
+template <int NV8>
+__global__ __launch_bounds__(256) void k_rmsnorm_qk_b8(bf16* __restrict__ qkv, int M, int D, const bf16* __restrict__ gq,
+                                                       const bf16* __restrict__ gk) {
+    const int w = blockIdx.x * 4 + threadIdx.x / kWave;   // (row, part)
+    const int lane = threadIdx.x % kWave;
+    if (w >= 2 * M) return;
+    const int row = w >> 1, part = w & 1;
+    bf16* x = qkv + (size_t)row * 3 * D + (size_t)part * D;
+    const bf16* g = part ? gk : gq;
+    const int n8 = D / 8;
+    bf16x8 v[NV8];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV8; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n8) {
+            v[i] = *(const bf16x8*)(x + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; e += 4) {
+                const float a = (float)v[i][e], b = (float)v[i][e + 1], cc = (float)v[i][e + 2], d = (float)v[i][e + 3];
+                s += (a * a + b * b) + (cc * cc + d * d);
+            }
+        }
+    }
+    const float r = 1.0f / sqrtf(wave_sum(s) / (float)D + 1e-6f);
+#pragma unroll
+    for (int i = 0; i < NV8; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n8) {
+            const bf16x8 gv = *(const bf16x8*)(g + 8 * c);
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[i][e] * r * (float)gv[e]);
+            *(bf16x8*)(x + 8 * c) = o;
+        }
+    }
+}
+
 template <typename T>
 static hipError_t rms_dispatch(T* qkv, int M, int D, const T* gq, const T* gk, hipStream_t st) {
     const int need = (D / 4 + kWave - 1) / kWave;
@@ -299,6 +339,18 @@ static hipError_t rms_dispatch(T* qkv, int M, int D, const T* gq, const T* gk, h
 
 hipError_t launch_rmsnorm_qk(void* qkv, int dt, int M, int D, const void* gq, const void* gk, hipStream_t st) {
     if (dt == LWO_F32) return rms_dispatch<float>((float*)qkv, M, D, (const float*)gq, (const float*)gk, st);
+    if (D % 8 == 0) {
+        const int need = (D / 8 + kWave - 1) / kWave;
+        dim3 grid((2 * M + 3) / 4);
+#define LWO_RMS8_CASE(NV)                                                                                    \
+    if (need <= NV) {                                                                                        \
+        LWO_KL((k_rmsnorm_qk_b8<NV>), grid, 256, 0, st, (bf16*)qkv, M, D, (const bf16*)gq, (const bf16*)gk);  \
+        return hipGetLastError();                                                                            \
+    }
+        LWO_RMS8_CASE(1) LWO_RMS8_CASE(2) LWO_RMS8_CASE(4) LWO_RMS8_CASE(6) LWO_RMS8_CASE(8) LWO_RMS8_CASE(10)
+        LWO_RMS8_CASE(12) LWO_RMS8_CASE(16)
+#undef LWO_RMS8_CASE
+    }
     return rms_dispatch<bf16>((bf16*)qkv, M, D, (const bf16*)gq, (const bf16*)gk, st);
 }
 
@@ -329,7 +381,51 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
     if (lane == 0) scales[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
+// The same with the row held in registers between the two passes (one HBM read).
+template <int NV8>
+__global__ __launch_bounds__(256) void k_quant_rows_reg(const bf16* __restrict__ in, int M, int N,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (row >= M) return;
+    const bf16* x = in + (size_t)row * N;
+    const int n8 = N / 8;
+    bf16x8 v[NV8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV8; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n8) {
+            v[i] = *(const bf16x8*)(x + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[i][e]));
+        }
+    }
+    amax = wave_max(amax);
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    uint8_t* o = codes + (size_t)row * N;
+#pragma unroll
+    for (int i = 0; i < NV8; ++i) {
+        const int c = lane + kWave * i;
+        if (c < n8) {
+            const bf16x8 u = v[i];
+            uint32_t w0 = pack2_e4m3((float)u[0] * inv, (float)u[1] * inv) | (pack2_e4m3((float)u[2] * inv, (float)u[3] * inv) << 16);
+            uint32_t w1 = pack2_e4m3((float)u[4] * inv, (float)u[5] * inv) | (pack2_e4m3((float)u[6] * inv, (float)u[7] * inv) << 16);
+            *(uint2*)(o + 8 * c) = make_uint2(w0, w1);
+        }
+    }
+    if (lane == 0) scales[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
 hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st) {
+    const int need = (N / 8 + kWave - 1) / kWave;
+#define LWO_Q_CASE(NV)                                                                                         \
+    if (need <= NV) {                                                                                          \
+        LWO_KL((k_quant_rows_reg<NV>), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales);         \
+        return hipGetLastError();                                                                              \
+    }
+    LWO_Q_CASE(1) LWO_Q_CASE(2) LWO_Q_CASE(4) LWO_Q_CASE(8) LWO_Q_CASE(10) LWO_Q_CASE(16) LWO_Q_CASE(28)
+#undef LWO_Q_CASE
     LWO_KL((k_quant_rows), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales);
     return hipGetLastError();
 }
