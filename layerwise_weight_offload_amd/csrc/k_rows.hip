@@ -155,87 +155,104 @@ hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* 
 
 // ------------------------------------------------------------------ LayerNorm (+ modulation, + fp8)
 
-// OUT: 0 float, 1 bf16, 2 fp8 codes + row scale.  NV4 = float4 chunks per lane (>= D / 256).
+// OUT: 0 float, 1 bf16, 2 fp8 codes + row scale.  Two wavefronts share a row,
+// each holding half of it in registers (the first half has the odd float4 chunk,
+// NV4 chunks per lane, >= ceil(D / 8) / 64),
+// which keeps the register count, and so the wavefronts per SIMD, where the
+// HBM stream needs them; their partial sums meet in LDS and are added in a fixed
+// order (first half + second half), so every output type sees the same floats.
 template <int OUT, bool MOD, int NV4>
 __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M, int D, int T,
                                             const float* __restrict__ mod, int shc, int scc,
                                             void* __restrict__ out, float* __restrict__ out_scale) {
-    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    if (row >= M) return;
-    const int n4 = D / 4;
-    const float* x = xr + (size_t)row * D;
+    __shared__ float red[3][2][2];                      // [quantity][row of the workgroup][half]
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int rw = wave / 2, hf = wave % 2;             // row within the workgroup, half of the row
+    const int row = blockIdx.x * 2 + rw;
+    const bool live = row < M;
+    const int n4 = D / 4, nh0 = (n4 + 1) / 2;
+    const int nh = hf ? n4 - nh0 : nh0, c0 = hf ? nh0 : 0;   // float4 chunks of this half, first chunk
+    const float* x = xr + (size_t)(live ? row : 0) * D;
     float4 v[NV4];
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int c = lane + kWave * i;
-        v[i] = c < n4 ? load4(x + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[i] = live && c < nh ? load4(x + 4 * (c0 + c)) : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     }
-    const float mean = wave_sum(s) / (float)D;
+    s = wave_sum(s);
+    if (lane == 0) red[0][rw][hf] = s;
+    __syncthreads();
+    const float mean = (red[0][rw][0] + red[0][rw][1]) / (float)D;
     float s2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int c = lane + kWave * i;
-        if (c < n4) {
+        if (c < nh) {
             float a = v[i].x - mean, b = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
             s2 += (a * a + b * b) + (cc * cc + d * d);
         }
     }
-    const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)D + 1e-6f);
-    const int bi = row / T;
+    s2 = wave_sum(s2);
+    if (lane == 0) red[1][rw][hf] = s2;
+    __syncthreads();
+    const float rstd = 1.0f / sqrtf((red[1][rw][0] + red[1][rw][1]) / (float)D + 1e-6f);
+    const int bi = (live ? row : 0) / T;
     const float* shift = MOD ? mod + ((size_t)bi * 6 + shc) * D : nullptr;
     const float* scale = MOD ? mod + ((size_t)bi * 6 + scc) * D : nullptr;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
-        const int c = lane + kWave * i;
+        const int c = lane + kWave * i, cc4 = c0 + c;
         float4 y = make_float4((v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd,
                                (v[i].w - mean) * rstd);
-        if (MOD && c < n4) {
-            const float4 sc = load4(scale + 4 * c), sh = load4(shift + 4 * c);
+        if (MOD && c < nh) {
+            const float4 sc = load4(scale + 4 * cc4), sh = load4(shift + 4 * cc4);
             y.x = y.x * (1.0f + sc.x) + sh.x;
             y.y = y.y * (1.0f + sc.y) + sh.y;
             y.z = y.z * (1.0f + sc.z) + sh.z;
             y.w = y.w * (1.0f + sc.w) + sh.w;
         }
         if (OUT == 2) {
-            if (c < n4) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
+            if (c < nh) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
             v[i] = y;
-        } else if (c < n4) {
-            if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * c, y);
-            else store4((bf16*)out + (size_t)row * D + 4 * c, y);
+        } else if (live && c < nh) {
+            if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * cc4, y);
+            else store4((bf16*)out + (size_t)row * D + 4 * cc4, y);
         }
     }
     if (OUT == 2) {
         amax = wave_max(amax);
+        if (lane == 0) red[2][rw][hf] = amax;
+        __syncthreads();
+        amax = fmaxf(red[2][rw][0], red[2][rw][1]);
         const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
         uint8_t* o = (uint8_t*)out + (size_t)row * D;
 #pragma unroll
         for (int i = 0; i < NV4; ++i) {
             const int c = lane + kWave * i;
-            if (c < n4) {
+            if (live && c < nh) {
                 uint32_t lo = pack2_e4m3(v[i].x * inv, v[i].y * inv), hi = pack2_e4m3(v[i].z * inv, v[i].w * inv);
-                *(uint32_t*)(o + 4 * c) = lo | (hi << 16);
+                *(uint32_t*)(o + 4 * (c0 + c)) = lo | (hi << 16);
             }
         }
-        if (lane == 0) out_scale[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (live && lane == 0 && hf == 0) out_scale[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
     }
 }
 
 template <int OUT, bool MOD>
 static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float* mod, int shc, int scc, void* out,
                               float* out_scale, hipStream_t st) {
-    const int need = (D / 4 + kWave - 1) / kWave;
-    dim3 grid((M + 3) / 4);
+    const int need = ((D / 4 + 1) / 2 + kWave - 1) / kWave;
+    dim3 grid((M + 1) / 2);
 #define LWO_LN_CASE(NV)                                                                                     \
     if (need <= NV) {                                                                                       \
         LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, 0, st, xr, M, D, T, mod, shc, scc, out, out_scale);              \
         return hipGetLastError();                                                                           \
     }
-    LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(5) LWO_LN_CASE(8)
-    LWO_LN_CASE(12) LWO_LN_CASE(16) LWO_LN_CASE(20) LWO_LN_CASE(24) LWO_LN_CASE(32)
+    LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(6) LWO_LN_CASE(8)
+    LWO_LN_CASE(10) LWO_LN_CASE(12) LWO_LN_CASE(16)
 #undef LWO_LN_CASE
     return hipErrorInvalidValue;
 }
