@@ -2,9 +2,11 @@
 // conversion, adaLN modulation, LayerNorm (+ modulation, + fp8 row
 // quantisation), q/k RMSNorm, fp8 row quantisation and the slot checksum.
 //
-// Every row kernel gives one 64-lane wavefront to one row and keeps the row
-// in registers, so LayerNorm takes its mean and variance in two exact
-// passes without re-reading HBM; 4 wavefronts share a 256-thread workgroup.
+// The row kernels keep their row in registers, so LayerNorm takes its mean
+// and variance in two exact passes and the quantiser its amax and codes
+// without re-reading HBM: one 64-lane wavefront per row (q/k RMSNorm, fp8
+// quantisation) or two per row, each with half of it (LayerNorm); four
+// wavefronts share a 256-thread workgroup.
 #include "../../include/lwo.h"
 #include "kcommon.h"
 #include "kernels.h"
