@@ -362,16 +362,19 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // Epilogue through LDS.  Per 32-row slice of its block, a wavefront writes
     // the fp32 accumulators into its own buffer (row stride CW floats), reads
     // them back as row-contiguous float4s (CH lanes per row, RPP rows per
-    // pass) and applies the epilogue with 8- or 16-byte global accesses; for
-    // the residual forms the loads of up to eight passes are issued before
-    // any store.
+    // pass) and applies the epilogue with 8- or 16-byte global accesses.  The
+    // residual forms load the fp32 residual rows of slice i + 1 before slice
+    // i's LDS round trip, so the slices' load latencies overlap, and read the
+    // gate row once when the tile's rows all lie in one batch.
     constexpr int CW = 32 * TN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
+    constexpr bool RES = EPI >= EPI_GATED;
     static_assert((NW / 4) * 32 * CW * 4 <= AB, "epilogue staging fits the A buffers");
     float* lds = (float*)((wave % 4 == 0 ? A_0 : wave % 4 == 1 ? A_1 : wave % 4 == 2 ? A_2 : A_3) +
                           (wave / 4) * 32 * CW * 4);
     const int c4 = lane % CH, rr = lane / CH;           // float4 column chunk and row-in-pass of this lane
     const int nb = n0 + wn * CW + 4 * c4;               // its first output column (CW = BN / NWN)
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
+    const int mw = m0 + wm * (BM / 2);                  // first row of this wavefront's block
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
     if (ncol && g.bias) {
         const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nb);
@@ -380,8 +383,27 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     if (FP8 && ncol)
         ws4 = make_float4(g.w_scale[nb / g.w_seg], g.w_scale[(nb + 1) / g.w_seg], g.w_scale[(nb + 2) / g.w_seg],
                           g.w_scale[(nb + 3) / g.w_seg]);
+    float4 xq[2][NP];                                   // residual rows of two slices (residual forms)
+    auto load_x = [&](int i, float4 (&dst)[NP]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int m = mw + i * 32 + p * RPP + rr;
+            if (ncol && m < g.M) dst[p] = *(const float4*)(g.xr + (size_t)m * g.ldx + nb);
+        }
+    };
+    bool one_batch = false;
+    float4 g1 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (EPI == EPI_GATED) {
+        const int bfirst = m0 / g.rows_per_batch, blast = (min(m0 + BM, g.M) - 1) / g.rows_per_batch;
+        one_batch = bfirst == blast;
+        if (one_batch && ncol) g1 = *(const float4*)(g.gate + (size_t)bfirst * g.gate_ld + nb);
+    }
+    if constexpr (RES) load_x(0, xq[0]);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        if constexpr (RES) {
+            if (i + 1 < TM) load_x(i + 1, xq[(i + 1) % 2]);
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -390,30 +412,24 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
 #pragma unroll
         for (int h = 0; h < NP / PB; ++h) {
-            float4 v[PB], xo[PB], gt[PB];
+            float4 v[PB];
             int mrow[PB];
 #pragma unroll
             for (int it = 0; it < PB; ++it) {
                 const int row = (h * PB + it) * RPP + rr;
-                mrow[it] = m0 + wm * (BM / 2) + i * 32 + row;
+                mrow[it] = mw + i * 32 + row;
                 float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
                 if (FP8) {
                     const float as = mrow[it] < g.M ? g.a_scale[mrow[it]] : 0.0f;
                     a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
                 }
                 v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
-                if (EPI >= EPI_GATED && ncol && mrow[it] < g.M) {
-                    xo[it] = *(const float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb);
-                    gt[it] = EPI == EPI_GATED
-                                 ? *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb)
-                                 : make_float4(1.f, 1.f, 1.f, 1.f);
-                }
             }
 #pragma unroll
             for (int it = 0; it < PB; ++it) {
                 if (!ncol || mrow[it] >= g.M) continue;
                 const float4 y = v[it];
-                if (EPI <= EPI_GELU) {
+                if constexpr (EPI <= EPI_GELU) {
                     bf16x4 o;
                     if (EPI == EPI_GELU) {
                         o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
@@ -423,7 +439,10 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                     }
                     *(bf16x4*)((bf16*)g.out + (size_t)mrow[it] * g.ldo + nb) = o;
                 } else {
-                    const float4 x = xo[it], gg = gt[it];
+                    const float4 x = xq[i % 2][h * PB + it];
+                    float4 gg = g1;
+                    if (EPI == EPI_GATED && !one_batch)
+                        gg = *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb);
                     *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
                         make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
                 }
