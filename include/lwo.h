@@ -33,11 +33,24 @@
  *
  * Block layout (shared with the flat extents the caller may provide): every
  * tensor starts at a multiple of 256 bytes, the extent is a multiple of 4096
- * bytes, gaps are zero.  Weight matrices ("*.w", row-major [out, in]) are in
- * the linear dtype; biases, norm gains and modulation tables in the
- * activation dtype; with fp8 linears ten float32 per-tensor scales follow
- * every other tensor, in weight-matrix order.  lwo_block_layout() lists the
- * tensors and offsets.
+ * bytes, gaps are zero.  Weight matrices ("*.w", [out, in]) are in the
+ * linear dtype; biases, norm gains and modulation tables in the activation
+ * dtype; with fp8 linears ten float32 per-tensor scales follow every other
+ * tensor, in weight-matrix order.  lwo_block_layout() lists the tensors and
+ * offsets.
+ *
+ * Tiled weights: a bf16 or fp8 matrix that a block GEMM multiplies (every
+ * "*.w" except the DiT kind's "ada.w") is stored in tiles of 64 rows x 64
+ * bytes (32 bf16 or 64 fp8 elements of a row), the order in which the GEMM
+ * reads it.  For W [N, K] with R = K * element bytes per row (N a multiple
+ * of 64, R of 64), the byte at row n, row byte c of the row-major matrix
+ * sits at
+ *     ((n / 64) * (R / 64) + c / 64) * 4096 + (n % 64) * 64 + c % 64,
+ * so the tiles of one 64-row band follow each other along K, and a 64-row,
+ * 64-byte stage of the GEMM is 4 KB of consecutive memory.  Row-major
+ * matrices stacked along N (q|k|v) tile to the tiled stacked matrix.
+ * lwo_block_layout() marks these tensors (tiled = 1); float32 matrices and
+ * "ada.w" stay row-major.
  *
  * Block math (the workload's transformer block; LN is LayerNorm with eps
  * 1e-6 and no affine, GELU is the tanh form):
@@ -103,6 +116,7 @@ typedef struct lwo_tensor_info {
     int32_t rank;          /* 1 or 2 */
     int32_t shape[2];
     int32_t dtype;         /* lwo_dtype */
+    int32_t tiled;         /* 1: stored in 64-row x 64-byte tiles (above); 0: row-major */
 } lwo_tensor_info;
 
 /* Where build takes each block's flat extent from.
@@ -157,13 +171,20 @@ lwo_status lwo_block_layout(const lwo_model_desc* desc, lwo_tensor_info* out, in
 /* Flatten one block: tensors[i] (host, float32, row-major, in the order of
  * lwo_block_layout, excluding the fp8 scale table) are converted to their
  * stored dtype and written at their offsets in dst (host, dst_bytes >=
- * extent_bytes); padding is zeroed.  bf16 rounds to nearest-even; fp8 uses
+ * extent_bytes), tiled where the table says so; padding is zeroed.  bf16 rounds to nearest-even; fp8 uses
  * one scale per tensor, s = amax|w| / 448 (1 for an all-zero tensor), codes
  * = e4m3(w / s) rounded to nearest-even and saturated, and the scales go to
  * "linear.scales".  Source: [DLO] "Feature compatibility" (per-tensor fp8
  * linears finalised before offload); [LW] flattened tensors. */
 lwo_status lwo_pack_block(const lwo_model_desc* desc, const float* const* tensors, int32_t n_tensors,
                           void* dst, uint64_t dst_bytes);
+
+/* Rearrange a row-major weight [N, K] of dtype BF16 or FP8_E4M3 (host, N * K
+ * elements) into the tiled order above (host dst, the same size, not
+ * overlapping src), the form lwo_op_linear takes.  LWO_EINVAL for another
+ * dtype, N not a multiple of 64, K * element bytes not a multiple of 64, or a
+ * null pointer. */
+lwo_status lwo_tile_weight(int32_t dtype, const void* src, int32_t N, int32_t K, void* dst);
 
 /* Position-weighted SplitMix64 sum over a host buffer (bytes % 8 == 0):
  * sum_i SplitMix64(w_i ^ (i * 0x9E3779B97F4A7C15)) mod 2^64 over the
@@ -373,7 +394,9 @@ lwo_status lwo_destroy_block_store(lwo_store* store);
  * dtype F32: A, W, bias, out float32.  BF16: A, W, bias, out bf16.
  * FP8_E4M3: A and W e4m3 codes, Y = (A W^T) * w_scale[n / w_seg] *
  * a_scale[m] + bias with bias and out bf16.  xr and gate are float32.
- * K must be a multiple of 16 (F32), 64 (BF16) or 128 (FP8); lda = K, ldw = K. */
+ * K must be a multiple of 16 (F32), 64 (BF16) or 128 (FP8); lda = K.  W is
+ * row-major (ldw = K) for F32 and tiled (the block layout's tiled weights,
+ * lwo_tile_weight) for BF16 and FP8, with N a multiple of 64. */
 lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void* a, const float* a_scale, const void* w,
                          const float* w_scale, int32_t w_seg, const void* bias, int32_t M, int32_t N, int32_t K,
                          void* out, int32_t ldo, float* xr, int32_t ldx, const float* gate, int32_t gate_ld,

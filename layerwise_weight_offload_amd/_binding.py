@@ -50,7 +50,7 @@ class _Desc(C.Structure):
 
 class _TensorInfo(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("offset", C.c_uint64), ("bytes", C.c_uint64), ("rank", C.c_int32),
-                ("shape", C.c_int32 * 2), ("dtype", C.c_int32)]
+                ("shape", C.c_int32 * 2), ("dtype", C.c_int32), ("tiled", C.c_int32)]
 
 
 _FILL = C.CFUNCTYPE(C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_uint64)
@@ -87,6 +87,7 @@ _P = C.c_void_p
 _lib_block_layout = _sig("lwo_block_layout", C.c_int, C.POINTER(_Desc), C.POINTER(_TensorInfo), C.c_int32,
                          C.POINTER(C.c_int32), C.POINTER(C.c_uint64))
 _lib_pack_block = _sig("lwo_pack_block", C.c_int, C.POINTER(_Desc), C.POINTER(C.c_void_p), C.c_int32, _P, C.c_uint64)
+_lib_tile_weight = _sig("lwo_tile_weight", C.c_int, C.c_int32, _P, C.c_int32, C.c_int32, _P)
 _lib_extent_checksum = _sig("lwo_extent_checksum", C.c_int, _P, C.c_uint64, C.POINTER(C.c_uint64))
 _lib_register_ranges = _sig("lwo_register_ranges", C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_uint64), C.c_int32,
                             C.c_uint64, C.c_uint64, _REG, _UNREG, _P, C.POINTER(C.c_uint64),
@@ -121,7 +122,7 @@ _lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P
 _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
 _lib_probe_mfma = _sig("lwo_probe_mfma", C.c_int, _I, _I, _I, _P, C.c_uint64, _P, C.POINTER(C.c_double))
 
-EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_extent_checksum", "lwo_register_ranges",
+EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_tile_weight", "lwo_extent_checksum", "lwo_register_ranges",
             "lwo_build_block_store", "lwo_build_mixed_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
             "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
@@ -205,16 +206,27 @@ class ModelDesc:
 
 
 def block_layout(desc: ModelDesc):
-    """([dict(name, offset, bytes, shape, dtype)], extent_bytes)."""
+    """([dict(name, offset, bytes, shape, dtype, tiled)], extent_bytes)."""
     d = desc._c()
     n = C.c_int32()
     ext = C.c_uint64()
     _check(_lib_block_layout(C.byref(d), None, 0, C.byref(n), C.byref(ext)))
     arr = (_TensorInfo * n.value)()
     _check(_lib_block_layout(C.byref(d), arr, n.value, C.byref(n), C.byref(ext)))
-    out = [dict(name=t.name.decode(), offset=t.offset, bytes=t.bytes, shape=tuple(t.shape[:t.rank]), dtype=t.dtype)
-           for t in arr]
+    out = [dict(name=t.name.decode(), offset=t.offset, bytes=t.bytes, shape=tuple(t.shape[:t.rank]), dtype=t.dtype,
+                tiled=bool(t.tiled)) for t in arr]
     return out, ext.value
+
+
+def tile_weight(dtype: int, w: np.ndarray) -> np.ndarray:
+    """Row-major weight [N, K] (bf16 as uint16 or fp8 codes as uint8, host)
+    -> a new uint8 array in the tiled order that op_linear takes."""
+    w = np.ascontiguousarray(w)
+    if w.ndim != 2:
+        raise ValueError("tile_weight: w must be 2-D")
+    out = np.empty(w.nbytes, dtype=np.uint8)
+    _check(_lib_tile_weight(dtype, w.ctypes.data, w.shape[0], w.shape[1], out.ctypes.data))
+    return out
 
 
 def pack_block(desc: ModelDesc, tensors, dst=None, dst_bytes: int | None = None):

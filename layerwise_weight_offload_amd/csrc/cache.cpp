@@ -182,7 +182,7 @@ void block_digests(const std::vector<const uint8_t*>& ptr, uint64_t bytes, std::
 
 // ------------------------------------------------------------------ entry metadata
 
-const char* kFormat = "lwo-flat-blocks-1";
+const char* kFormat = "lwo-flat-blocks-2";
 constexpr uint64_t kPage = 4096;
 
 // Canonical text of everything that gives the block bytes their meaning.
@@ -194,8 +194,8 @@ std::string canonical_meta(const lwo_model_desc& d, const Layout& L) {
              (unsigned long long)L.extent_bytes);
     s += line;
     for (const TensorSlot& t : L.tensors) {
-        snprintf(line, sizeof(line), "%s %llu %llu %d %d %d %d\n", t.name.c_str(), (unsigned long long)t.offset,
-                 (unsigned long long)t.bytes, t.dtype, t.rank, t.shape[0], t.shape[1]);
+        snprintf(line, sizeof(line), "%s %llu %llu %d %d %d %d %s\n", t.name.c_str(), (unsigned long long)t.offset,
+                 (unsigned long long)t.bytes, t.dtype, t.rank, t.shape[0], t.shape[1], t.tiled ? "tiled" : "rows");
         s += line;
     }
     return s;
@@ -236,7 +236,8 @@ std::string manifest_json(const lwo_model_desc& d, const Layout& L, const std::s
     for (size_t i = 0; i < L.tensors.size(); ++i) {
         const TensorSlot& t = L.tensors[i];
         j += "    {\"name\": \"" + json_escape(t.name) + "\", \"offset\": " + std::to_string(t.offset) +
-             ", \"bytes\": " + std::to_string(t.bytes) + ", \"dtype\": " + std::to_string(t.dtype) + ", \"shape\": [" +
+             ", \"bytes\": " + std::to_string(t.bytes) + ", \"dtype\": " + std::to_string(t.dtype) +
+             ", \"tiled\": " + (t.tiled ? "true" : "false") + ", \"shape\": [" +
              std::to_string(t.shape[0]) + (t.rank == 2 ? ", " + std::to_string(t.shape[1]) : std::string()) + "]}" +
              (i + 1 < L.tensors.size() ? ",\n" : "\n");
     }

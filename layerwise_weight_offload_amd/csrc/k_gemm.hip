@@ -3,8 +3,10 @@
 //
 // k_gemm_deep takes bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) operands and
-// accumulates in fp32.  Both operands are K-contiguous ([M,K] activations,
-// [N,K] weights), so each lane's MFMA fragment is one or two 16-byte LDS
+// accumulates in fp32.  Both operands are K-contiguous: [M,K] row-major
+// activations, and [N,K] weights tiled in 64-row x 64-byte tiles (the block
+// layout's tiled weights), so a stage of weight rows is one run of
+// consecutive memory and each lane's MFMA fragment is one or two 16-byte LDS
 // reads from a row.  No split-K: every output is produced by one lane in a
 // fixed order, so results are deterministic run to run.  Tiles of 256x256,
 // 256x128, 128x128 or 128x64 by problem size; direct-to-LDS loads three
@@ -162,8 +164,14 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     const int m0 = tmi * BM, n0 = tni * BN;
     const size_t rowA = (size_t)g.K * (FP8 ? 1 : 2);
     const unsigned char* A0 = (const unsigned char*)g.a + (size_t)m0 * rowA;
-    const unsigned char* W0 = (const unsigned char*)g.w + (size_t)n0 * rowA;
+    const unsigned char* W0 = (const unsigned char*)g.w;
     // Rows past M or N re-read the last row (finite data); their outputs are not stored.
+    // W is tiled: 64-row x 64-byte tiles, those of one 64-row band in k order,
+    // so row n's 64 bytes at stage byte kb + 64 t sit at
+    // (n / 64) * rowA * 64 + (kb / 64 + t) * 4096 + (n % 64) * 64, and one stage
+    // of a 64-row band is 4 KB (64-byte stages) or 8 KB (128-byte) of
+    // consecutive memory.  offW holds the part that does not move with kb; the
+    // stage's own part is kb * 64.
     uint32_t offA[LIA], offW[LIW];
 #pragma unroll
     for (int i = 0; i < LIA; ++i) {
@@ -173,7 +181,8 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < LIW; ++i) {
         const int r = (wave * LIW + i) * RPI + lane / CPR;
-        offW[i] = (uint32_t)(min(r, g.N - 1 - n0) * rowA) + (uint32_t)(((lane % CPR) ^ swz(r)) * 16);
+        const int n = n0 + min(r, g.N - 1 - n0), ch = (lane % CPR) ^ swz(r);
+        offW[i] = (uint32_t)((n >> 6) * rowA * 64) + (uint32_t)((ch >> 2) * 4096 + (n & 63) * 64 + (ch & 3) * 16);
     }
     auto abuf = [&](auto b) -> unsigned char* {
         if constexpr (decltype(b)::value == 0) return A_0;
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                                              16, 0, 0);
 #pragma unroll
         for (int i = 0; i < LIW; ++i)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W0 + offW[i] + kb),
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W0 + offW[i] + kb * 64),
                                              (__attribute__((address_space(3))) void*)(wd + (wave * LIW + i) * RPI * SB),
                                              16, 0, 0);
     };

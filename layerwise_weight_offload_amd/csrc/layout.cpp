@@ -65,6 +65,10 @@ static void add(Layout& L, uint64_t& off, const char* name, int r0, int r1, int 
     t.shape[1] = r1;
     t.dtype = dtype;
     t.bytes = (uint64_t)r0 * (uint64_t)(r1 ? r1 : 1) * (uint64_t)dtype_bytes(dtype);
+    // GEMM weights in bf16/fp8 are stored in the order the GEMM reads them;
+    // the DiT modulation matrix is read by a GEMV and stays row-major.
+    const size_t len = std::strlen(name);
+    t.tiled = len > 2 && std::strcmp(name + len - 2, ".w") == 0 && dtype != LWO_F32 && std::strcmp(name, "ada.w") != 0;
     off += t.bytes;
     L.tensors.push_back(t);
 }
@@ -132,6 +136,20 @@ BlockPtrs block_ptrs(const Layout& L, const lwo_model_desc& d, const char* base)
         p.w_scale = (const float*)at("linear.scales");
     }
     return p;
+}
+
+// ------------------------------------------------------------------ tiled weights
+
+// Byte (n, c) of a row-major [N, R bytes] matrix goes to tile (n / 64, c / 64)
+// at ((n / 64) * (R / 64) + c / 64) * 4096, row n % 64, byte c % 64 of the
+// tile: each tile row is 64 consecutive bytes of the source row.
+void tile_rows(const unsigned char* src, int N, uint64_t R, unsigned char* dst) {
+    const uint64_t tiles_per_band = R / 64;
+    for (int n = 0; n < N; ++n) {
+        const unsigned char* row = src + (uint64_t)n * R;
+        unsigned char* band = dst + (uint64_t)(n / 64) * tiles_per_band * 4096 + (uint64_t)(n % 64) * 64;
+        for (uint64_t t = 0; t < tiles_per_band; ++t) std::memcpy(band + t * 4096, row + t * 64, 64);
+    }
 }
 
 // ------------------------------------------------------------------ codecs
@@ -209,6 +227,7 @@ extern "C" lwo_status lwo_block_layout(const lwo_model_desc* desc, lwo_tensor_in
         o.shape[0] = t.shape[0];
         o.shape[1] = t.shape[1];
         o.dtype = t.dtype;
+        o.tiled = t.tiled ? 1 : 0;
     }
     return LWO_OK;
 }
@@ -228,11 +247,14 @@ extern "C" lwo_status lwo_pack_block(const lwo_model_desc* desc, const float* co
     std::memset(out, 0, L.extent_bytes);
     float scales[10];
     int n_scales = 0;
+    std::vector<unsigned char> rowmajor;
     for (int i = 0; i < n_in; ++i) {
         const TensorSlot& t = L.tensors[i];
         const uint64_t n = t.bytes / (uint64_t)dtype_bytes(t.dtype);
         const float* src = tensors[i];
-        unsigned char* o = out + t.offset;
+        // A tiled tensor is encoded row-major into a scratch buffer, then tiled.
+        if (t.tiled) rowmajor.resize(t.bytes);
+        unsigned char* o = t.tiled ? rowmajor.data() : out + t.offset;
         if (t.dtype == LWO_F32) {
             std::memcpy(o, src, t.bytes);
         } else if (t.dtype == LWO_BF16) {
@@ -245,12 +267,23 @@ extern "C" lwo_status lwo_pack_block(const lwo_model_desc* desc, const float* co
             for (uint64_t j = 0; j < n; ++j) o[j] = f32_to_e4m3_rne_sat(src[j] / s);
             scales[n_scales++] = s;
         }
+        if (t.tiled) tile_rows(rowmajor.data(), t.shape[0], (uint64_t)t.shape[1] * dtype_bytes(t.dtype), out + t.offset);
     }
     if (fp8) {
         const TensorSlot& t = L.tensors.back();
         if (n_scales != 10) { set_error("pack: expected ten fp8 weight matrices"); return LWO_EINVAL; }
         std::memcpy(out + t.offset, scales, sizeof(scales));
     }
+    return LWO_OK;
+}
+
+extern "C" lwo_status lwo_tile_weight(int32_t dtype, const void* src, int32_t N, int32_t K, void* dst) {
+    clear_error();
+    if (dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) { set_error("tile_weight: dtype must be BF16 or FP8_E4M3"); return LWO_EINVAL; }
+    const uint64_t R = (uint64_t)(K > 0 ? K : 0) * (uint64_t)dtype_bytes(dtype);
+    if (N < 1 || K < 1 || N % 64 || R % 64) { set_error("tile_weight: N must be a multiple of 64 and K * element bytes of 64"); return LWO_EINVAL; }
+    if (!src || !dst) { set_error("tile_weight: null pointer"); return LWO_EINVAL; }
+    tile_rows((const unsigned char*)src, N, R, (unsigned char*)dst);
     return LWO_OK;
 }
 

@@ -42,6 +42,7 @@ struct TensorSlot {
     int rank = 1;
     int shape[2] = {0, 0};
     int dtype = LWO_F32;
+    bool tiled = false;   // 64-row x 64-byte tiles (bf16/fp8 GEMM weights)
 };
 
 struct Layout {

@@ -35,6 +35,7 @@ extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void*
     const int kq = dtype == LWO_F32 ? 16 : (dtype == LWO_BF16 ? 64 : 128);
     if (K % kq) return bad("linear: K must be a multiple of " + std::to_string(kq));
     if (N % 8) return bad("linear: N must be a multiple of 8");
+    if (dtype != LWO_F32 && N % 64) return bad("linear: N must be a multiple of 64 (tiled bf16/fp8 weights)");
     if (!a || !w || !aligned16(a) || !aligned16(w)) return bad("linear: a and w must be 16-byte aligned device pointers");
     if (bias && ((uintptr_t)bias & 7u)) return bad("linear: bias must be 8-byte aligned");
     if (dtype == LWO_FP8_E4M3 && (!a_scale || !w_scale || w_seg < 1)) return bad("linear: fp8 needs a_scale, w_scale and w_seg");

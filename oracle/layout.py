@@ -13,6 +13,11 @@ is this project's choice (the pages give none):
 * the extent is rounded up to a multiple of 4096 bytes; gaps are zero;
 * a weight matrix ``*.w`` is stored in the linear dtype, every other tensor
   (bias, norm gain, modulation table) in the activation dtype;
+* a bf16 or fp8 weight matrix other than the DiT kind's ``ada.w`` is stored
+  tiled: its row-major bytes, viewed as 64-row x 64-byte tiles, are written
+  tile after tile, the tiles of each 64-row band in order along a row and the
+  bands in row order; inside a tile its 64 rows of 64 bytes follow each other.
+  float32 matrices and ``ada.w`` are row-major;
 * with fp8 linears, the ten per-tensor float32 scales follow every other
   tensor, in the order the weight matrices appear.
 
@@ -72,6 +77,22 @@ def _names_shapes(kind: str, D: int, F: int):
     raise ValueError(kind)
 
 
+def tiled(name: str, dtype: str) -> bool:
+    return name.endswith(".w") and dtype in ("bf16", "fp8") and name != "ada.w"
+
+
+def tile_bytes(rows: np.ndarray) -> np.ndarray:
+    """[N, R] uint8 row-major bytes -> flat uint8 in the tiled order above."""
+    N, R = rows.shape
+    assert N % 64 == 0 and R % 64 == 0, (N, R)
+    return np.ascontiguousarray(rows.reshape(N // 64, 64, R // 64, 64).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_bytes(flat: np.ndarray, N: int, R: int) -> np.ndarray:
+    """Inverse of tile_bytes: flat tiled bytes -> [N, R] row-major bytes."""
+    return np.ascontiguousarray(flat.reshape(N // 64, R // 64, 64, 64).transpose(0, 2, 1, 3)).reshape(N, R)
+
+
 def _round_up(v: int, a: int) -> int:
     return (v + a - 1) // a * a
 
@@ -117,6 +138,8 @@ def pack_block(w, tensors) -> bytes:
             codes, sc = codecs.quantize_tensor_e4m3(t)
             raw = codes.reshape(-1)
             scales.append(sc)
+        if tiled(s.name, s.dtype):
+            raw = tile_bytes(raw.reshape(s.shape[0], -1))
         buf[s.offset:s.offset + s.nbytes] = raw
     if w.linear_dtype == "fp8":
         s = by_name["linear.scales"]
@@ -134,6 +157,8 @@ def unpack_block(w, extent: bytes) -> dict:
     raw = {}
     for s in slots:
         seg = b[s.offset:s.offset + s.nbytes]
+        if tiled(s.name, s.dtype):
+            seg = untile_bytes(seg, s.shape[0], s.nbytes // s.shape[0]).reshape(-1)
         if s.dtype == "f32":
             v = seg.view(np.float32).astype(np.float64)
         elif s.dtype == "bf16":

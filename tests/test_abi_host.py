@@ -40,8 +40,28 @@ def test_layout_matches_oracle(lib, name):
     got, ext = lib.block_layout(lib.ModelDesc.from_workload(w))
     want, want_ext = o_layout.layout_for(w)
     assert ext == want_ext
-    assert [(t["name"], t["offset"], t["bytes"], t["shape"], t["dtype"]) for t in got] == \
-           [(s.name, s.offset, s.nbytes, tuple(s.shape), DT[s.dtype]) for s in want]
+    assert [(t["name"], t["offset"], t["bytes"], t["shape"], t["dtype"], t["tiled"]) for t in got] == \
+           [(s.name, s.offset, s.nbytes, tuple(s.shape), DT[s.dtype], o_layout.tiled(s.name, s.dtype)) for s in want]
+
+
+@pytest.mark.parametrize("dtype,N,K", [(1, 64, 32), (1, 192, 1152), (2, 128, 64), (2, 64, 448)])
+def test_tile_weight_matches_oracle(lib, dtype, N, K):
+    rng = np.random.default_rng(N + K)
+    w = rng.integers(0, 1 << 16, (N, K), dtype=np.uint16) if dtype == 1 else rng.integers(0, 256, (N, K), dtype=np.uint8)
+    got = lib.tile_weight(dtype, w)
+    want = o_layout.tile_bytes(w.view(np.uint8).reshape(N, -1))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype,N,K", [(0, 64, 64), (1, 100, 64), (1, 64, 16), (2, 64, 32), (1, 0, 64)])
+def test_tile_weight_rejects(lib, dtype, N, K):
+    w = np.zeros((max(N, 1), K), dtype=np.uint16 if dtype != 2 else np.uint8)
+    with pytest.raises(lib.LwoError) as e:
+        if N == 0:
+            lib._binding._check(lib._binding._lib_tile_weight(dtype, w.ctypes.data, 0, K, w.ctypes.data))
+        else:
+            lib.tile_weight(dtype, w)
+    assert e.value.name == "LWO_EINVAL"
 
 
 def _edge_tensors(w, b):

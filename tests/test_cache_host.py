@@ -51,13 +51,14 @@ def test_publish_open_roundtrip(lib, tmp_path):
     entry = tmp_path / key
     man = json.loads((entry / "manifest.json").read_text())
     stride = (ext + 4095) // 4096 * 4096
-    assert man["format"] == "lwo-flat-blocks-1" and man["key"] == key == man["content_digest"]
+    assert man["format"] == "lwo-flat-blocks-2" and man["key"] == key == man["content_digest"]
     assert man["n_blocks"] == desc.n_blocks and man["extent_bytes"] == ext and man["stride"] == stride
     assert (entry / "blocks.bin").stat().st_size == stride * desc.n_blocks == man["file_bytes"]
     digests = [hashlib.sha256(b.tobytes()).digest() for b in bufs]
     assert man["block_sha256"] == [d.hex() for d in digests]
     assert hashlib.sha256(man["meta"].encode() + b"".join(digests)).hexdigest() == key
-    assert [t["name"] for t in man["tensors"]] == [t["name"] for t in lib.block_layout(desc)[0]]
+    assert [(t["name"], t["tiled"]) for t in man["tensors"]] == \
+           [(t["name"], t["tiled"]) for t in lib.block_layout(desc)[0]]
     raw = (entry / "blocks.bin").read_bytes()
     for b, buf in enumerate(bufs):   # extent then zero padding to the stride
         assert raw[b * stride:b * stride + ext] == buf.tobytes()

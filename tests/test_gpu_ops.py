@@ -50,6 +50,14 @@ def _stream():
     return s
 
 
+def _tiled_dev(lib, dtype, w_dev):
+    """Device copy of a row-major bf16 (torch) or fp8 (uint8 codes) weight in
+    the tiled order op_linear takes, made on the host by lwo_tile_weight."""
+    torch = _torch()
+    host = w_dev.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == BF16 else w_dev.cpu().numpy()
+    return torch.from_numpy(lib.tile_weight(dtype, host)).to("cuda:0")
+
+
 def _sample(rng, M, N, n):
     m = np.concatenate([rng.integers(0, M, n - 4), [0, M - 1, M - 1, (M // 128) * 128 % M]])
     nn = np.concatenate([rng.integers(0, N, n - 4), [0, N - 1, 0, N - 1]])
@@ -80,19 +88,20 @@ def test_linear_bf16_sampled(lib, M, N, K, epi):
     w32 = (rng.standard_normal((N, K), dtype=np.float32) * 0.02).astype(np.float32)
     b32 = (rng.standard_normal(N, dtype=np.float32) * 0.02).astype(np.float32)
     a, w, b = _bf16_dev(a32), _bf16_dev(w32), _bf16_dev(b32)
+    wt = _tiled_dev(lib, BF16, w)
     del a32, w32
     s = _stream()
     out = xr = gate = None
     T = max(1, M // 2)   # two "batches" for the gate
     if epi <= 1:
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
-        lib.op_linear(BF16, epi, a.data_ptr(), w.data_ptr(), M, N, K, s.cuda_stream, bias=b.data_ptr(),
+        lib.op_linear(BF16, epi, a.data_ptr(), wt.data_ptr(), M, N, K, s.cuda_stream, bias=b.data_ptr(),
                       out=out.data_ptr(), ldo=N)
     else:
         x0 = rng.standard_normal((M, N), dtype=np.float32)
         xr = torch.from_numpy(x0).to("cuda:0")
         gate = torch.from_numpy(rng.standard_normal((2, 6 * N), dtype=np.float32)).to("cuda:0") if epi == 2 else None
-        lib.op_linear(BF16, epi, a.data_ptr(), w.data_ptr(), M, N, K, s.cuda_stream, bias=b.data_ptr(),
+        lib.op_linear(BF16, epi, a.data_ptr(), wt.data_ptr(), M, N, K, s.cuda_stream, bias=b.data_ptr(),
                       xr=xr.data_ptr(), ldx=N, gate=gate.data_ptr() if gate is not None else 0, gate_ld=6 * N,
                       rows_per_gate=T)
     s.synchronize()
@@ -131,7 +140,7 @@ def test_linear_fp8_sampled(lib, M, N, K, seg):
     w_sc = (rng.uniform(0.5, 2.0, N // seg) * 1e-3).astype(np.float32)
     b32 = (rng.standard_normal(N, dtype=np.float32) * 0.02).astype(np.float32)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
-    a, w, asc, wsc, b = dev(a_codes), dev(w_codes), dev(a_sc), dev(w_sc), _bf16_dev(b32)
+    a, w, asc, wsc, b = dev(a_codes), dev(lib.tile_weight(FP8, w_codes)), dev(a_sc), dev(w_sc), _bf16_dev(b32)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     s = _stream()
     lib.op_linear(FP8, 0, a.data_ptr(), w.data_ptr(), M, N, K, s.cuda_stream, a_scale=asc.data_ptr(),
@@ -300,6 +309,8 @@ def test_op_argument_validation(lib):
     s = _stream()
     with pytest.raises(lib.LwoError):   # K not a multiple of 64
         lib.op_linear(BF16, 0, a.data_ptr(), a.data_ptr(), 8, 8, 32, s.cuda_stream, out=a.data_ptr(), ldo=8)
+    with pytest.raises(lib.LwoError):   # N not a multiple of 64 (tiled bf16 weights)
+        lib.op_linear(BF16, 0, a.data_ptr(), a.data_ptr(), 8, 96, 64, s.cuda_stream, out=a.data_ptr(), ldo=96)
     with pytest.raises(lib.LwoError):   # misaligned pointer
         lib.op_linear(BF16, 0, a.data_ptr() + 2, a.data_ptr(), 8, 8, 64, s.cuda_stream, out=a.data_ptr(), ldo=8)
     with pytest.raises(lib.LwoError):   # head dim 96

@@ -85,3 +85,58 @@ def test_fp8_scales_follow_weights_in_order():
     assert len(wl) == 10
     for i, a in enumerate(wl):
         assert sc[i] == np.float32(np.max(np.abs(a)) / np.float32(448))
+
+
+def test_tile_bytes_hand_positions():
+    """A 128 x 128-byte matrix makes 2 x 2 tiles of 4096 bytes: tile (band 0,
+    bytes 0-63) first, then (band 0, bytes 64-127), then band 1 likewise; in
+    a tile, row after row of 64 bytes.  Offsets below are worked by hand."""
+    rows = (np.arange(128 * 128, dtype=np.int64).reshape(128, 128) * 7919 % 251).astype(np.uint8)
+    flat = layout.tile_bytes(rows)
+    assert flat.size == 128 * 128
+    assert np.array_equal(flat[0:64], rows[0, 0:64])
+    assert np.array_equal(flat[64:128], rows[1, 0:64])
+    assert np.array_equal(flat[4032:4096], rows[63, 0:64])
+    assert np.array_equal(flat[4096:4160], rows[0, 64:128])
+    assert np.array_equal(flat[4096 + 5 * 64:4096 + 6 * 64], rows[5, 64:128])
+    assert np.array_equal(flat[8192:8256], rows[64, 0:64])
+    assert np.array_equal(flat[12288 + 63 * 64:16384], rows[127, 64:128])
+    assert np.array_equal(layout.untile_bytes(flat, 128, 128), rows)
+
+
+def test_tile_bytes_is_a_permutation_and_keeps_bands():
+    """Every tile row is 64 consecutive source bytes; a 64-row band's tiles
+    hold exactly that band's rows, so matrices stacked along N tile to the
+    stacked tiled matrix."""
+    rng = np.random.default_rng(5)
+    a, b = rng.integers(0, 256, (64, 192), dtype=np.uint8), rng.integers(0, 256, (128, 192), dtype=np.uint8)
+    stacked = layout.tile_bytes(np.concatenate([a, b]))
+    assert np.array_equal(stacked, np.concatenate([layout.tile_bytes(a), layout.tile_bytes(b)]))
+    assert np.array_equal(np.sort(stacked), np.sort(np.concatenate([a, b]).reshape(-1)))
+
+
+@pytest.mark.parametrize("name", ["dit_t_bf16", "video_t_fp8"])
+def test_pack_tiles_gemm_weights_only(name):
+    """bf16/fp8 GEMM weights are tiled; the DiT modulation matrix and every
+    non-matrix tensor keep their row-major bytes."""
+    w = lwo_synth.get(name)
+    t = lwo_synth.block_tensors(w, 0)
+    ext = np.frombuffer(layout.pack_block(w, t), np.uint8)
+    slots, _ = layout.layout_for(w)
+    names = [nm for nm, _ in lwo_synth.tensor_inventory(w)]
+    for nm, a in zip(names, t):
+        s = next(x for x in slots if x.name == nm)
+        seg = ext[s.offset:s.offset + s.nbytes]
+        if s.dtype == "bf16":
+            raw = codecs.bf16_encode(a).view(np.uint8).reshape(-1)
+        elif s.dtype == "fp8":
+            raw = codecs.quantize_tensor_e4m3(a)[0].reshape(-1)
+        else:
+            continue
+        if nm.endswith(".w") and nm != "ada.w":
+            assert layout.tiled(nm, s.dtype)
+            assert not np.array_equal(seg, raw)
+            assert np.array_equal(seg, layout.tile_bytes(raw.reshape(s.shape[0], -1)))
+        else:
+            assert not layout.tiled(nm, s.dtype)
+            assert np.array_equal(seg, raw)
