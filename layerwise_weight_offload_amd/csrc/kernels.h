@@ -28,7 +28,7 @@ enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_GATED = 2, EPI_RESID = 3 };
 
 struct GemmArgs {
     const void* a;          // [M, K] row-major, lda = K
-    const void* w;          // [N, K] row-major (a Linear weight [out, in])
+    const void* w;          // [N, K] (a Linear weight [out, in]): row-major for fp32, 64x64-byte tiles for bf16/fp8
     int M, N, K;
     int dtype;              // lwo_dtype of A and W: F32, BF16, or FP8_E4M3 (A codes + per-row a_scale)
     int act_dtype;          // dtype of bias and of `out`
