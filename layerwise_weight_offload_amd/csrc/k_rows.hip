@@ -261,6 +261,7 @@ static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float*
 
 hipError_t launch_ln(const float* xr, int M, int D, int T, const float* mod, int shift_chunk, int scale_chunk,
                      void* out, int out_dt, float* out_scale, hipStream_t st) {
+    if (M <= 0) return hipSuccess;   // no rows: nothing to launch (a zero grid is an invalid launch)
     const bool m = mod != nullptr;
     if (out_dt == LWO_F32) return m ? ln_dispatch<0, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
                                     : ln_dispatch<0, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
@@ -357,6 +358,7 @@ static hipError_t rms_dispatch(T* qkv, int M, int D, const T* gq, const T* gk, h
 }
 
 hipError_t launch_rmsnorm_qk(void* qkv, int dt, int M, int D, const void* gq, const void* gk, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
     if (dt == LWO_F32) return rms_dispatch<float>((float*)qkv, M, D, (const float*)gq, (const float*)gk, st);
     if (D % 8 == 0) {
         const int need = (D / 8 + kWave - 1) / kWave;
@@ -437,6 +439,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_reg(const bf16* __restrict__
 }
 
 hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
     const int need = (N / 8 + kWave - 1) / kWave;
 #define LWO_Q_CASE(NV)                                                                                         \
     if (need <= NV) {                                                                                          \

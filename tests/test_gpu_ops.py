@@ -303,6 +303,32 @@ def test_rmsnorm_qk(lib, M, D, dtype):
     assert np.array_equal(got[:, 2 * D:], before[:, 2 * D:])   # v untouched
 
 
+def test_ops_with_no_rows_write_nothing(lib):
+    """M = 0 (and Tq = 0) is a valid, empty call: it returns OK and leaves every output as it was."""
+    torch = _torch()
+    print("[empty] M = 0 for every op", flush=True)
+    s = _stream()
+    a = torch.zeros(64 * 64, dtype=torch.bfloat16, device="cuda:0")
+    w = torch.zeros(64 * 128, dtype=torch.uint8, device="cuda:0")
+    sc = torch.ones(64, dtype=torch.float32, device="cuda:0")
+    sent = torch.full((4096,), 7.0, dtype=torch.float32, device="cuda:0")
+    s8 = torch.full((4096,), 7, dtype=torch.uint8, device="cuda:0")
+    lib.op_linear(BF16, 0, a.data_ptr(), a.data_ptr(), 0, 64, 64, s.cuda_stream, out=sent.data_ptr(), ldo=64)
+    lib.op_linear(BF16, 2, a.data_ptr(), a.data_ptr(), 0, 64, 64, s.cuda_stream, xr=sent.data_ptr(), ldx=64,
+                  gate=sc.data_ptr(), gate_ld=64, rows_per_gate=1)
+    lib.op_linear(FP8, 0, w.data_ptr(), w.data_ptr(), 0, 64, 128, s.cuda_stream, a_scale=sc.data_ptr(),
+                  w_scale=sc.data_ptr(), w_seg=64, out=sent.data_ptr(), ldo=64)
+    lib.op_attention(BF16, a.data_ptr(), 64, a.data_ptr(), 64, a.data_ptr(), 64, sent.data_ptr(), 64, 1, 1, 0, 4, 64,
+                     s.cuda_stream)
+    lib.op_layernorm(sent.data_ptr(), 0, 64, sent.data_ptr(), BF16, s.cuda_stream)
+    lib.op_layernorm(sent.data_ptr(), 0, 64, s8.data_ptr(), FP8, s.cuda_stream, out_scale=sent.data_ptr())
+    lib.op_quantize_rows(a.data_ptr(), 0, 64, s8.data_ptr(), sent.data_ptr(), s.cuda_stream)
+    lib.op_rmsnorm_qk(BF16, sent.data_ptr(), 0, 64, a.data_ptr(), a.data_ptr(), s.cuda_stream)
+    lib.op_rmsnorm_qk(F32, sent.data_ptr(), 0, 64, sent.data_ptr(), sent.data_ptr(), s.cuda_stream)
+    s.synchronize()
+    assert bool((sent == 7.0).all()) and bool((s8 == 7).all())
+
+
 def test_op_argument_validation(lib):
     torch = _torch()
     a = torch.zeros(64 * 64, dtype=torch.bfloat16, device="cuda:0")
