@@ -79,6 +79,8 @@ def _sample(rng, M, N, n):
     (256, 15360, 5120, 0),       # video at 256 tokens: QKV
     (256, 5120, 13824, 2),       # video at 256 tokens: FFN down, gated
     (200, 576, 2304, 1),         # ragged M and N
+    (2000, 1088, 576, 2),        # gated, 128x128 tiles with ragged M and N and a stage tail
+    (2048, 1152, 128, 3),        # residual, 128x128 tiles with fewer stages than the loads in flight
 ])
 def test_linear_bf16_sampled(lib, M, N, K, epi):
     torch = _torch()
