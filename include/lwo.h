@@ -24,7 +24,9 @@
  *         not reused until dependent work completes).
  *
  * Conventions for every call:
- *   - returns lwo_status; LWO_OK is 0; no C++ exception crosses the ABI;
+ *   - returns lwo_status; LWO_OK is 0; no C++ exception crosses the ABI:
+ *     host memory exhaustion inside a call returns LWO_ENOMEM, any other
+ *     internal exception (e.g. a thread that cannot start) LWO_EIO;
  *   - on failure nothing is left half-built, and lwo_last_error() returns a
  *     thread-local message describing the last failure on this thread;
  *   - pointers documented as "device" are HIP device pointers on the

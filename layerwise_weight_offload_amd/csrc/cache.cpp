@@ -357,221 +357,261 @@ struct lwo_cache {
 // ------------------------------------------------------------------ C ABI
 
 extern "C" lwo_status lwo_sha256(const void* data, uint64_t bytes, uint8_t* out32) {
-    clear_error();
-    if ((!data && bytes) || !out32) { set_error("sha256: NULL argument"); return LWO_EINVAL; }
-    Sha256 h;
-    h.update(data, bytes);
-    h.final(out32);
-    return LWO_OK;
+    try {
+        clear_error();
+        if ((!data && bytes) || !out32) { set_error("sha256: NULL argument"); return LWO_EINVAL; }
+        Sha256 h;
+        h.update(data, bytes);
+        h.final(out32);
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_sha256");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_sha256", e.what());
+    } catch (...) {
+        return fail_exception("lwo_sha256", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_cache_publish(const char* dir, const lwo_model_desc* desc, const lwo_block_source* src,
                                         uint32_t wait_ms, char* key_out, int32_t* created) {
-    clear_error();
-    if (!dir || !desc || !src || !key_out || !created) { set_error("cache_publish: NULL argument"); return LWO_EINVAL; }
-    if (!src->extents && !src->fill) { set_error("cache_publish: source has neither extents nor fill"); return LWO_EINVAL; }
-    LWO_TRY(validate_desc(desc));
-    const lwo_model_desc& d = *desc;
-    const Layout L = make_layout(d);
-    const uint64_t ext = L.extent_bytes, stride = (ext + kPage - 1) / kPage * kPage;
-    const int n = d.n_blocks;
-    *created = 0;
-    key_out[0] = 0;
+    try {
+        clear_error();
+        if (!dir || !desc || !src || !key_out || !created) { set_error("cache_publish: NULL argument"); return LWO_EINVAL; }
+        if (!src->extents && !src->fill) { set_error("cache_publish: source has neither extents nor fill"); return LWO_EINVAL; }
+        LWO_TRY(validate_desc(desc));
+        const lwo_model_desc& d = *desc;
+        const Layout L = make_layout(d);
+        const uint64_t ext = L.extent_bytes, stride = (ext + kPage - 1) / kPage * kPage;
+        const int n = d.n_blocks;
+        *created = 0;
+        key_out[0] = 0;
 
-    // Pass 1: block digests (a fill source is packed into a scratch extent).
-    std::vector<uint8_t> digests;
-    std::vector<uint8_t> scratch;
-    if (src->extents) {
-        std::vector<const uint8_t*> ptr(n);
-        for (int b = 0; b < n; ++b) {
-            if (!src->extents[b]) { set_error("cache_publish: extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
-            ptr[b] = (const uint8_t*)src->extents[b];
-        }
-        block_digests(ptr, ext, digests);
-    } else {
-        scratch.assign(ext, 0);
-        digests.assign((size_t)n * 32, 0);
-        for (int b = 0; b < n; ++b) {
-            if (src->fill(src->user, b, scratch.data(), ext) != 0) {
-                set_error("cache_publish: fill failed for block " + std::to_string(b));
-                return LWO_EINVAL;
+        // Pass 1: block digests (a fill source is packed into a scratch extent).
+        std::vector<uint8_t> digests;
+        std::vector<uint8_t> scratch;
+        if (src->extents) {
+            std::vector<const uint8_t*> ptr(n);
+            for (int b = 0; b < n; ++b) {
+                if (!src->extents[b]) { set_error("cache_publish: extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
+                ptr[b] = (const uint8_t*)src->extents[b];
             }
-            Sha256 h;
-            h.update(scratch.data(), ext);
-            h.final(&digests[(size_t)b * 32]);
+            block_digests(ptr, ext, digests);
+        } else {
+            scratch.assign(ext, 0);
+            digests.assign((size_t)n * 32, 0);
+            for (int b = 0; b < n; ++b) {
+                if (src->fill(src->user, b, scratch.data(), ext) != 0) {
+                    set_error("cache_publish: fill failed for block " + std::to_string(b));
+                    return LWO_EINVAL;
+                }
+                Sha256 h;
+                h.update(scratch.data(), ext);
+                h.final(&digests[(size_t)b * 32]);
+            }
         }
-    }
-    const std::string meta = canonical_meta(d, L);
-    uint8_t cd[32];
-    content_digest(meta, digests, cd);
-    const std::string key = hex(cd, 32);
-    std::memcpy(key_out, key.c_str(), 65);
+        const std::string meta = canonical_meta(d, L);
+        uint8_t cd[32];
+        content_digest(meta, digests, cd);
+        const std::string key = hex(cd, 32);
+        std::memcpy(key_out, key.c_str(), 65);
 
-    // Ownership: an exclusive flock on <dir>/<key>.lock, polled up to wait_ms.
-    const std::string root = dir, entry = root + "/" + key, lockp = entry + ".lock";
-    ::mkdir(root.c_str(), 0755);
-    const int lfd = ::open(lockp.c_str(), O_RDWR | O_CREAT | O_CLOEXEC, 0644);
-    if (lfd < 0) { set_error("cache_publish: cannot open " + lockp + ": " + std::strerror(errno)); return LWO_EIO; }
-    const auto t0 = std::chrono::steady_clock::now();
-    while (::flock(lfd, LOCK_EX | LOCK_NB) != 0) {
-        if (errno != EWOULDBLOCK && errno != EINTR) {
-            ::close(lfd);
-            set_error(std::string("cache_publish: flock: ") + std::strerror(errno));
+        // Ownership: an exclusive flock on <dir>/<key>.lock, polled up to wait_ms.
+        const std::string root = dir, entry = root + "/" + key, lockp = entry + ".lock";
+        ::mkdir(root.c_str(), 0755);
+        const int lfd = ::open(lockp.c_str(), O_RDWR | O_CREAT | O_CLOEXEC, 0644);
+        if (lfd < 0) { set_error("cache_publish: cannot open " + lockp + ": " + std::strerror(errno)); return LWO_EIO; }
+        const auto t0 = std::chrono::steady_clock::now();
+        while (::flock(lfd, LOCK_EX | LOCK_NB) != 0) {
+            if (errno != EWOULDBLOCK && errno != EINTR) {
+                ::close(lfd);
+                set_error(std::string("cache_publish: flock: ") + std::strerror(errno));
+                return LWO_EIO;
+            }
+            if (std::chrono::steady_clock::now() - t0 >= std::chrono::milliseconds(wait_ms)) {
+                ::close(lfd);
+                set_error("cache_publish: another writer holds " + lockp);
+                return LWO_ETIMEOUT;
+            }
+            std::this_thread::sleep_for(std::chrono::milliseconds(5));
+        }
+        auto unlock = [&] { ::flock(lfd, LOCK_UN); ::close(lfd); };
+
+        if (exists(entry + "/manifest.json")) {   // published before: join it
+            unlock();
+            return LWO_OK;
+        }
+        // Stale temporaries of this key belong to writers that died holding the lock.
+        if (DIR* dd = ::opendir(root.c_str())) {
+            const std::string pre = ".tmp-" + key + "-";
+            std::vector<std::string> stale;
+            while (struct dirent* e = ::readdir(dd))
+                if (std::strncmp(e->d_name, pre.c_str(), pre.size()) == 0) stale.push_back(root + "/" + e->d_name);
+            ::closedir(dd);
+            for (const std::string& p : stale) remove_tree(p);
+        }
+        std::mt19937_64 rng((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ (uint64_t)::getpid());
+        const std::string tmp = root + "/.tmp-" + key + "-" + std::to_string(::getpid()) + "-" + std::to_string(rng() % 1000000);
+        if (::mkdir(tmp.c_str(), 0755) != 0) {
+            unlock();
+            set_error("cache_publish: cannot create " + tmp + ": " + std::strerror(errno));
             return LWO_EIO;
         }
-        if (std::chrono::steady_clock::now() - t0 >= std::chrono::milliseconds(wait_ms)) {
-            ::close(lfd);
-            set_error("cache_publish: another writer holds " + lockp);
-            return LWO_ETIMEOUT;
+        auto fail = [&](const std::string& msg) {
+            remove_tree(tmp);
+            unlock();
+            set_error("cache_publish: " + msg);
+            return LWO_EIO;
+        };
+        // Pass 2: blocks.bin (extent, zero padding to the stride).
+        {
+            const int fd = ::open((tmp + "/blocks.bin").c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
+            if (fd < 0) return fail("cannot create blocks.bin");
+            std::vector<uint8_t> pad(stride - ext, 0);
+            for (int b = 0; b < n; ++b) {
+                const void* p = src->extents ? src->extents[b] : nullptr;
+                if (!p) {
+                    if (src->fill(src->user, b, scratch.data(), ext) != 0) { ::close(fd); return fail("fill failed on the second pass"); }
+                    p = scratch.data();
+                }
+                if (!write_all(fd, p, ext) || (pad.size() && !write_all(fd, pad.data(), pad.size()))) {
+                    ::close(fd);
+                    return fail("write of blocks.bin failed");
+                }
+            }
+            const bool ok = ::fsync(fd) == 0;
+            ::close(fd);
+            if (!ok) return fail("fsync of blocks.bin failed");
         }
-        std::this_thread::sleep_for(std::chrono::milliseconds(5));
-    }
-    auto unlock = [&] { ::flock(lfd, LOCK_UN); ::close(lfd); };
-
-    if (exists(entry + "/manifest.json")) {   // published before: join it
+        {
+            const std::string j = manifest_json(d, L, meta, stride, digests, key);
+            const int fd = ::open((tmp + "/manifest.json").c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
+            if (fd < 0) return fail("cannot create manifest.json");
+            const bool ok = write_all(fd, j.data(), j.size()) && ::fsync(fd) == 0;
+            ::close(fd);
+            if (!ok) return fail("write of manifest.json failed");
+        }
+        if (!fsync_path(tmp, O_RDONLY | O_DIRECTORY)) return fail("fsync of the temporary directory failed");
+        if (::rename(tmp.c_str(), entry.c_str()) != 0) return fail(std::string("rename failed: ") + std::strerror(errno));
+        (void)fsync_path(root, O_RDONLY | O_DIRECTORY);
         unlock();
+        *created = 1;
         return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_cache_publish");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_cache_publish", e.what());
+    } catch (...) {
+        return fail_exception("lwo_cache_publish", "unknown exception");
     }
-    // Stale temporaries of this key belong to writers that died holding the lock.
-    if (DIR* dd = ::opendir(root.c_str())) {
-        const std::string pre = ".tmp-" + key + "-";
-        std::vector<std::string> stale;
-        while (struct dirent* e = ::readdir(dd))
-            if (std::strncmp(e->d_name, pre.c_str(), pre.size()) == 0) stale.push_back(root + "/" + e->d_name);
-        ::closedir(dd);
-        for (const std::string& p : stale) remove_tree(p);
-    }
-    std::mt19937_64 rng((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ (uint64_t)::getpid());
-    const std::string tmp = root + "/.tmp-" + key + "-" + std::to_string(::getpid()) + "-" + std::to_string(rng() % 1000000);
-    if (::mkdir(tmp.c_str(), 0755) != 0) {
-        unlock();
-        set_error("cache_publish: cannot create " + tmp + ": " + std::strerror(errno));
-        return LWO_EIO;
-    }
-    auto fail = [&](const std::string& msg) {
-        remove_tree(tmp);
-        unlock();
-        set_error("cache_publish: " + msg);
-        return LWO_EIO;
-    };
-    // Pass 2: blocks.bin (extent, zero padding to the stride).
-    {
-        const int fd = ::open((tmp + "/blocks.bin").c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
-        if (fd < 0) return fail("cannot create blocks.bin");
-        std::vector<uint8_t> pad(stride - ext, 0);
-        for (int b = 0; b < n; ++b) {
-            const void* p = src->extents ? src->extents[b] : nullptr;
-            if (!p) {
-                if (src->fill(src->user, b, scratch.data(), ext) != 0) { ::close(fd); return fail("fill failed on the second pass"); }
-                p = scratch.data();
-            }
-            if (!write_all(fd, p, ext) || (pad.size() && !write_all(fd, pad.data(), pad.size()))) {
-                ::close(fd);
-                return fail("write of blocks.bin failed");
-            }
-        }
-        const bool ok = ::fsync(fd) == 0;
-        ::close(fd);
-        if (!ok) return fail("fsync of blocks.bin failed");
-    }
-    {
-        const std::string j = manifest_json(d, L, meta, stride, digests, key);
-        const int fd = ::open((tmp + "/manifest.json").c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
-        if (fd < 0) return fail("cannot create manifest.json");
-        const bool ok = write_all(fd, j.data(), j.size()) && ::fsync(fd) == 0;
-        ::close(fd);
-        if (!ok) return fail("write of manifest.json failed");
-    }
-    if (!fsync_path(tmp, O_RDONLY | O_DIRECTORY)) return fail("fsync of the temporary directory failed");
-    if (::rename(tmp.c_str(), entry.c_str()) != 0) return fail(std::string("rename failed: ") + std::strerror(errno));
-    (void)fsync_path(root, O_RDONLY | O_DIRECTORY);
-    unlock();
-    *created = 1;
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_cache_open(const char* dir, const char* key, const lwo_model_desc* desc, int32_t verify,
                                      lwo_cache** out) {
-    clear_error();
-    if (!dir || !key || !desc || !out) { set_error("cache_open: NULL argument"); return LWO_EINVAL; }
-    *out = nullptr;
-    LWO_TRY(validate_desc(desc));
-    const Layout L = make_layout(*desc);
-    const uint64_t ext = L.extent_bytes, stride = (ext + kPage - 1) / kPage * kPage;
-    const int n = desc->n_blocks;
-    const std::string entry = std::string(dir) + "/" + key;
-    std::string j;
-    if (!read_file(entry + "/manifest.json", j)) { set_error("cache_open: no manifest in " + entry); return LWO_EIO; }
-    std::string fmt, meta, cdhex;
-    uint64_t m_ext = 0, m_stride = 0, m_n = 0, m_file = 0;
-    std::vector<uint8_t> digests;
-    if (!json_string(j, "format", fmt) || fmt != kFormat || !json_string(j, "meta", meta) ||
-        !json_string(j, "content_digest", cdhex) || !json_u64(j, "extent_bytes", m_ext) ||
-        !json_u64(j, "stride", m_stride) || !json_u64(j, "n_blocks", m_n) || !json_u64(j, "file_bytes", m_file) ||
-        !json_digest_list(j, "block_sha256", (int)m_n, digests)) {
-        set_error("cache_open: malformed manifest in " + entry);
-        return LWO_EIO;
+    try {
+        clear_error();
+        if (!dir || !key || !desc || !out) { set_error("cache_open: NULL argument"); return LWO_EINVAL; }
+        *out = nullptr;
+        LWO_TRY(validate_desc(desc));
+        const Layout L = make_layout(*desc);
+        const uint64_t ext = L.extent_bytes, stride = (ext + kPage - 1) / kPage * kPage;
+        const int n = desc->n_blocks;
+        const std::string entry = std::string(dir) + "/" + key;
+        std::string j;
+        if (!read_file(entry + "/manifest.json", j)) { set_error("cache_open: no manifest in " + entry); return LWO_EIO; }
+        std::string fmt, meta, cdhex;
+        uint64_t m_ext = 0, m_stride = 0, m_n = 0, m_file = 0;
+        std::vector<uint8_t> digests;
+        if (!json_string(j, "format", fmt) || fmt != kFormat || !json_string(j, "meta", meta) ||
+            !json_string(j, "content_digest", cdhex) || !json_u64(j, "extent_bytes", m_ext) ||
+            !json_u64(j, "stride", m_stride) || !json_u64(j, "n_blocks", m_n) || !json_u64(j, "file_bytes", m_file) ||
+            !json_digest_list(j, "block_sha256", (int)m_n, digests)) {
+            set_error("cache_open: malformed manifest in " + entry);
+            return LWO_EIO;
+        }
+        if (meta != canonical_meta(*desc, L) || m_ext != ext || m_stride != stride || m_n != (uint64_t)n ||
+            m_file != stride * (uint64_t)n) {
+            set_error("cache_open: the entry was published for a different block layout");
+            return LWO_EINVAL;
+        }
+        uint8_t cd[32];
+        content_digest(meta, digests, cd);
+        if (hex(cd, 32) != cdhex || cdhex != key) {
+            set_error("cache_open: content digest does not match the key");
+            return LWO_ECHECKSUM;
+        }
+        lwo_cache* c = new (std::nothrow) lwo_cache();
+        if (!c) { set_error("out of host memory"); return LWO_ENOMEM; }
+        c->fd = ::open((entry + "/blocks.bin").c_str(), O_RDONLY | O_CLOEXEC);
+        struct stat st;
+        if (c->fd < 0 || ::fstat(c->fd, &st) != 0 || (uint64_t)st.st_size != m_file) {
+            lwo_cache_close(c);
+            set_error("cache_open: blocks.bin is missing or has the wrong size");
+            return LWO_EIO;
+        }
+        c->map_bytes = m_file;
+        c->base = ::mmap(nullptr, m_file, PROT_READ, MAP_SHARED, c->fd, 0);
+        if (c->base == MAP_FAILED) {
+            c->base = nullptr;
+            lwo_cache_close(c);
+            set_error(std::string("cache_open: mmap failed: ") + std::strerror(errno));
+            return LWO_EIO;
+        }
+        c->extents.resize(n);
+        std::vector<const uint8_t*> ptr(n);
+        for (int b = 0; b < n; ++b) ptr[b] = (const uint8_t*)c->base + stride * (uint64_t)b, c->extents[b] = ptr[b];
+        if (verify) {
+            std::vector<uint8_t> got;
+            block_digests(ptr, ext, got);
+            for (int b = 0; b < n; ++b)
+                if (std::memcmp(&got[(size_t)b * 32], &digests[(size_t)b * 32], 32) != 0) {
+                    lwo_cache_close(c);
+                    set_error("cache_open: block " + std::to_string(b) + " does not match its manifest digest");
+                    return LWO_ECHECKSUM;
+                }
+        }
+        *out = c;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_cache_open");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_cache_open", e.what());
+    } catch (...) {
+        return fail_exception("lwo_cache_open", "unknown exception");
     }
-    if (meta != canonical_meta(*desc, L) || m_ext != ext || m_stride != stride || m_n != (uint64_t)n ||
-        m_file != stride * (uint64_t)n) {
-        set_error("cache_open: the entry was published for a different block layout");
-        return LWO_EINVAL;
-    }
-    uint8_t cd[32];
-    content_digest(meta, digests, cd);
-    if (hex(cd, 32) != cdhex || cdhex != key) {
-        set_error("cache_open: content digest does not match the key");
-        return LWO_ECHECKSUM;
-    }
-    lwo_cache* c = new (std::nothrow) lwo_cache();
-    if (!c) { set_error("out of host memory"); return LWO_ENOMEM; }
-    c->fd = ::open((entry + "/blocks.bin").c_str(), O_RDONLY | O_CLOEXEC);
-    struct stat st;
-    if (c->fd < 0 || ::fstat(c->fd, &st) != 0 || (uint64_t)st.st_size != m_file) {
-        lwo_cache_close(c);
-        set_error("cache_open: blocks.bin is missing or has the wrong size");
-        return LWO_EIO;
-    }
-    c->map_bytes = m_file;
-    c->base = ::mmap(nullptr, m_file, PROT_READ, MAP_SHARED, c->fd, 0);
-    if (c->base == MAP_FAILED) {
-        c->base = nullptr;
-        lwo_cache_close(c);
-        set_error(std::string("cache_open: mmap failed: ") + std::strerror(errno));
-        return LWO_EIO;
-    }
-    c->extents.resize(n);
-    std::vector<const uint8_t*> ptr(n);
-    for (int b = 0; b < n; ++b) ptr[b] = (const uint8_t*)c->base + stride * (uint64_t)b, c->extents[b] = ptr[b];
-    if (verify) {
-        std::vector<uint8_t> got;
-        block_digests(ptr, ext, got);
-        for (int b = 0; b < n; ++b)
-            if (std::memcmp(&got[(size_t)b * 32], &digests[(size_t)b * 32], 32) != 0) {
-                lwo_cache_close(c);
-                set_error("cache_open: block " + std::to_string(b) + " does not match its manifest digest");
-                return LWO_ECHECKSUM;
-            }
-    }
-    *out = c;
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_cache_extents(const lwo_cache* c, const void** out, int32_t cap, int32_t* n) {
-    clear_error();
-    if (!c) { set_error("cache_extents: NULL cache"); return LWO_EINVAL; }
-    if (n) *n = (int32_t)c->extents.size();
-    if (!out && cap == 0) return LWO_OK;
-    if (!out || cap < (int32_t)c->extents.size()) { set_error("cache_extents: capacity too small"); return LWO_EINVAL; }
-    for (size_t b = 0; b < c->extents.size(); ++b) out[b] = c->extents[b];
-    return LWO_OK;
+    try {
+        clear_error();
+        if (!c) { set_error("cache_extents: NULL cache"); return LWO_EINVAL; }
+        if (n) *n = (int32_t)c->extents.size();
+        if (!out && cap == 0) return LWO_OK;
+        if (!out || cap < (int32_t)c->extents.size()) { set_error("cache_extents: capacity too small"); return LWO_EINVAL; }
+        for (size_t b = 0; b < c->extents.size(); ++b) out[b] = c->extents[b];
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_cache_extents");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_cache_extents", e.what());
+    } catch (...) {
+        return fail_exception("lwo_cache_extents", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_cache_close(lwo_cache* c) {
-    clear_error();
-    if (!c) return LWO_OK;
-    if (c->base) ::munmap(c->base, c->map_bytes);
-    if (c->fd >= 0) ::close(c->fd);
-    delete c;
-    return LWO_OK;
+    try {
+        clear_error();
+        if (!c) return LWO_OK;
+        if (c->base) ::munmap(c->base, c->map_bytes);
+        if (c->fd >= 0) ::close(c->fd);
+        delete c;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_cache_close");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_cache_close", e.what());
+    } catch (...) {
+        return fail_exception("lwo_cache_close", "unknown exception");
+    }
 }

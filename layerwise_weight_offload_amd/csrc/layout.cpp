@@ -22,6 +22,26 @@ static thread_local std::string g_err;
 void set_error(const std::string& msg) { g_err = msg; }
 void clear_error() { g_err.clear(); }
 
+// No C++ exception crosses the C ABI: every entry point catches what its
+// body throws and reports it through these (which themselves never throw).
+lwo_status fail_alloc(const char* where) noexcept {
+    try {
+        g_err = std::string(where) + ": out of host memory";
+    } catch (...) {
+        g_err.clear();
+    }
+    return LWO_ENOMEM;
+}
+
+lwo_status fail_exception(const char* where, const char* what) noexcept {
+    try {
+        g_err = std::string(where) + ": " + what;
+    } catch (...) {
+        g_err.clear();
+    }
+    return LWO_EIO;
+}
+
 int dtype_bytes(int dt) { return dt == LWO_F32 ? 4 : dt == LWO_BF16 ? 2 : 1; }
 
 int Layout::find(const char* name) const {
@@ -209,89 +229,121 @@ using namespace lwo;
 
 extern "C" lwo_status lwo_block_layout(const lwo_model_desc* desc, lwo_tensor_info* out, int32_t cap,
                                        int32_t* n, uint64_t* extent_bytes) {
-    clear_error();
-    LWO_TRY(validate_desc(desc));
-    Layout L = make_layout(*desc);
-    if (n) *n = (int32_t)L.tensors.size();
-    if (extent_bytes) *extent_bytes = L.extent_bytes;
-    if (!out) return cap == 0 ? LWO_OK : (set_error("out is NULL"), LWO_EINVAL);
-    if (cap < (int32_t)L.tensors.size()) { set_error("cap smaller than the tensor count"); return LWO_EINVAL; }
-    for (size_t i = 0; i < L.tensors.size(); ++i) {
-        const TensorSlot& t = L.tensors[i];
-        lwo_tensor_info& o = out[i];
-        std::memset(&o, 0, sizeof(o));
-        std::strncpy(o.name, t.name.c_str(), sizeof(o.name) - 1);
-        o.offset = t.offset;
-        o.bytes = t.bytes;
-        o.rank = t.rank;
-        o.shape[0] = t.shape[0];
-        o.shape[1] = t.shape[1];
-        o.dtype = t.dtype;
-        o.tiled = t.tiled ? 1 : 0;
+    try {
+        clear_error();
+        LWO_TRY(validate_desc(desc));
+        Layout L = make_layout(*desc);
+        if (n) *n = (int32_t)L.tensors.size();
+        if (extent_bytes) *extent_bytes = L.extent_bytes;
+        if (!out) return cap == 0 ? LWO_OK : (set_error("out is NULL"), LWO_EINVAL);
+        if (cap < (int32_t)L.tensors.size()) { set_error("cap smaller than the tensor count"); return LWO_EINVAL; }
+        for (size_t i = 0; i < L.tensors.size(); ++i) {
+            const TensorSlot& t = L.tensors[i];
+            lwo_tensor_info& o = out[i];
+            std::memset(&o, 0, sizeof(o));
+            std::strncpy(o.name, t.name.c_str(), sizeof(o.name) - 1);
+            o.offset = t.offset;
+            o.bytes = t.bytes;
+            o.rank = t.rank;
+            o.shape[0] = t.shape[0];
+            o.shape[1] = t.shape[1];
+            o.dtype = t.dtype;
+            o.tiled = t.tiled ? 1 : 0;
+        }
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_block_layout");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_block_layout", e.what());
+    } catch (...) {
+        return fail_exception("lwo_block_layout", "unknown exception");
     }
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_pack_block(const lwo_model_desc* desc, const float* const* tensors, int32_t n_tensors,
                                      void* dst, uint64_t dst_bytes) {
-    clear_error();
-    LWO_TRY(validate_desc(desc));
-    Layout L = make_layout(*desc);
-    const bool fp8 = desc->linear_dtype == LWO_FP8_E4M3;
-    const int n_in = (int)L.tensors.size() - (fp8 ? 1 : 0);
-    if (!tensors || n_tensors != n_in) { set_error("pack: expected " + std::to_string(n_in) + " tensors"); return LWO_EINVAL; }
-    if (!dst || dst_bytes < L.extent_bytes) { set_error("pack: destination too small"); return LWO_EINVAL; }
-    for (int i = 0; i < n_in; ++i)
-        if (!tensors[i]) { set_error("pack: tensor " + L.tensors[i].name + " is NULL"); return LWO_EINVAL; }
-    unsigned char* out = (unsigned char*)dst;
-    std::memset(out, 0, L.extent_bytes);
-    float scales[10];
-    int n_scales = 0;
-    std::vector<unsigned char> rowmajor;
-    for (int i = 0; i < n_in; ++i) {
-        const TensorSlot& t = L.tensors[i];
-        const uint64_t n = t.bytes / (uint64_t)dtype_bytes(t.dtype);
-        const float* src = tensors[i];
-        // A tiled tensor is encoded row-major into a scratch buffer, then tiled.
-        if (t.tiled) rowmajor.resize(t.bytes);
-        unsigned char* o = t.tiled ? rowmajor.data() : out + t.offset;
-        if (t.dtype == LWO_F32) {
-            std::memcpy(o, src, t.bytes);
-        } else if (t.dtype == LWO_BF16) {
-            uint16_t* ob = (uint16_t*)o;
-            for (uint64_t j = 0; j < n; ++j) ob[j] = f32_to_bf16_rne(src[j]);
-        } else {
-            float amax = 0.0f;
-            for (uint64_t j = 0; j < n; ++j) amax = std::fmax(amax, std::fabs(src[j]));
-            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-            for (uint64_t j = 0; j < n; ++j) o[j] = f32_to_e4m3_rne_sat(src[j] / s);
-            scales[n_scales++] = s;
+    try {
+        clear_error();
+        LWO_TRY(validate_desc(desc));
+        Layout L = make_layout(*desc);
+        const bool fp8 = desc->linear_dtype == LWO_FP8_E4M3;
+        const int n_in = (int)L.tensors.size() - (fp8 ? 1 : 0);
+        if (!tensors || n_tensors != n_in) { set_error("pack: expected " + std::to_string(n_in) + " tensors"); return LWO_EINVAL; }
+        if (!dst || dst_bytes < L.extent_bytes) { set_error("pack: destination too small"); return LWO_EINVAL; }
+        for (int i = 0; i < n_in; ++i)
+            if (!tensors[i]) { set_error("pack: tensor " + L.tensors[i].name + " is NULL"); return LWO_EINVAL; }
+        unsigned char* out = (unsigned char*)dst;
+        std::memset(out, 0, L.extent_bytes);
+        float scales[10];
+        int n_scales = 0;
+        std::vector<unsigned char> rowmajor;
+        for (int i = 0; i < n_in; ++i) {
+            const TensorSlot& t = L.tensors[i];
+            const uint64_t n = t.bytes / (uint64_t)dtype_bytes(t.dtype);
+            const float* src = tensors[i];
+            // A tiled tensor is encoded row-major into a scratch buffer, then tiled.
+            if (t.tiled) rowmajor.resize(t.bytes);
+            unsigned char* o = t.tiled ? rowmajor.data() : out + t.offset;
+            if (t.dtype == LWO_F32) {
+                std::memcpy(o, src, t.bytes);
+            } else if (t.dtype == LWO_BF16) {
+                uint16_t* ob = (uint16_t*)o;
+                for (uint64_t j = 0; j < n; ++j) ob[j] = f32_to_bf16_rne(src[j]);
+            } else {
+                float amax = 0.0f;
+                for (uint64_t j = 0; j < n; ++j) amax = std::fmax(amax, std::fabs(src[j]));
+                const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+                for (uint64_t j = 0; j < n; ++j) o[j] = f32_to_e4m3_rne_sat(src[j] / s);
+                scales[n_scales++] = s;
+            }
+            if (t.tiled) tile_rows(rowmajor.data(), t.shape[0], (uint64_t)t.shape[1] * dtype_bytes(t.dtype), out + t.offset);
         }
-        if (t.tiled) tile_rows(rowmajor.data(), t.shape[0], (uint64_t)t.shape[1] * dtype_bytes(t.dtype), out + t.offset);
+        if (fp8) {
+            const TensorSlot& t = L.tensors.back();
+            if (n_scales != 10) { set_error("pack: expected ten fp8 weight matrices"); return LWO_EINVAL; }
+            std::memcpy(out + t.offset, scales, sizeof(scales));
+        }
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_pack_block");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_pack_block", e.what());
+    } catch (...) {
+        return fail_exception("lwo_pack_block", "unknown exception");
     }
-    if (fp8) {
-        const TensorSlot& t = L.tensors.back();
-        if (n_scales != 10) { set_error("pack: expected ten fp8 weight matrices"); return LWO_EINVAL; }
-        std::memcpy(out + t.offset, scales, sizeof(scales));
-    }
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_tile_weight(int32_t dtype, const void* src, int32_t N, int32_t K, void* dst) {
-    clear_error();
-    if (dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) { set_error("tile_weight: dtype must be BF16 or FP8_E4M3"); return LWO_EINVAL; }
-    const uint64_t R = (uint64_t)(K > 0 ? K : 0) * (uint64_t)dtype_bytes(dtype);
-    if (N < 1 || K < 1 || N % 64 || R % 64) { set_error("tile_weight: N must be a multiple of 64 and K * element bytes of 64"); return LWO_EINVAL; }
-    if (!src || !dst) { set_error("tile_weight: null pointer"); return LWO_EINVAL; }
-    tile_rows((const unsigned char*)src, N, R, (unsigned char*)dst);
-    return LWO_OK;
+    try {
+        clear_error();
+        if (dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) { set_error("tile_weight: dtype must be BF16 or FP8_E4M3"); return LWO_EINVAL; }
+        const uint64_t R = (uint64_t)(K > 0 ? K : 0) * (uint64_t)dtype_bytes(dtype);
+        if (N < 1 || K < 1 || N % 64 || R % 64) { set_error("tile_weight: N must be a multiple of 64 and K * element bytes of 64"); return LWO_EINVAL; }
+        if (!src || !dst) { set_error("tile_weight: null pointer"); return LWO_EINVAL; }
+        tile_rows((const unsigned char*)src, N, R, (unsigned char*)dst);
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_tile_weight");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_tile_weight", e.what());
+    } catch (...) {
+        return fail_exception("lwo_tile_weight", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_extent_checksum(const void* host, uint64_t bytes, uint64_t* sum) {
-    clear_error();
-    if (!sum || (bytes && !host) || bytes % 8) { set_error("checksum: bad arguments"); return LWO_EINVAL; }
-    *sum = extent_checksum_host(host, bytes);
-    return LWO_OK;
+    try {
+        clear_error();
+        if (!sum || (bytes && !host) || bytes % 8) { set_error("checksum: bad arguments"); return LWO_EINVAL; }
+        *sum = extent_checksum_host(host, bytes);
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_extent_checksum");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_extent_checksum", e.what());
+    } catch (...) {
+        return fail_exception("lwo_extent_checksum", "unknown exception");
+    }
 }
 
 extern "C" const char* lwo_last_error(void) { return g_err.c_str(); }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <exception>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -14,6 +16,8 @@ namespace lwo {
 // ------------------------------------------------------------------ errors
 
 void set_error(const std::string& msg);
+lwo_status fail_alloc(const char* where) noexcept;                     // LWO_ENOMEM
+lwo_status fail_exception(const char* where, const char* what) noexcept;  // LWO_EIO
 void clear_error();
 
 #define LWO_HIP_TRY(expr)                                                              \

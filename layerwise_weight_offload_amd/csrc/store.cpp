@@ -145,55 +145,63 @@ struct lwo_store {
 extern "C" lwo_status lwo_register_ranges(const void* const* ptrs, const uint64_t* bytes, int32_t n, uint64_t page,
                                           uint64_t budget, lwo_register_fn reg, lwo_unregister_fn unreg, void* user,
                                           uint64_t* out_base, uint64_t* out_len, int32_t cap, int32_t* n_out) {
-    clear_error();
-    if (n < 0 || (n && (!ptrs || !bytes)) || !reg || !unreg || page == 0 || (page & (page - 1))) {
-        set_error("register: bad arguments (page must be a power of two)");
-        return LWO_EINVAL;
-    }
-    // page-align every range outward, then coalesce overlapping or adjacent ranges
-    std::vector<std::pair<uint64_t, uint64_t>> r;   // [begin, end)
-    for (int i = 0; i < n; ++i) {
-        if (!bytes[i]) continue;
-        uint64_t b = (uint64_t)(uintptr_t)ptrs[i];
-        uint64_t e = b + bytes[i];
-        r.emplace_back(b & ~(page - 1), (e + page - 1) & ~(page - 1));
-    }
-    std::sort(r.begin(), r.end());
-    std::vector<std::pair<uint64_t, uint64_t>> c;
-    for (auto& x : r) {
-        if (!c.empty() && x.first <= c.back().second) c.back().second = std::max(c.back().second, x.second);
-        else c.push_back(x);
-    }
-    uint64_t total = 0;
-    for (auto& x : c) total += x.second - x.first;
-    if (n_out) *n_out = (int32_t)c.size();
-    if (cap < (int32_t)c.size() || (!c.empty() && (!out_base || !out_len))) {
-        set_error("register: output capacity smaller than the coalesced range count");
-        return LWO_EINVAL;
-    }
-    if (total > budget) {   // checked before any registration call
-        set_error("register: " + std::to_string(total) + " bytes exceed the budget of " + std::to_string(budget));
-        return LWO_EBUDGET;
-    }
-    for (size_t i = 0; i < c.size(); ++i) {
-        if (reg(user, (void*)(uintptr_t)c[i].first, c[i].second - c[i].first) != 0) {
-            bool rb_ok = true;
-            for (size_t j = i; j-- > 0;)
-                if (unreg(user, (void*)(uintptr_t)c[j].first) != 0) rb_ok = false;
-            if (!rb_ok) {
-                set_error("register: range " + std::to_string(i) + " failed and a rollback unregister failed; "
-                          "the ranges that could not be unregistered must stay mapped");
-                return LWO_EROLLBACK;
-            }
-            set_error("register: range " + std::to_string(i) + " failed; all earlier ranges were unregistered");
-            return LWO_EREGISTER;
+    try {
+        clear_error();
+        if (n < 0 || (n && (!ptrs || !bytes)) || !reg || !unreg || page == 0 || (page & (page - 1))) {
+            set_error("register: bad arguments (page must be a power of two)");
+            return LWO_EINVAL;
         }
+        // page-align every range outward, then coalesce overlapping or adjacent ranges
+        std::vector<std::pair<uint64_t, uint64_t>> r;   // [begin, end)
+        for (int i = 0; i < n; ++i) {
+            if (!bytes[i]) continue;
+            uint64_t b = (uint64_t)(uintptr_t)ptrs[i];
+            uint64_t e = b + bytes[i];
+            r.emplace_back(b & ~(page - 1), (e + page - 1) & ~(page - 1));
+        }
+        std::sort(r.begin(), r.end());
+        std::vector<std::pair<uint64_t, uint64_t>> c;
+        for (auto& x : r) {
+            if (!c.empty() && x.first <= c.back().second) c.back().second = std::max(c.back().second, x.second);
+            else c.push_back(x);
+        }
+        uint64_t total = 0;
+        for (auto& x : c) total += x.second - x.first;
+        if (n_out) *n_out = (int32_t)c.size();
+        if (cap < (int32_t)c.size() || (!c.empty() && (!out_base || !out_len))) {
+            set_error("register: output capacity smaller than the coalesced range count");
+            return LWO_EINVAL;
+        }
+        if (total > budget) {   // checked before any registration call
+            set_error("register: " + std::to_string(total) + " bytes exceed the budget of " + std::to_string(budget));
+            return LWO_EBUDGET;
+        }
+        for (size_t i = 0; i < c.size(); ++i) {
+            if (reg(user, (void*)(uintptr_t)c[i].first, c[i].second - c[i].first) != 0) {
+                bool rb_ok = true;
+                for (size_t j = i; j-- > 0;)
+                    if (unreg(user, (void*)(uintptr_t)c[j].first) != 0) rb_ok = false;
+                if (!rb_ok) {
+                    set_error("register: range " + std::to_string(i) + " failed and a rollback unregister failed; "
+                              "the ranges that could not be unregistered must stay mapped");
+                    return LWO_EROLLBACK;
+                }
+                set_error("register: range " + std::to_string(i) + " failed; all earlier ranges were unregistered");
+                return LWO_EREGISTER;
+            }
+        }
+        for (size_t i = 0; i < c.size(); ++i) {
+            out_base[i] = c[i].first;
+            out_len[i] = c[i].second - c[i].first;
+        }
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_register_ranges");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_register_ranges", e.what());
+    } catch (...) {
+        return fail_exception("lwo_register_ranges", "unknown exception");
     }
-    for (size_t i = 0; i < c.size(); ++i) {
-        out_base[i] = c[i].first;
-        out_len[i] = c[i].second - c[i].first;
-    }
-    return LWO_OK;
 }
 
 static int32_t hip_register_cb(void*, void* base, uint64_t bytes) {
@@ -468,63 +476,95 @@ static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, cons
 
 extern "C" lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t host_mode,
                                             uint64_t register_budget, int32_t device, lwo_store** out) {
-    clear_error();
-    if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
-    *out = nullptr;
-    LWO_TRY(validate_desc(desc));
-    std::vector<int32_t> bt(desc->n_blocks, 0);
-    return build_store(desc, 1, bt.data(), desc->n_blocks, src, host_mode, register_budget, device, out);
+    try {
+        clear_error();
+        if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
+        *out = nullptr;
+        LWO_TRY(validate_desc(desc));
+        std::vector<int32_t> bt(desc->n_blocks, 0);
+        return build_store(desc, 1, bt.data(), desc->n_blocks, src, host_mode, register_budget, device, out);
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_build_block_store");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_build_block_store", e.what());
+    } catch (...) {
+        return fail_exception("lwo_build_block_store", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_build_mixed_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type,
                                             int32_t n_blocks, const lwo_block_source* src, int32_t host_mode,
                                             uint64_t register_budget, int32_t device, lwo_store** out) {
-    clear_error();
-    return build_store(types, n_types, block_type, n_blocks, src, host_mode, register_budget, device, out);
+    try {
+        clear_error();
+        return build_store(types, n_types, block_type, n_blocks, src, host_mode, register_budget, device, out);
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_build_mixed_store");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_build_mixed_store", e.what());
+    } catch (...) {
+        return fail_exception("lwo_build_mixed_store", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_destroy_block_store(lwo_store* s) {
-    clear_error();
-    release(s);
-    return LWO_OK;
+    try {
+        clear_error();
+        release(s);
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_destroy_block_store");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_destroy_block_store", e.what());
+    } catch (...) {
+        return fail_exception("lwo_destroy_block_store", "unknown exception");
+    }
 }
 
 // ------------------------------------------------------------------ resident prefix
 
 extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    if (k < 0 || k > s->d.n_blocks) { set_error("resident prefix out of range"); return LWO_EINVAL; }
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
-    LWO_HIP_TRY(hipDeviceSynchronize());
-    char* region = nullptr;
-    if (k > 0) {
-        const uint64_t bytes = s->roff[k - 1] + s->bext[k - 1];
-        if (hipMalloc(&region, bytes) != hipSuccess) {
-            set_error("hipMalloc of the resident region (" + std::to_string(bytes) + " bytes) failed");
-            return LWO_ENOMEM;   // previous prefix stays in effect
-        }
-        for (int b = 0; b < k; ++b) {
-            if (h2d_block(s, region + s->roff[b], b) != LWO_OK) {
-                (void)hipStreamSynchronize(s->copy);
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        if (k < 0 || k > s->d.n_blocks) { set_error("resident prefix out of range"); return LWO_EINVAL; }
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        LWO_HIP_TRY(hipDeviceSynchronize());
+        char* region = nullptr;
+        if (k > 0) {
+            const uint64_t bytes = s->roff[k - 1] + s->bext[k - 1];
+            if (hipMalloc(&region, bytes) != hipSuccess) {
+                set_error("hipMalloc of the resident region (" + std::to_string(bytes) + " bytes) failed");
+                return LWO_ENOMEM;   // previous prefix stays in effect
+            }
+            for (int b = 0; b < k; ++b) {
+                if (h2d_block(s, region + s->roff[b], b) != LWO_OK) {
+                    (void)hipStreamSynchronize(s->copy);
+                    (void)hipFree(region);
+                    set_error("copy of resident block " + std::to_string(b) + " failed");
+                    return LWO_EHIP;
+                }
+            }
+            if (hipStreamSynchronize(s->copy) != hipSuccess) {
                 (void)hipFree(region);
-                set_error("copy of resident block " + std::to_string(b) + " failed");
+                set_error("copy of the resident prefix failed");
                 return LWO_EHIP;
             }
         }
-        if (hipStreamSynchronize(s->copy) != hipSuccess) {
-            (void)hipFree(region);
-            set_error("copy of the resident prefix failed");
-            return LWO_EHIP;
-        }
+        if (s->resident) (void)hipFree(s->resident);
+        s->resident = region;
+        s->k = k;
+        LWO_TRY(prime_head(s));
+        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_set_resident_prefix");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_set_resident_prefix", e.what());
+    } catch (...) {
+        return fail_exception("lwo_set_resident_prefix", "unknown exception");
     }
-    if (s->resident) (void)hipFree(s->resident);
-    s->resident = region;
-    s->k = k;
-    LWO_TRY(prime_head(s));
-    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
-    return LWO_OK;
 }
 
 // ------------------------------------------------------------------ the step
@@ -592,150 +632,222 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
 }
 
 extern "C" lwo_status lwo_run_denoise_step(lwo_store* s, void* x, const void* cond, const void* ctx, void* hip_stream) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    if (!hip_stream) { set_error("run needs a non-null stream (the legacy null stream would serialise with the copy stream)"); return LWO_EINVAL; }
-    if (!x || !cond) { set_error("x and cond are required"); return LWO_EINVAL; }
-    if (s->d.kind == LWO_KIND_VIDEO && !ctx) { set_error("video kind needs ctx"); return LWO_EINVAL; }
-    if (s->d.kind == LWO_KIND_DIT && ctx) { set_error("DiT kind takes no ctx"); return LWO_EINVAL; }
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    if (s->max_inflight > 0 && s->steps >= (uint64_t)s->max_inflight)   // pacing: bound host run-ahead
-        LWO_HIP_TRY(hipEventSynchronize(s->step_done[(s->steps - s->max_inflight) % 16]));
-    lwo_status st = run_step(s, x, cond, ctx, (hipStream_t)hip_stream);
-    if (st != LWO_OK) s->dead = true;   // the ring's events no longer describe the slots
-    return st;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        if (!hip_stream) { set_error("run needs a non-null stream (the legacy null stream would serialise with the copy stream)"); return LWO_EINVAL; }
+        if (!x || !cond) { set_error("x and cond are required"); return LWO_EINVAL; }
+        if (s->d.kind == LWO_KIND_VIDEO && !ctx) { set_error("video kind needs ctx"); return LWO_EINVAL; }
+        if (s->d.kind == LWO_KIND_DIT && ctx) { set_error("DiT kind takes no ctx"); return LWO_EINVAL; }
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        if (s->max_inflight > 0 && s->steps >= (uint64_t)s->max_inflight)   // pacing: bound host run-ahead
+            LWO_HIP_TRY(hipEventSynchronize(s->step_done[(s->steps - s->max_inflight) % 16]));
+        lwo_status st = run_step(s, x, cond, ctx, (hipStream_t)hip_stream);
+        if (st != LWO_OK) s->dead = true;   // the ring's events no longer describe the slots
+        return st;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_run_denoise_step");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_run_denoise_step", e.what());
+    } catch (...) {
+        return fail_exception("lwo_run_denoise_step", "unknown exception");
+    }
 }
 
 // ------------------------------------------------------------------ validation and stats
 
 extern "C" lwo_status lwo_set_max_inflight(lwo_store* s, int32_t max_inflight) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    if (max_inflight < 0 || max_inflight > 16) { set_error("max_inflight must be 0..16"); return LWO_EINVAL; }
-    s->max_inflight = max_inflight;
-    return LWO_OK;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        if (max_inflight < 0 || max_inflight > 16) { set_error("max_inflight must be 0..16"); return LWO_EINVAL; }
+        s->max_inflight = max_inflight;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_set_max_inflight");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_set_max_inflight", e.what());
+    } catch (...) {
+        return fail_exception("lwo_set_max_inflight", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_set_validation(lwo_store* s, int32_t on) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    if (on) compute_host_sums(s);
-    s->validation = on != 0;
-    return LWO_OK;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        if (on) compute_host_sums(s);
+        s->validation = on != 0;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_set_validation");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_set_validation", e.what());
+    } catch (...) {
+        return fail_exception("lwo_set_validation", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_set_copy_timing(lwo_store* s, int32_t on) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    s->timing = on != 0;
-    return LWO_OK;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        s->timing = on != 0;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_set_copy_timing");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_set_copy_timing", e.what());
+    } catch (...) {
+        return fail_exception("lwo_set_copy_timing", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_copy_times(lwo_store* s, float* ms, int32_t cap, int32_t* n) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
-    int cnt = s->n_timed;
-    if (n) *n = cnt;
-    for (int i = 0; i < cnt && i < cap && ms; ++i)
-        LWO_HIP_TRY(hipEventElapsedTime(&ms[i], s->tev[2 * i], s->tev[2 * i + 1]));
-    return LWO_OK;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        int cnt = s->n_timed;
+        if (n) *n = cnt;
+        for (int i = 0; i < cnt && i < cap && ms; ++i)
+            LWO_HIP_TRY(hipEventElapsedTime(&ms[i], s->tev[2 * i], s->tev[2 * i + 1]));
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_copy_times");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_copy_times", e.what());
+    } catch (...) {
+        return fail_exception("lwo_copy_times", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* host_sum, uint64_t* slot_sum) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    if (block < 0 || block >= s->d.n_blocks || !host_sum || !slot_sum) { set_error("bad block or output"); return LWO_EINVAL; }
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_HIP_TRY(hipDeviceSynchronize());
-    compute_host_sums(s);
-    const uint64_t ext = s->bext[block];
-    const char* base = nullptr;
-    if (block < s->k) {
-        base = s->resident + s->roff[block];
-    } else if (s->slot_block[0] == block || s->slot_block[1] == block) {
-        base = s->slot[s->slot_block[0] == block ? 0 : 1];
-    } else {
-        // borrow the slot the ring is not about to read
-        int sl = 1 - s->head_slot;
-        LWO_TRY(h2d_block(s, s->slot[sl], block));
-        LWO_HIP_TRY(hipEventRecord(s->copy_done[sl], s->copy));
-        s->slot_block[sl] = block;
-        base = s->slot[sl];
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        if (block < 0 || block >= s->d.n_blocks || !host_sum || !slot_sum) { set_error("bad block or output"); return LWO_EINVAL; }
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_HIP_TRY(hipDeviceSynchronize());
+        compute_host_sums(s);
+        const uint64_t ext = s->bext[block];
+        const char* base = nullptr;
+        if (block < s->k) {
+            base = s->resident + s->roff[block];
+        } else if (s->slot_block[0] == block || s->slot_block[1] == block) {
+            base = s->slot[s->slot_block[0] == block ? 0 : 1];
+        } else {
+            // borrow the slot the ring is not about to read
+            int sl = 1 - s->head_slot;
+            LWO_TRY(h2d_block(s, s->slot[sl], block));
+            LWO_HIP_TRY(hipEventRecord(s->copy_done[sl], s->copy));
+            s->slot_block[sl] = block;
+            base = s->slot[sl];
+        }
+        LWO_TRY(enqueue_zero_u64(s->ws.sums, 1, s->copy));
+        LWO_TRY(enqueue_checksum(base, ext, s->ws.sums, s->copy));
+        uint64_t got = 0;
+        LWO_HIP_TRY(hipMemcpyAsync(&got, s->ws.sums, 8, hipMemcpyDeviceToHost, s->copy));
+        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        *host_sum = s->host_sums[block];
+        *slot_sum = got;
+        if (got != s->host_sums[block]) { set_error("slot checksum differs from the host extent"); return LWO_ECHECKSUM; }
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_block_checksum");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_block_checksum", e.what());
+    } catch (...) {
+        return fail_exception("lwo_block_checksum", "unknown exception");
     }
-    LWO_TRY(enqueue_zero_u64(s->ws.sums, 1, s->copy));
-    LWO_TRY(enqueue_checksum(base, ext, s->ws.sums, s->copy));
-    uint64_t got = 0;
-    LWO_HIP_TRY(hipMemcpyAsync(&got, s->ws.sums, 8, hipMemcpyDeviceToHost, s->copy));
-    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
-    *host_sum = s->host_sums[block];
-    *slot_sum = got;
-    if (got != s->host_sums[block]) { set_error("slot checksum differs from the host extent"); return LWO_ECHECKSUM; }
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_set_kernel_timing(lwo_store* s, int32_t on) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_HIP_TRY(hipDeviceSynchronize());
-    s->kt.reset();
-    s->kt.on = on != 0;
-    return LWO_OK;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_HIP_TRY(hipDeviceSynchronize());
+        s->kt.reset();
+        s->kt.on = on != 0;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_set_kernel_timing");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_set_kernel_timing", e.what());
+    } catch (...) {
+        return fail_exception("lwo_set_kernel_timing", "unknown exception");
+    }
 }
 
 extern "C" lwo_status lwo_kernel_stats(lwo_store* s, lwo_kernel_stat* out, int32_t cap, int32_t* n) {
-    clear_error();
-    LWO_TRY(check_store(s));
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_TRY(s->kt.collect());
-    const int cnt = (int)s->kt.agg.size();
-    if (n) *n = cnt;
-    if (!out && cap == 0) return LWO_OK;   // count query
-    if (cnt > cap || !out) { set_error("kernel_stats: capacity too small"); return LWO_EINVAL; }
-    for (int i = 0; i < cnt; ++i) {
-        const KernelTimer::Agg& a = s->kt.agg[i];
-        std::memset(&out[i], 0, sizeof(out[i]));
-        std::strncpy(out[i].name, a.name.c_str(), sizeof(out[i].name) - 1);
-        out[i].launches = a.launches;
-        out[i].total_ms = a.ms;
-        out[i].flops = a.flops;
-        out[i].bytes = a.bytes;
+    try {
+        clear_error();
+        LWO_TRY(check_store(s));
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_TRY(s->kt.collect());
+        const int cnt = (int)s->kt.agg.size();
+        if (n) *n = cnt;
+        if (!out && cap == 0) return LWO_OK;   // count query
+        if (cnt > cap || !out) { set_error("kernel_stats: capacity too small"); return LWO_EINVAL; }
+        for (int i = 0; i < cnt; ++i) {
+            const KernelTimer::Agg& a = s->kt.agg[i];
+            std::memset(&out[i], 0, sizeof(out[i]));
+            std::strncpy(out[i].name, a.name.c_str(), sizeof(out[i].name) - 1);
+            out[i].launches = a.launches;
+            out[i].total_ms = a.ms;
+            out[i].flops = a.flops;
+            out[i].bytes = a.bytes;
+        }
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_kernel_stats");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_kernel_stats", e.what());
+    } catch (...) {
+        return fail_exception("lwo_kernel_stats", "unknown exception");
     }
-    return LWO_OK;
 }
 
 extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
-    clear_error();
-    if (!s || !o) { set_error("NULL argument"); return LWO_EINVAL; }
-    LWO_HIP_TRY(hipSetDevice(s->device));
-    LWO_HIP_TRY(hipDeviceSynchronize());
-    std::memset(o, 0, sizeof(*o));
-    const uint64_t ext = s->max_ext;
-    uint64_t all = 0;
-    for (uint64_t e : s->bext) all += e;
-    o->extent_bytes = ext;
-    o->slot_bytes = ext;
-    o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->bext[s->k - 1] : 0);
-    o->workspace_bytes = s->ws.bytes;
-    o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : all;
-    o->staging_bytes = s->host_mode == LWO_HOST_STAGED ? 2 * ext : 0;
-    o->pack_bytes = s->pack_bytes;
-    o->pack_ms = s->pack_ms;
-    o->pack_threads = s->host_mode == LWO_HOST_STAGED ? s->pack_threads + 1 : 0;
-    o->h2d_copies = s->h2d_copies;
-    o->h2d_bytes = s->h2d_bytes;
-    o->steps = s->steps;
-    uint64_t mism = 0;
-    if (s->ws.sums) LWO_HIP_TRY(hipMemcpy(&mism, s->ws.sums + 1, 8, hipMemcpyDeviceToHost));
-    o->checksum_mismatches = mism;
-    o->registered_ranges = s->reg_base.size();
-    for (uint64_t l : s->reg_len) o->registered_bytes += l;
-    o->resident_prefix = s->k;
-    o->head_slot = s->head_slot;
-    o->host_mode = s->host_mode;
-    o->validation = s->validation;
-    o->build_ms = s->build_ms;
-    return LWO_OK;
+    try {
+        clear_error();
+        if (!s || !o) { set_error("NULL argument"); return LWO_EINVAL; }
+        LWO_HIP_TRY(hipSetDevice(s->device));
+        LWO_HIP_TRY(hipDeviceSynchronize());
+        std::memset(o, 0, sizeof(*o));
+        const uint64_t ext = s->max_ext;
+        uint64_t all = 0;
+        for (uint64_t e : s->bext) all += e;
+        o->extent_bytes = ext;
+        o->slot_bytes = ext;
+        o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->bext[s->k - 1] : 0);
+        o->workspace_bytes = s->ws.bytes;
+        o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : all;
+        o->staging_bytes = s->host_mode == LWO_HOST_STAGED ? 2 * ext : 0;
+        o->pack_bytes = s->pack_bytes;
+        o->pack_ms = s->pack_ms;
+        o->pack_threads = s->host_mode == LWO_HOST_STAGED ? s->pack_threads + 1 : 0;
+        o->h2d_copies = s->h2d_copies;
+        o->h2d_bytes = s->h2d_bytes;
+        o->steps = s->steps;
+        uint64_t mism = 0;
+        if (s->ws.sums) LWO_HIP_TRY(hipMemcpy(&mism, s->ws.sums + 1, 8, hipMemcpyDeviceToHost));
+        o->checksum_mismatches = mism;
+        o->registered_ranges = s->reg_base.size();
+        for (uint64_t l : s->reg_len) o->registered_bytes += l;
+        o->resident_prefix = s->k;
+        o->head_slot = s->head_slot;
+        o->host_mode = s->host_mode;
+        o->validation = s->validation;
+        o->build_ms = s->build_ms;
+        return LWO_OK;
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_get_stats");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_get_stats", e.what());
+    } catch (...) {
+        return fail_exception("lwo_get_stats", "unknown exception");
+    }
 }
