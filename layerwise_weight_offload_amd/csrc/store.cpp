@@ -445,26 +445,37 @@ static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, cons
     auto t0 = std::chrono::steady_clock::now();
     lwo_store* s = new (std::nothrow) lwo_store();
     if (!s) { set_error("out of host memory"); return LWO_ENOMEM; }
-    s->tdesc = td;
-    for (const lwo_model_desc& t : td) s->tlay.push_back(make_layout(t));
-    s->btype.assign(block_type, block_type + n_blocks);
-    s->d = td[0];
-    for (const lwo_model_desc& t : td) {
-        s->d.ffn = std::max(s->d.ffn, t.ffn);
-        if (t.linear_dtype == LWO_FP8_E4M3) s->d.linear_dtype = LWO_FP8_E4M3;
+    // An exception part-way (host memory) must not leak the partial store either.
+    lwo_status st = LWO_OK;
+    try {
+        s->tdesc = td;
+        for (const lwo_model_desc& t : td) s->tlay.push_back(make_layout(t));
+        s->btype.assign(block_type, block_type + n_blocks);
+        s->d = td[0];
+        for (const lwo_model_desc& t : td) {
+            s->d.ffn = std::max(s->d.ffn, t.ffn);
+            if (t.linear_dtype == LWO_FP8_E4M3) s->d.linear_dtype = LWO_FP8_E4M3;
+        }
+        uint64_t off = 0;
+        for (int b = 0; b < n_blocks; ++b) {
+            s->bext.push_back(s->tlay[block_type[b]].extent_bytes);
+            s->roff.push_back(off);
+            off += s->bext[b];
+            s->max_ext = std::max(s->max_ext, s->bext[b]);
+        }
+        s->device = device;
+        s->host_mode = host_mode;
+        st = build(s, src, host_mode, register_budget);
+    } catch (...) {
+        release(s);
+        throw;
     }
-    uint64_t off = 0;
-    for (int b = 0; b < n_blocks; ++b) {
-        s->bext.push_back(s->tlay[block_type[b]].extent_bytes);
-        s->roff.push_back(off);
-        off += s->bext[b];
-        s->max_ext = std::max(s->max_ext, s->bext[b]);
-    }
-    s->device = device;
-    s->host_mode = host_mode;
-    lwo_status st = build(s, src, host_mode, register_budget);
     if (st != LWO_OK) {
-        std::string msg = lwo_last_error();
+        std::string msg;
+        try {
+            msg = lwo_last_error();
+        } catch (...) {
+        }
         release(s);   // fail closed: nothing of the partial build survives
         set_error(msg);
         return st;
