@@ -110,10 +110,11 @@ def block_flops(w) -> float:
     return gemm + attn
 
 
-def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12):
+def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12, type_of=None):
     """The oracle (float64, every weight resident) on a bounded sample: whole
     blocks of the step while the time budget lasts; for a block above
-    max_block_flops, one block at fewer tokens, scaled by the FLOP ratio."""
+    max_block_flops, one block at fewer tokens, scaled by the FLOP ratio.
+    type_of(b): block b's workload in a mixed stack (w gives the inputs)."""
     import numpy as np
     import lwo_synth
     from oracle import dit as o_dit
@@ -136,9 +137,10 @@ def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12):
     x, cond, ctx = o_dit.decode_inputs(w_run, *lwo_synth.step_inputs(w_run))
     done, spent = 0, 0.0
     while done < w.n_blocks and (done == 0 or (spent < seconds and scale == 1.0)):
-        ext = o_layout.pack_block(w_run, lwo_synth.block_tensors(w_run, done))   # packing is not timed
+        wb = w_run if type_of is None else type_of(done)
+        ext = o_layout.pack_block(wb, lwo_synth.block_tensors(wb, done))   # packing is not timed
         t0 = time.perf_counter()
-        x = o_dit.stack_forward(w_run, [ext], x, cond, ctx, blocks=[0])
+        x = o_dit.stack_forward(wb, [ext], x, cond, ctx, blocks=[0])
         spent += time.perf_counter() - t0
         done += 1
         log(f"oracle block {done}: {spent:.1f} s so far")
@@ -207,19 +209,36 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         return copy_calibration(torch)
-    w = lwo_synth.get(args.workload)
-    k = w.resident_prefix if args.resident_prefix is None else args.resident_prefix
-    L = w.n_blocks
-    desc = lwo.ModelDesc.from_workload(w)
-    _, ext = lwo.block_layout(desc)
+    mixed = lwo_synth.MIXED.get(args.workload)
+    if mixed is not None:   # a stack of several block types (extents of different sizes)
+        if args.host_mode != "pin_copy":
+            print("bench.py: mixed stacks are measured in pin_copy mode", file=sys.stderr)
+            return 2
+        w = mixed.inputs
+        L = mixed.n_blocks
+        k = 0 if args.resident_prefix is None else args.resident_prefix
+        tdescs = [lwo.ModelDesc.from_workload(t.with_(n_blocks=L)) for t in mixed.types]
+        text = [lwo.block_layout(d)[1] for d in tdescs]
+        desc_of = lambda b: tdescs[mixed.block_type[b]]
+        ext_of = [text[t] for t in mixed.block_type]
+        type_of = mixed.type_of
+    else:
+        w = lwo_synth.get(args.workload)
+        k = w.resident_prefix if args.resident_prefix is None else args.resident_prefix
+        L = w.n_blocks
+        desc = lwo.ModelDesc.from_workload(w)
+        desc_of = lambda b: desc
+        ext_of = [lwo.block_layout(desc)[1]] * L
+        type_of = None
+    ext = max(ext_of)
 
     # ---- build the store from the seeded generator (drawn ahead on host threads)
-    blocks = lwo_synth.iter_blocks(w)
+    blocks = lwo_synth.iter_blocks(mixed if mixed is not None else w)
 
     def fill(b, dst, n):
         bb, t = next(blocks)
         assert bb == b
-        lwo.pack_block(desc, t, dst=dst, dst_bytes=n)
+        lwo.pack_block(desc_of(b), t, dst=dst, dst_bytes=n)
         if b % 8 == 7 or b == L - 1:
             log(f"packed block {b + 1}/{L}")
 
@@ -240,9 +259,12 @@ def main() -> int:
             log(f"flat-block file {key[:12]}... ({'published' if created else 'joined'}) and verified mapping in "
                 f"{time.perf_counter() - t1:.1f} s")
         store = lwo.build_block_store(desc, extents=pageable, host_mode=lwo.HOST_STAGED)
+    elif mixed is not None:
+        store = lwo.build_mixed_store(tdescs, mixed.block_type, fill=fill)
     else:
         store = lwo.build_block_store(desc, fill=fill)
-    log(f"built {L} x {ext / 1e6:.2f} MB extents ({args.host_mode}) in {time.perf_counter() - t0:.1f} s")
+    log(f"built {L} extents of {', '.join(f'{e / 1e6:.2f}' for e in sorted(set(ext_of)))} MB ({args.host_mode}) "
+        f"in {time.perf_counter() - t0:.1f} s")
 
     dt = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     xs, cs, cxs = lwo_synth.step_inputs(w)
@@ -302,13 +324,15 @@ def main() -> int:
 
     m = L - k
     copies_per_step = m if m >= 3 else 0
-    bytes_per_step = copies_per_step * ext
+    bytes_per_step = sum(ext_of[k:]) if copies_per_step else 0
     h2d_gbps = bytes_per_step / (t_str * 1e-3) / 1e9 if bytes_per_step else 0.0
     t_copy = bytes_per_step / (peak_block * 1e9) * 1e3 if bytes_per_step else 0.0
     overlap = None
     if t_copy > 0:
         overlap = max(0.0, min(1.0, (t_res + t_copy - t_str) / min(t_res, t_copy)))
-    per_copy = [ext / (c * 1e-3) / 1e9 for c in copy_ms if c > 0]
+    # A step copies blocks k+1 .. L-1, then block k for the next step.
+    copy_order = list(range(k + 1, L)) + [k]
+    per_copy = [ext_of[copy_order[i % len(copy_order)]] / (c * 1e-3) / 1e9 for i, c in enumerate(copy_ms) if c > 0]
 
     steps_timed = args.steps
     flops_step = sum(kk["flops"] for kk in kstats) / steps_timed
@@ -329,7 +353,7 @@ def main() -> int:
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof.update({"kernel": dom["name"], "avg_launch_ms": round(avg_ms, 4), "launches_per_step": dom["launches"] // steps_timed,
                  "algorithmic_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
-                 "traffic": committed_traffic(dom["name"], w.name)})
+                 "traffic": committed_traffic(dom["name"], args.workload)})
 
     kernels = {kk["name"]: {"ms_per_step": round(kk["total_ms"] / steps_timed, 4),
                             "launches_per_step": kk["launches"] // steps_timed,
@@ -340,14 +364,16 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         store.destroy()   # release pinned host memory before the oracle allocates
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, type_of=type_of)
 
     out = {
         "metric": METRIC, "value": round(t_str, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t_str, 3), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8+bf16"}[w.linear_dtype],
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8+bf16"}[
+            "fp8" if mixed is not None and any(t.linear_dtype == "fp8" for t in mixed.types) else w.linear_dtype],
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs)",
-        "config": {"workload": w.name, "kind": w.kind, "blocks": L, "hidden": w.hidden, "heads": w.heads,
+        "config": {"workload": args.workload, "kind": w.kind, "blocks": L, "hidden": w.hidden, "heads": w.heads,
                    "ffn": w.ffn, "batch": w.batch, "tokens": w.tokens, "ctx_tokens": w.ctx_tokens,
                    "act_dtype": w.act_dtype, "linear_dtype": w.linear_dtype, "resident_prefix": k,
                    "streamed_blocks": m, "host_mode": args.host_mode + ("+file" if args.cache_dir else ""),
@@ -372,6 +398,10 @@ def main() -> int:
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    if mixed is not None:
+        out["config"]["types"] = [{"heads": t.heads, "ffn": t.ffn, "linear_dtype": t.linear_dtype, "extent_bytes": e}
+                                  for t, e in zip(mixed.types, text)]
+        out["config"]["block_type"] = list(mixed.block_type)
     line = json.dumps(out)
     print(line, flush=True)
     if args.json_out:

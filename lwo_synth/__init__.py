@@ -144,6 +144,11 @@ _mix("video_mixed_fp8", [Workload("video_mixed_fp8.a", KIND_VIDEO, 1, 256, 2, 10
                          Workload("video_mixed_fp8.b", KIND_VIDEO, 1, 256, 2, 512, 1, 300, 40, "bf16", "fp8", 403,
                                   gamma_jitter=True)],
      [0, 1, 0, 1])
+# the 40-block video stack at 256 tokens with bf16 and fp8 linears alternating (extents of 702.7 and 351.5 MB)
+_mix("video14b_t256_mixed",
+     [Workload("video14b_t256_mixed.a", KIND_VIDEO, 1, 5120, 40, 13824, 1, 256, 512, "bf16", "bf16", 103),
+      Workload("video14b_t256_mixed.b", KIND_VIDEO, 1, 5120, 40, 13824, 1, 256, 512, "bf16", "fp8", 103)],
+     [0, 1] * 20)
 
 
 def get_mixed(name: str) -> MixedStack:
@@ -197,19 +202,21 @@ def block_tensors(w: Workload, b: int) -> list[np.ndarray]:
     return out
 
 
-def iter_blocks(w: Workload, threads: int | None = None):
-    """Yield (b, tensors) for every block, drawing ahead on a thread pool
-    (numpy's generators release the GIL while filling large arrays)."""
+def iter_blocks(w, threads: int | None = None):
+    """Yield (b, tensors) for every block of a Workload or a MixedStack (block
+    b drawn with its own type), drawing ahead on a thread pool (numpy's
+    generators release the GIL while filling large arrays)."""
     threads = threads or min(16, os.cpu_count() or 1)
     ahead = max(1, min(threads, 4))
+    type_of = w.type_of if isinstance(w, MixedStack) else (lambda b: w)
     with _fut.ThreadPoolExecutor(max_workers=threads) as ex:
         futs = {}
         for b in range(min(ahead, w.n_blocks)):
-            futs[b] = ex.submit(block_tensors, w, b)
+            futs[b] = ex.submit(block_tensors, type_of(b), b)
         for b in range(w.n_blocks):
             nb = b + ahead
             if nb < w.n_blocks:
-                futs[nb] = ex.submit(block_tensors, w, nb)
+                futs[nb] = ex.submit(block_tensors, type_of(nb), nb)
             yield b, futs.pop(b).result()
 
 
