@@ -93,3 +93,22 @@ def test_committed_traffic_record_is_well_formed():
     b = _bench()
     got = b.committed_traffic("gemm_bf16_gated", "dit_xl_bf16")
     assert got is None or (isinstance(got, int) and got > 37306368)
+
+
+def test_cpu_baseline_runs_each_block_with_its_own_type():
+    """The mixed-stack baseline decodes and runs block b with its own type: on
+    a small fp32 stack it matches the oracle's mixed stack over all blocks."""
+    import numpy as np
+    from oracle import dit as o_dit
+    from oracle import layout as o_layout
+    b = _bench()
+    m = lwo_synth.get_mixed("dit_mixed_fp32")
+    r = b.cpu_baseline(m.inputs, 1e9, type_of=m.type_of)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["sample"].startswith(f"{m.n_blocks} of {m.n_blocks} blocks")
+    # the same per-block decode, checked against the oracle's mixed stack
+    x, cond, ctx = o_dit.decode_inputs(m.inputs, *lwo_synth.step_inputs(m.inputs))
+    ext = [o_layout.pack_block(m.type_of(i), lwo_synth.block_tensors(m.type_of(i), i)) for i in range(m.n_blocks)]
+    y = x
+    for i in range(m.n_blocks):
+        y = o_dit.stack_forward(m.type_of(i), [ext[i]], y, cond, ctx, blocks=[0])
+    assert np.array_equal(y, o_dit.stack_forward_mixed(m, ext, x, cond, ctx))
