@@ -175,6 +175,37 @@ def video_block(x: np.ndarray, cond: np.ndarray, ctx: np.ndarray, p: dict, heads
     return x
 
 
+def video_block_rows(x: np.ndarray, cond: np.ndarray, ctx: np.ndarray, p: dict, heads: int,
+                     rows, fp8_act: bool = False) -> np.ndarray:
+    """video_block's output at token indices ``rows`` only (every batch),
+    [B, len(rows), D].  Self-attention's keys and values need every token;
+    every other step of the block (the per-row fp8 quantisation included)
+    acts on each token's row alone, so it is taken on the selected rows.  The
+    steps and their order are video_block's."""
+    B, T, D = x.shape
+    rows = np.asarray(rows)
+    qa = (lambda z, stored_bf16=False: fp8_activation(z, stored_bf16)) if fp8_act else (lambda z, stored_bf16=False: z)
+    m = cond + p["mod.table"][None, :, :]
+    sh1, sc1, g1, sh2, sc2, g2 = chunks6(m)
+    h = qa(layer_norm(x) * (1.0 + sc1) + sh1)                  # every token: keys and values
+    bq, bk, bv = p["attn.qkv.b"][:D], p["attn.qkv.b"][D:2 * D], p["attn.qkv.b"][2 * D:]
+    k = rms_norm(linear(h, p["attn.k.w"], bk), p["attn.k.norm"])
+    v = linear(h, p["attn.v.w"], bv)
+    xr = x[:, rows]
+    q = rms_norm(linear(h[:, rows], p["attn.q.w"], bq), p["attn.q.norm"])
+    del h
+    xr = xr + g1 * linear(qa(attention(q, k, v, heads), True), p["attn.o.w"], p["attn.o.b"])
+    cq = linear(qa(layer_norm(xr)), p["cross.q.w"], p["cross.q.b"])
+    bck, bcv = p["cross.kv.b"][:D], p["cross.kv.b"][D:]
+    ctx_in = qa(ctx, True)
+    ck = linear(ctx_in, p["cross.k.w"], bck)
+    cv = linear(ctx_in, p["cross.v.w"], bcv)
+    xr = xr + linear(qa(attention(cq, ck, cv, heads), True), p["cross.o.w"], p["cross.o.b"])
+    hr = qa(layer_norm(xr) * (1.0 + sc2) + sh2)
+    return xr + g2 * linear(qa(gelu_tanh(linear(hr, p["ffn.fc1.w"], p["ffn.fc1.b"])), True), p["ffn.fc2.w"],
+                            p["ffn.fc2.b"])
+
+
 def block_forward(w, x, cond, ctx, params: dict, fp8_act: bool = False) -> np.ndarray:
     if w.kind == "dit":
         return dit_block(x, cond, params, w.heads)

@@ -127,6 +127,20 @@ def test_dit_zero_gate_identity():
     assert np.array_equal(dit.dit_block(x, c, p, w.heads), x)
 
 
+def test_video_block_rows_equal_the_full_block():
+    """The sampled-row video block (keys and values over every token, every
+    other step on the chosen rows) gives the full block's rows, in any row
+    order and with repeats, for both batches."""
+    w = _small("video")
+    p = _params(w)
+    x, c, ctx = _inputs(w)
+    for fp8_act in (False, True):
+        full = dit.video_block(x, c, ctx, p, w.heads, fp8_act=fp8_act)
+        for rows in ([0], [8, 0, 3], [2, 2, 7], list(range(w.tokens))):
+            got = dit.video_block_rows(x, c, ctx, p, w.heads, rows, fp8_act=fp8_act)
+            np.testing.assert_allclose(got, full[:, rows], rtol=1e-12, atol=1e-12)
+
+
 def test_video_zero_gate_identity():
     w = _small("video")
     p = _params(w)
