@@ -69,8 +69,10 @@ __global__ void k_silu(const T* __restrict__ in, float* __restrict__ out, int n)
 
 // A GEMV over the [6D, D] weight, bound by reading it once: 16 lanes own one
 // row, a workgroup owns 16 rows.  K goes in windows of 16 16-byte loads per
-// lane; each window's loads are issued before SiLU(cond) of the window (computed
-// once per step) is staged into LDS (for up to four batches), so the two overlap.
+// lane.  Each thread first loads its share of the window's SiLU(cond)
+// (computed once per step, up to four batches) into registers, then issues
+// the weight loads, then stages the SiLU values into LDS: both sets of loads
+// are in flight together, so the window costs one memory round trip.
 template <typename T>
 __global__ __launch_bounds__(256) void k_mod_dit(const float* __restrict__ sc_in, const T* __restrict__ w,
                                                  const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
@@ -83,16 +85,26 @@ __global__ __launch_bounds__(256) void k_mod_dit(const float* __restrict__ sc_in
         const int nb = min(4, B - b0);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < D; k0 += WIN) {
+            const int wn = min(WIN, D - k0);
+            constexpr int SPT = 4 * WIN / 256;          // SiLU values per thread and window (four batches)
+            float sv[SPT];
+#pragma unroll
+            for (int t = 0; t < SPT; ++t) {
+                const int j = t / (WIN / 256), kk = (t % (WIN / 256)) * 256 + threadIdx.x;
+                sv[t] = (j < nb && kk < wn) ? sc_in[(size_t)(b0 + j) * D + k0 + kk] : 0.0f;
+            }
             intx4 raw[CL];
 #pragma unroll
             for (int i = 0; i < CL; ++i) {
                 const int k = k0 + (i * 16 + l16) * EV;
                 raw[i] = k < D ? *(const intx4*)(wr + k) : intx4{0, 0, 0, 0};
             }
-            const int wn = min(WIN, D - k0);
             __syncthreads();                            // the previous window's reads are done
-            for (int j = 0; j < nb; ++j)
-                for (int kk = threadIdx.x; kk < wn; kk += 256) sc[j][kk] = sc_in[(size_t)(b0 + j) * D + k0 + kk];
+#pragma unroll
+            for (int t = 0; t < SPT; ++t) {
+                const int j = t / (WIN / 256), kk = (t % (WIN / 256)) * 256 + threadIdx.x;
+                if (j < nb && kk < wn) sc[j][kk] = sv[t];
+            }
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < CL; ++i) {
