@@ -68,29 +68,31 @@ __global__ void k_silu(const T* __restrict__ in, float* __restrict__ out, int n)
 }
 
 // A GEMV over the [6D, D] weight, bound by reading it once: 16 lanes own one
-// row, a workgroup owns 16 rows.  K goes in windows of 16 16-byte loads per
+// row, a workgroup of NT threads owns NT / 16 rows (512: the DiT-XL matrix in
+// one round of workgroups, one per CU).  K goes in windows of 16 16-byte loads per
 // lane.  Each thread first loads its share of the window's SiLU(cond)
 // (computed once per step, up to four batches) into registers, then issues
 // the weight loads, then stages the SiLU values into LDS: both sets of loads
 // are in flight together, so the window costs one memory round trip.
-template <typename T>
-__global__ __launch_bounds__(256) void k_mod_dit(const float* __restrict__ sc_in, const T* __restrict__ w,
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_mod_dit(const float* __restrict__ sc_in, const T* __restrict__ w,
                                                  const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
     constexpr int EV = 16 / sizeof(T);                  // elements per 16-byte load (8 bf16, 4 f32)
     constexpr int CL = 16, WIN = CL * 16 * EV;          // loads per lane per window, window elements
     __shared__ float sc[4][WIN];
-    const int n = blockIdx.x * 16 + threadIdx.x / 16, l16 = threadIdx.x % 16;
+    static_assert(WIN % NT == 0 && NT % 16 == 0, "workgroup size");
+    const int n = blockIdx.x * (NT / 16) + threadIdx.x / 16, l16 = threadIdx.x % 16;
     const T* wr = w + (size_t)min(n, 6 * D - 1) * D;
     for (int b0 = 0; b0 < B; b0 += 4) {
         const int nb = min(4, B - b0);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < D; k0 += WIN) {
             const int wn = min(WIN, D - k0);
-            constexpr int SPT = 4 * WIN / 256;          // SiLU values per thread and window (four batches)
+            constexpr int SPT = 4 * WIN / NT;           // SiLU values per thread and window (four batches)
             float sv[SPT];
 #pragma unroll
             for (int t = 0; t < SPT; ++t) {
-                const int j = t / (WIN / 256), kk = (t % (WIN / 256)) * 256 + threadIdx.x;
+                const int j = t / (WIN / NT), kk = (t % (WIN / NT)) * NT + threadIdx.x;
                 sv[t] = (j < nb && kk < wn) ? sc_in[(size_t)(b0 + j) * D + k0 + kk] : 0.0f;
             }
             intx4 raw[CL];
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void k_mod_dit(const float* __restrict__ sc_in
             __syncthreads();                            // the previous window's reads are done
 #pragma unroll
             for (int t = 0; t < SPT; ++t) {
-                const int j = t / (WIN / 256), kk = (t % (WIN / 256)) * 256 + threadIdx.x;
+                const int j = t / (WIN / NT), kk = (t % (WIN / NT)) * NT + threadIdx.x;
                 if (j < nb && kk < wn) sc[j][kk] = sv[t];
             }
             __syncthreads();
@@ -154,9 +156,9 @@ hipError_t launch_silu(const void* in, int dt, float* out, int n, hipStream_t st
 hipError_t launch_mod_dit(const float* silu_cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st) {
     if (D < 8 || D % 8) return hipErrorInvalidValue;
-    const dim3 grid((6 * D + 15) / 16);
-    if (dt == LWO_F32) LWO_KL((k_mod_dit<float>), grid, 256, 0, st, silu_cond, (const float*)w, (const float*)b, mod, B, D);
-    else LWO_KL((k_mod_dit<bf16>), grid, 256, 0, st, silu_cond, (const bf16*)w, (const bf16*)b, mod, B, D);
+    const dim3 grid((6 * D + 31) / 32);
+    if (dt == LWO_F32) LWO_KL((k_mod_dit<float, 512>), grid, 512, 0, st, silu_cond, (const float*)w, (const float*)b, mod, B, D);
+    else LWO_KL((k_mod_dit<bf16, 512>), grid, 512, 0, st, silu_cond, (const bf16*)w, (const bf16*)b, mod, B, D);
     return hipGetLastError();
 }
 
