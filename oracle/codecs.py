@@ -49,6 +49,10 @@ def bf16_encode(x: np.ndarray) -> np.ndarray:
     t_val = toward.view(np.float32).astype(np.float64)
     with np.errstate(over="ignore", invalid="ignore"):
         a_val = away.view(np.float32).astype(np.float64)
+        # past the largest finite value the next pattern is infinity; as a grid
+        # point it stands at 2^128, so magnitudes from the midpoint up round to
+        # infinity (IEEE 754 round to nearest on overflow)
+        a_val = np.where(np.isinf(a_val) & np.isfinite(xv), np.copysign(2.0 ** 128, xv), a_val)
         d_t = np.abs(xv - t_val)
         d_a = np.abs(a_val - xv)
     t_hi = (toward >> np.uint32(16)).astype(np.uint16)
@@ -67,6 +71,25 @@ def bf16_encode(x: np.ndarray) -> np.ndarray:
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """float32 -> float64 value of its bf16 rounding."""
     return bf16_decode(bf16_encode(x))
+
+
+def bf16_round_grid(x: np.ndarray) -> np.ndarray:
+    """float32 -> float64 value of its bf16 rounding, from the format's grid
+    instead of its bit patterns: bf16 keeps 8 significant bits, so inside the
+    binade [2^(E-1), 2^E) (``frexp``'s exponent E) its values are the
+    multiples of 2^(E-8), and below the smallest normal 2^-126 the multiples
+    of 2^-133.  The value is the nearest multiple, ties to the even multiple
+    (``rint``), which is the even mantissa pattern; a magnitude that rounds to
+    2^128 or more overflows to infinity.  All of it is exact in float64.  The
+    same values as ``bf16_round`` (pinned bit for bit), several times faster
+    on the hundreds of millions of weights of a large block."""
+    xv = np.asarray(x, dtype=np.float32).astype(np.float64)
+    _, e = np.frexp(xv)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = np.rint(xv / q) * q
+        v = np.where(np.abs(v) >= 2.0 ** 128, np.copysign(np.inf, xv), v)
+    return v
 
 
 # ---------------------------------------------------------------- fp8 e4m3
@@ -114,6 +137,21 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     if nan.any():
         out[nan] = 0x7F
     return out
+
+
+def e4m3_round_grid(x: np.ndarray) -> np.ndarray:
+    """float -> float64 value of its e4m3 rounding (as e4m3_decode(e4m3_encode(x))),
+    from the format's grid: magnitudes are first saturated to 448; inside the
+    binade [2^(E-1), 2^E) the values are the multiples of 2^(E-4) (3 mantissa
+    bits), below the smallest normal 2^-6 the multiples of 2^-9 (the
+    subnormals m/8 * 2^-6); the nearest multiple is taken, ties to the even
+    one (the even code).  The sign is kept; NaN stays NaN."""
+    xv = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(xv), E4M3_MAX)
+    _, e = np.frexp(a)
+    q = np.ldexp(1.0, np.maximum(e - 4, -9))
+    with np.errstate(invalid="ignore"):
+        return np.copysign(np.rint(a / q) * q, xv)
 
 
 def quantize_tensor_e4m3(w: np.ndarray) -> tuple[np.ndarray, np.float32]:

@@ -176,3 +176,34 @@ def unpack_block(w, extent: bytes) -> dict:
             out[name] = (codecs.e4m3_decode(raw[name]) * np.float64(np.float32(sc[i]))).reshape(shape)
         out["_scales"] = sc.astype(np.float32)
     return out
+
+
+def stored_params(w, tensors) -> dict:
+    """The float64 tensors unpack_block(w, pack_block(w, tensors)) returns,
+    formed from the generator's float32 tensors without building the extent:
+    each tensor is rounded to its stored dtype (bf16 grid rounding; fp8 with
+    quantize_tensor_e4m3's per-tensor scale s, the code's value times s as
+    one multiply).  Tiling only moves bytes, so it does not enter.  Pinned
+    equal to the pack/unpack round trip for every kind and dtype; the GPU
+    parity tests of full-size stacks use it because packing hundreds of
+    millions of weights through the byte codecs is slow."""
+    slots, _ = layout_for(w)
+    by_name = {s.name: s for s in slots}
+    names = [n for n, _ in _names_shapes(w.kind, w.hidden, w.ffn)]
+    out, scales = {}, []
+    for name, t in zip(names, tensors):
+        s = by_name[name]
+        t = np.ascontiguousarray(t, dtype=np.float32)
+        assert t.shape == s.shape, (name, t.shape, s.shape)
+        if s.dtype == "f32":
+            out[name] = t.astype(np.float64)
+        elif s.dtype == "bf16":
+            out[name] = codecs.bf16_round_grid(t)
+        else:
+            amax = np.float32(np.max(np.abs(t))) if t.size else np.float32(0.0)
+            sc = np.float32(amax / np.float32(codecs.E4M3_MAX)) if amax > 0 else np.float32(1.0)
+            out[name] = codecs.e4m3_round_grid((t / sc).astype(np.float32)) * np.float64(sc)
+            scales.append(sc)
+    if w.linear_dtype == "fp8":
+        out["_scales"] = np.asarray(scales, dtype=np.float32)
+    return out

@@ -30,6 +30,7 @@ def test_bf16_encode_matches_torch_random():
 def test_bf16_encode_ties_and_specials():
     # exact halfway cases: 1 + 2^-8 (tie, even neighbour is 1.0), 1 + 3*2^-8 (tie, rounds up)
     ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 3.3895314e38,
+                     3.3961776e38, -3.3961776e38, 3.3961773e38, 3.4e38, np.finfo(np.float32).max,
                      np.inf, -np.inf, 0.0, -0.0, 1e-45, 65504.0], dtype=np.float32)
     np.testing.assert_array_equal(codecs.bf16_encode(ties), _bf16_torch(ties))
     assert codecs.bf16_encode(np.array([1 + 2 ** -8], np.float32))[0] == 0x3F80
@@ -157,3 +158,83 @@ def test_checksum_brute_force_and_properties():
     assert checksum.extent_checksum(bytes(a)) != checksum.extent_checksum(buf)
     with pytest.raises(ValueError):
         checksum.extent_checksum(b"1234567")
+
+
+# ------------------------------------------------------------------ grid rounding (fast stored values)
+
+def _bf16_neighbourhood() -> np.ndarray:
+    """Every bf16 pattern with several low halves: exact values, the smallest
+    steps above them, the ties just below/at/above the midpoint and the last
+    pattern before the next value (float32 bit patterns, both signs)."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0, 1, 0x3FFF, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    return u.view(np.float32)
+
+
+def test_bf16_round_grid_equals_the_pattern_codec():
+    x = _bf16_neighbourhood()
+    want = codecs.bf16_round(x)
+    got = codecs.bf16_round_grid(x)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), x[~same][:8]
+    assert (np.signbit(got) == np.signbit(want))[~np.isnan(want)].all()
+    rng = np.random.default_rng(11)
+    y = (rng.standard_normal(300_000) * np.exp(rng.uniform(-90, 88, 300_000))).astype(np.float32)
+    np.testing.assert_array_equal(codecs.bf16_round_grid(y), codecs.bf16_round(y))
+    # largest finite bf16, the overflow tie, and the subnormal steps
+    edge = np.array([3.3895314e38, 3.3961776e38, -3.3961776e38, 2 ** -133, 1.5 * 2 ** -133, 2 ** -134,
+                     2.5 * 2 ** -133, 1e-45], dtype=np.float32)
+    np.testing.assert_array_equal(codecs.bf16_round_grid(edge), codecs.bf16_round(edge))
+
+
+def test_e4m3_round_grid_equals_the_table_codec():
+    pos = codecs.E4M3_VALUES[:127]
+    mids = (pos[1:] + pos[:-1]) / 2
+    nudge = np.concatenate([mids * (1 - 2 ** -20), mids * (1 + 2 ** -20)])
+    rng = np.random.default_rng(12)
+    wide = rng.standard_normal(200_000) * np.exp(rng.uniform(-16, 8, 200_000))
+    x = np.concatenate([pos, -pos, mids, -mids, nudge, -nudge, wide, [0.0, -0.0, 448.0, 449.0, 464.0, 480.0,
+                                                                    1e9, -1e9, np.inf, -np.inf, np.nan]])
+    want = codecs.e4m3_decode(codecs.e4m3_encode(x))
+    got = codecs.e4m3_round_grid(x)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), x[~same][:8]
+    assert (np.signbit(got) == np.signbit(want))[~np.isnan(want)].all()
+
+
+# ------------------------------------------------------------------ the fp8 activation emulation
+
+@pytest.mark.parametrize("stored_bf16", [False, True])
+def test_fp8_activation_matches_torch_casts(stored_bf16):
+    """oracle.dit.fp8_activation against torch: (optionally) a bf16 cast of the
+    float32 rows, the per-row scale amax/448 in float32, a float8_e4m3fn cast
+    of the rows times 448/amax, and the codes' values times the scale."""
+    from oracle import dit
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((9, 200)) * np.exp(rng.uniform(-4, 4, (9, 1)))
+    z[4] = 0.0
+    z[6, :] = 1e-3
+    got = dit.fp8_activation(z, stored_bf16)
+    t = torch.from_numpy(z.astype(np.float32))
+    if stored_bf16:
+        t = t.to(torch.bfloat16).to(torch.float32)
+    amax = t.abs().amax(dim=1)
+    nz = amax > 0
+    scale = torch.where(nz, amax / 448.0, torch.ones_like(amax))
+    inv = torch.where(nz, 448.0 / torch.where(nz, amax, torch.ones_like(amax)), torch.zeros_like(amax))
+    codes = (t * inv[:, None]).to(torch.float8_e4m3fn)
+    want = codes.to(torch.float64) * scale.to(torch.float64)[:, None]
+    np.testing.assert_array_equal(got, want.numpy())
+    assert not got[4].any()
+
+
+def test_fp8_activation_bf16_pre_rounding_is_observable():
+    """The bf16 rounding before quantisation changes the code when it moves a
+    value across an e4m3 rounding boundary: with row amax 448 the scale is 1,
+    and 1 + 1/16 + 2^-10 (just above the e4m3 midpoint 1 + 1/16 between 1 and
+    1.125) rounds to bf16 1 + 1/16 exactly, a tie that goes to the even code 1.0."""
+    from oracle import dit
+    v = np.array([[1.0 + 2 ** -4 + 2 ** -10, 448.0]])
+    assert dit.fp8_activation(v, False)[0, 0] == 1.125
+    assert dit.fp8_activation(v, True)[0, 0] == 1.0

@@ -140,3 +140,14 @@ def test_pack_tiles_gemm_weights_only(name):
         else:
             assert not layout.tiled(nm, s.dtype)
             assert np.array_equal(seg, raw)
+
+
+@pytest.mark.parametrize("name", ["dit_tiny_fp32", "dit_t_bf16", "video_t_fp32", "video_t_bf16", "video_t_fp8"])
+def test_stored_params_equal_the_pack_unpack_round_trip(name):
+    w = lwo_synth.get(name)
+    t = lwo_synth.block_tensors(w, 2)
+    want = layout.unpack_block(w, layout.pack_block(w, t))
+    got = layout.stored_params(w, t)
+    assert sorted(got) == sorted(want)
+    for k in want:
+        assert got[k].dtype == want[k].dtype and np.array_equal(got[k], want[k]), k
