@@ -4,8 +4,10 @@
 One step = one pass of the whole block stack over one batch of synthetic
 input: every streamed block's weights are copied host -> device through the
 two slots while the previous block computes.  Default workload: the
-DiT-XL-shaped stack (28 blocks, D 1152, 16 heads, FFN 4608, batch 2, 1024
-tokens, bf16), all 28 blocks streamed.
+14B-class video DiT stack (40 blocks, D 5120, 40 heads of 128, FFN 13824,
+32760 tokens, 512 context tokens, bf16), all 40 blocks streamed: the largest
+workload that fits one GPU, and the one whose per-block compute must hide the
+next block's copy.
 
 Timed regions (HIP events recorded on the stream the library enqueues on):
   resident  blocks 0..L-1 kept on the device (no copies)       -> T_res
@@ -24,6 +26,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -110,45 +114,82 @@ def block_flops(w) -> float:
     return gemm + attn
 
 
+def _f32_params(p: dict) -> dict:
+    return {k: v.astype(np.float32) for k, v in p.items() if not k.startswith("_")}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, seconds: float, max_block_flops: float = 2.5e12, type_of=None):
-    """The oracle (float64, every weight resident) on a bounded sample: whole
-    blocks of the step while the time budget lasts; for a block above
-    max_block_flops, one block at fewer tokens, scaled by the FLOP ratio.
+    """The oracle (every weight resident, NumPy float32 with BLAS on every
+    host core) timed on a bounded sample of the step.
+
+    Blocks up to max_block_flops: whole blocks of the step in order while the
+    time budget lasts, per-block time x the block count.  Larger blocks (the
+    32760-token video blocks): the oracle's block evaluated at r query rows
+    (oracle.dit.video_block_rows: LayerNorm, K and V over every token, the
+    rest of the block for the r rows against all keys and values), timed at
+    two row counts.  Its cost is affine in r, so the two points extrapolate to
+    all rows of one full-shape block, then x the block count.  float64 (the
+    precision of the parity oracle) is timed the same way as an extra.
     type_of(b): block b's workload in a mixed stack (w gives the inputs)."""
-    import numpy as np
     import lwo_synth
     from oracle import dit as o_dit
     from oracle import layout as o_layout
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    scale, note = 1.0, ""
-    if block_flops(w) > max_block_flops:
-        t_sub = 2048
-        ws = w.with_(tokens=t_sub)
-        scale = block_flops(w) / block_flops(ws)
-        note = (f"; one block at {t_sub} of {w.tokens} tokens, scaled by the algorithmic FLOP ratio "
-                f"{scale:.1f} (an extrapolation)")
-        w_run = ws
-    else:
-        w_run = w
-    x, cond, ctx = o_dit.decode_inputs(w_run, *lwo_synth.step_inputs(w_run))
-    done, spent = 0, 0.0
-    while done < w.n_blocks and (done == 0 or (spent < seconds and scale == 1.0)):
-        wb = w_run if type_of is None else type_of(done)
-        ext = o_layout.pack_block(wb, lwo_synth.block_tensors(wb, done))   # packing is not timed
+    cores = int(_threads())
+    threads = min(16, os.cpu_count() or 1)
+    x64, c64, ctx64 = o_dit.decode_inputs(w, *lwo_synth.step_inputs(w))
+    if block_flops(w) <= max_block_flops:
+        x = x64.astype(np.float32)
+        cond = c64.astype(np.float32)
+        ctx = None if ctx64 is None else ctx64.astype(np.float32)
+        done, spent = 0, 0.0
+        while done < w.n_blocks and (done == 0 or spent < seconds):
+            wb = w if type_of is None else type_of(done)
+            p = _f32_params(o_layout.stored_params(wb, lwo_synth.block_tensors(wb, done), threads=threads))
+            t0 = time.perf_counter()
+            x = o_dit.block_forward(wb, x, cond, ctx, p)
+            spent += time.perf_counter() - t0
+            done += 1
+            log(f"oracle block {done}: {spent:.1f} s so far")
+        return {"value": round(spent / done * 1e3 * w.n_blocks, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+                "sample": f"{done} of {w.n_blocks} blocks of one step timed ({spent:.1f} s), per-block time x "
+                          f"{w.n_blocks}; NumPy float32, {cores} BLAS threads"}
+    assert w.kind == "video"
+    p64 = o_layout.stored_params(w, lwo_synth.block_tensors(w, 0), threads=threads)
+
+    def timed_rows(dt, n):
+        rows = np.arange(n)
+        p = p64 if dt == np.float64 else _f32_params(p64)
+        args = [a.astype(dt) for a in (x64, c64, ctx64)]
         t0 = time.perf_counter()
-        x = o_dit.stack_forward(wb, [ext], x, cond, ctx, blocks=[0])
-        spent += time.perf_counter() - t0
-        done += 1
-        log(f"oracle block {done}: {spent:.1f} s so far")
-    per_block_ms = spent / done * 1e3 * scale
-    return {"value": round(per_block_ms * w.n_blocks, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {w.n_blocks} blocks of one step timed ({spent:.1f} s), "
-                      f"per-block time x {w.n_blocks}; float64 NumPy, weights decoded from the packed extents"
-                      + note}
+        o_dit.video_block_rows(*args, p, w.heads, rows)
+        return time.perf_counter() - t0
+
+    out = {}
+    for dt, (r1, r2) in ((np.float32, (256, 1024)), (np.float64, (64, 256))):
+        r2 = min(r2, w.tokens)
+        r1 = min(r1, r2 // 2)
+        t1, t2 = timed_rows(dt, r1), timed_rows(dt, r2)
+        per_block = t1 + (t2 - t1) * (w.tokens - r1) / (r2 - r1)
+        out[dt] = (per_block, t1, t2, r1, r2)
+        log(f"oracle block 0, {np.dtype(dt).name}: {r1} rows {t1:.1f} s, {r2} rows {t2:.1f} s -> "
+            f"{per_block:.0f} s for all {w.tokens} rows")
+    pb, t1, t2, r1, r2 = out[np.float32]
+    pb64 = out[np.float64][0]
+    return {"value": round(pb * 1e3 * w.n_blocks, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": f"block 0 at full shape (all {w.tokens} tokens for K/V, queries against all keys) evaluated "
+                      f"at {r1} and {r2} query rows ({t1:.1f} s and {t2:.1f} s), its affine cost in the rows "
+                      f"extrapolated to all {w.tokens} rows, x {w.n_blocks} blocks; NumPy float32, {cores} BLAS "
+                      f"threads",
+            "float64_value": round(pb64 * 1e3 * w.n_blocks, 1),
+            "float64_sample": f"the same at {out[np.float64][3]} and {out[np.float64][4]} rows in float64"}
 
 
 def mfma_probe(torch, lwo, s, reps: int = 3) -> dict:
@@ -179,7 +220,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dit_xl_bf16")
+    ap.add_argument("--workload", default="video14b_bf16")
     ap.add_argument("--resident-prefix", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,7 +239,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import layerwise_weight_offload_amd as lwo

@@ -189,21 +189,23 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
         return e;
     };
     const char* dtn = act == LWO_F32 ? "f32" : (fp8 ? "fp8" : "bf16");
-    auto gemm = [&](const GemmArgs& g) {
+    // One timing class per call site (the product and its epilogue), so that a
+    // class's launches all have one shape.
+    auto gemm = [&](const char* site, const GemmArgs& g) {
         static const char* epn[] = {"store", "gelu", "gated", "resid"};
         char name[48];
-        snprintf(name, sizeof(name), "gemm_%s_%s", dtn, epn[g.epi]);
+        snprintf(name, sizeof(name), "gemm_%s_%s_%s", dtn, site, epn[g.epi]);
         const double ea = dtype_bytes(g.dtype), eo = g.epi <= EPI_GELU ? ae : 8.0;
         const double bytes = (double)g.M * g.K * ea + (double)g.N * g.K * ea + (double)g.M * g.N * eo;
         return timed(name, 2.0 * g.M * g.N * g.K, bytes, [&] { return launch_gemm(g, st); });
     };
-    auto attn = [&](const void* q, int ldq, const void* k, const void* v, int ldkv, int Tk) {
+    auto attn = [&](const char* site, const void* q, int ldq, const void* k, const void* v, int ldkv, int Tk) {
         AttnArgs a{};
         a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldkv; a.v = v; a.ldv = ldkv;
         a.o = ws.attn; a.ldo = D;
         a.B = B; a.H = H; a.Tq = T; a.Tk = Tk; a.dh = dh; a.dtype = act;
         char name[48];
-        snprintf(name, sizeof(name), "attn_%s_d%d", act == LWO_F32 ? "f32" : "bf16", dh);
+        snprintf(name, sizeof(name), "attn_%s_%s_d%d", site, act == LWO_F32 ? "f32" : "bf16", dh);
         const double flops = 4.0 * B * H * (double)T * Tk * dh;
         const double bytes = (double)B * ((double)T * D * 2 + 2.0 * Tk * D) * ae;
         return timed(name, flops, bytes, [&] { return launch_attention(a, st); });
@@ -224,18 +226,18 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
         LWO_LAUNCH(ln(mod, 0, 1, ws.h, act, nullptr));
         GemmArgs g = gemm_args(d, ws.h, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
         g.out = big; g.ldo = 3 * D;
-        LWO_LAUNCH(gemm(g));
-        LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
+        LWO_LAUNCH(gemm("qkv", g));
+        LWO_LAUNCH(attn("self", big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
         g = gemm_args(d, ws.attn, p.o_w, M, D, D, EPI_GATED, p.o_b);
         g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
-        LWO_LAUNCH(gemm(g));
+        LWO_LAUNCH(gemm("o", g));
         LWO_LAUNCH(ln(mod, 3, 4, ws.h, act, nullptr));
         g = gemm_args(d, ws.h, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
         g.out = big; g.ldo = F;
-        LWO_LAUNCH(gemm(g));
+        LWO_LAUNCH(gemm("fc1", g));
         g = gemm_args(d, big, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
         g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
-        LWO_LAUNCH(gemm(g));
+        LWO_LAUNCH(gemm("fc2", g));
         return LWO_OK;
     }
 
@@ -246,48 +248,48 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     GemmArgs g = gemm_args(d, h_buf, p.q_w, M, 3 * D, D, EPI_STORE, p.qkv_b);
     g.out = big; g.ldo = 3 * D;
     fp8_in(g, 0, ws.q8_scale, true);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("qkv", g));
     LWO_LAUNCH(timed("rmsnorm_qk", 0.0, 4.0 * M * D * ae,
                      [&] { return launch_rmsnorm_qk(big, act, M, D, p.q_norm, p.k_norm, st); }));
-    LWO_LAUNCH(attn(big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
+    LWO_LAUNCH(attn("self", big, 3 * D, big + (size_t)D * ae, big + (size_t)2 * D * ae, 3 * D, T));
     const void* a_in = ws.attn;
     if (fp8) { LWO_LAUNCH(quant(ws.attn, M, D, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.o_w, M, D, D, EPI_GATED, p.o_b);
     g.xr = ws.xr; g.ldx = D; g.gate = mod + 2 * D; g.gate_ld = 6 * D;
     fp8_in(g, 3, ws.q8_scale, false);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("o", g));
 
     // cross-attention: ungated, plain LayerNorm on the queries, keys/values from the context
     LWO_LAUNCH(ln(nullptr, 0, 0, h_buf, h_dt, ws.q8_scale));
     g = gemm_args(d, h_buf, p.cq_w, M, D, D, EPI_STORE, p.cq_b);
     g.out = ws.cq; g.ldo = D;
     fp8_in(g, 4, ws.q8_scale, false);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("cq", g));
     g = gemm_args(d, fp8 ? (const void*)ws.ctx8 : ctx, p.ck_w, Mc, 2 * D, D, EPI_STORE, p.ckv_b);
     g.out = ws.ckv; g.ldo = 2 * D;
     fp8_in(g, 5, ws.ctx8_scale, true);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("ckv", g));
     const char* ckv = (const char*)ws.ckv;
-    LWO_LAUNCH(attn(ws.cq, D, ckv, ckv + (size_t)D * ae, 2 * D, d.ctx_tokens));
+    LWO_LAUNCH(attn("cross", ws.cq, D, ckv, ckv + (size_t)D * ae, 2 * D, d.ctx_tokens));
     a_in = ws.attn;
     if (fp8) { LWO_LAUNCH(quant(ws.attn, M, D, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.co_w, M, D, D, EPI_RESID, p.co_b);
     g.xr = ws.xr; g.ldx = D;
     fp8_in(g, 7, ws.q8_scale, false);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("co", g));
 
     // FFN
     LWO_LAUNCH(ln(mod, 3, 4, h_buf, h_dt, ws.q8_scale));
     g = gemm_args(d, h_buf, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
     g.out = big; g.ldo = F;
     fp8_in(g, 8, ws.q8_scale, false);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("fc1", g));
     a_in = big;
     if (fp8) { LWO_LAUNCH(quant(big, M, F, ws.q8, ws.q8_scale)); a_in = ws.q8; }
     g = gemm_args(d, a_in, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
     g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
     fp8_in(g, 9, ws.q8_scale, false);
-    LWO_LAUNCH(gemm(g));
+    LWO_LAUNCH(gemm("fc2", g));
     return LWO_OK;
 }
 

@@ -14,6 +14,7 @@ transformer: a tiny DiT, a DiT-XL-shaped stack, and a 14B-class video DiT):
                       T=32760 (21x30x52 latent patches), 512 context tokens
 * ``video14b_t256``   the same stack at T=256 (transfer-bound)
 * ``video14b_fp8``    the same stack with per-tensor fp8 e4m3 linear weights
+* ``video14b_t256_fp8`` the fp8 stack at T=256
 
 plus small variants (suffix ``_t``) whose shapes span several kernel tiles
 with ragged tails, used by the parity tests, and small mixed stacks of two
@@ -87,6 +88,8 @@ _add(Workload("video14b_t256", KIND_VIDEO, 40, 5120, 40, 13824, 1, 256, 512, "bf
 _add(Workload("video14b_t256_k8", KIND_VIDEO, 40, 5120, 40, 13824, 1, 256, 512, "bf16", "bf16", 103,
               resident_prefix=8))
 _add(Workload("video14b_fp8", KIND_VIDEO, 40, 5120, 40, 13824, 1, 32760, 512, "bf16", "fp8", 103))
+# the fp8 stack at 256 tokens: end-to-end parity of all 40 blocks with fp8 linears
+_add(Workload("video14b_t256_fp8", KIND_VIDEO, 40, 5120, 40, 13824, 1, 256, 512, "bf16", "fp8", 103))
 
 # Small variants for parity: several tiles along every axis and ragged tails.
 _add(Workload("dit_t_fp32", KIND_DIT, 3, 576, 8, 2304, 2, 200, 0, "f32", "f32", 201))

@@ -178,7 +178,19 @@ def unpack_block(w, extent: bytes) -> dict:
     return out
 
 
-def stored_params(w, tensors) -> dict:
+def _rows_parallel(fn, t: np.ndarray, threads: int) -> np.ndarray:
+    """fn applied to row ranges of t on a thread pool and concatenated; only
+    for elementwise fn, where splitting the rows cannot change a value."""
+    if threads <= 1 or t.ndim < 2 or t.shape[0] < 2 * threads:
+        return fn(t)
+    import concurrent.futures as fut
+    step = (t.shape[0] + threads - 1) // threads
+    with fut.ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(lambda i: fn(t[i:i + step]), range(0, t.shape[0], step)))
+    return np.concatenate(parts, axis=0)
+
+
+def stored_params(w, tensors, threads: int = 1) -> dict:
     """The float64 tensors unpack_block(w, pack_block(w, tensors)) returns,
     formed from the generator's float32 tensors without building the extent:
     each tensor is rounded to its stored dtype (bf16 grid rounding; fp8 with
@@ -186,7 +198,8 @@ def stored_params(w, tensors) -> dict:
     one multiply).  Tiling only moves bytes, so it does not enter.  Pinned
     equal to the pack/unpack round trip for every kind and dtype; the GPU
     parity tests of full-size stacks use it because packing hundreds of
-    millions of weights through the byte codecs is slow."""
+    millions of weights through the byte codecs is slow.  ``threads`` splits
+    the elementwise rounding of large tensors over row ranges."""
     slots, _ = layout_for(w)
     by_name = {s.name: s for s in slots}
     names = [n for n, _ in _names_shapes(w.kind, w.hidden, w.ffn)]
@@ -198,11 +211,12 @@ def stored_params(w, tensors) -> dict:
         if s.dtype == "f32":
             out[name] = t.astype(np.float64)
         elif s.dtype == "bf16":
-            out[name] = codecs.bf16_round_grid(t)
+            out[name] = _rows_parallel(codecs.bf16_round_grid, t, threads)
         else:
             amax = np.float32(np.max(np.abs(t))) if t.size else np.float32(0.0)
             sc = np.float32(amax / np.float32(codecs.E4M3_MAX)) if amax > 0 else np.float32(1.0)
-            out[name] = codecs.e4m3_round_grid((t / sc).astype(np.float32)) * np.float64(sc)
+            out[name] = _rows_parallel(lambda r: codecs.e4m3_round_grid((r / sc).astype(np.float32)) * np.float64(sc),
+                                       t, threads)
             scales.append(sc)
     if w.linear_dtype == "fp8":
         out["_scales"] = np.asarray(scales, dtype=np.float32)

@@ -3,6 +3,10 @@ step inputs on the device, run steps on a non-default stream, and compute
 the oracle's answer on the same inputs."""
 from __future__ import annotations
 
+import concurrent.futures as _fut
+import os
+import time
+
 import numpy as np
 
 import lwo_synth
@@ -67,3 +71,58 @@ def oracle_out(w, tensors=None, inputs=None, steps=1):
             from oracle import codecs
             x = codecs.bf16_round(x.astype(np.float32))
     return x0, x
+
+
+def build_with_oracle(lwo, w, fp8_act: bool = False):
+    """Build w's store (PIN_COPY) and, in the same pass over the generator's
+    blocks, run the oracle's stack forward on the same drawn tensors, so that
+    each block is drawn once and host memory holds one block's float32 and
+    float64 tensors at a time besides the store.  The oracle takes the stored
+    values from oracle.layout.stored_params and runs on a worker thread while
+    the library packs the next extent.  Returns (store, x0, want): the
+    oracle's input and its output after one pass over every block, in
+    float64, with the bf16 rounding of the output for a bf16 workload."""
+    desc = lwo.ModelDesc.from_workload(w)
+    x0, cond, ctx = o_dit.decode_inputs(w, *lwo_synth.step_inputs(w))
+    threads = min(16, os.cpu_count() or 1)
+    blocks = lwo_synth.iter_blocks(w, threads=threads)
+    pool = _fut.ThreadPoolExecutor(max_workers=1)
+    state = {"x": x0, "job": None}
+    t0 = time.perf_counter()
+
+    def advance(b, t):
+        p = o_layout.stored_params(w, t, threads=threads)
+        state["x"] = o_dit.block_forward(w, state["x"], cond, ctx, p, fp8_act=fp8_act)
+        if b % 4 == 3 or b == w.n_blocks - 1:
+            print(f"[oracle] {w.name}: block {b + 1}/{w.n_blocks} at {time.perf_counter() - t0:.0f} s", flush=True)
+
+    def fill(b, dst, n):
+        bb, t = next(blocks)
+        assert bb == b
+        if state["job"] is not None:
+            state["job"].result()        # the oracle runs the blocks in order
+        state["job"] = pool.submit(advance, b, t)
+        lwo.pack_block(desc, t, dst=dst, dst_bytes=n)
+
+    try:
+        store = lwo.build_block_store(desc, fill=fill)
+        state["job"].result()
+    finally:
+        pool.shutdown(wait=True)
+    want = state["x"]
+    if w.act_dtype == "bf16":   # the step hands x back in the activation dtype
+        from oracle import codecs
+        want = codecs.bf16_round(want.astype(np.float32))
+    return store, x0, want
+
+
+def row_col_errors(got: np.ndarray, want: np.ndarray):
+    """Largest relative L2 error of any token row and of any feature column of
+    [..., D] outputs (rows = every leading index).  A wrong row or column
+    shows an O(1) error there even when the whole-tensor figure hides it."""
+    g = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    r = np.asarray(want, np.float64).reshape(-1, want.shape[-1])
+    d = g - r
+    rows = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)
+    cols = np.linalg.norm(d, axis=0) / np.maximum(np.linalg.norm(r, axis=0), 1e-300)
+    return float(rows.max()), float(cols.max())

@@ -147,7 +147,8 @@ def test_stored_params_equal_the_pack_unpack_round_trip(name):
     w = lwo_synth.get(name)
     t = lwo_synth.block_tensors(w, 2)
     want = layout.unpack_block(w, layout.pack_block(w, t))
-    got = layout.stored_params(w, t)
-    assert sorted(got) == sorted(want)
-    for k in want:
-        assert got[k].dtype == want[k].dtype and np.array_equal(got[k], want[k]), k
+    for threads in (1, 3):
+        got = layout.stored_params(w, t, threads=threads)
+        assert sorted(got) == sorted(want)
+        for k in want:
+            assert got[k].dtype == want[k].dtype and np.array_equal(got[k], want[k]), (k, threads)
