@@ -1,10 +1,16 @@
 """GPU parity through the C ABI: streamed execution against the float64 oracle,
 streamed == resident bit for bit, slot bytes == host bytes.
 
-Tolerances (relative L2 over the whole output, float64; every token row and
-every feature column of the output is also held to 1.5 times the output
-bound, so that a wrong row or column, which the whole-tensor figure can hide,
-fails):
+Tolerances (relative L2 over the whole output, float64).  Every token row is
+also held to 1.5 times the output bound and every feature column to 5 times
+it, so that a wrong row or column, which the whole-tensor figure can hide,
+fails (its error is of order 1).  Rows are alike (the worst row measures
+1.1 times the whole tensor); columns are not: where a linear's input column is
+dominated by a per-column shift, it rounds the same way in every row and its
+error does not average out, so a few columns carry 3-4 times the whole
+tensor's error.  The oracle with emulated fp8 activations shows the same
+against the plain oracle (worst column 0.14-0.17 against 0.042 on a video
+block), so this is the arithmetic, not the kernels.
   * fp32 workloads: 1e-4 on x_out and on the block-stack update x_out - x_in
     (fp32 accumulation over K <= 4608 gives ~1e-6; the bound is the stated one);
   * bf16 workloads: 2e-2 on x_out (the stated bound) and 3e-2 on the update:
@@ -42,7 +48,7 @@ def _parity(lwo, name, tol_out, tol_delta, k=0, steps=1):
     print(f"[parity] {name}: rel_l2(out)={e_out:.3e} rel_l2(update)={e_delta:.3e} max row {e_row:.3e} "
           f"max column {e_col:.3e}", flush=True)
     assert e_out <= tol_out and e_delta <= tol_delta, (e_out, e_delta)
-    assert e_row <= 1.5 * tol_out and e_col <= 1.5 * tol_out, (e_row, e_col)
+    assert e_row <= 1.5 * tol_out and e_col <= 5 * tol_out, (e_row, e_col)
 
 
 def test_dit_tiny_fp32_full(lib):
@@ -87,7 +93,7 @@ def test_video14b_block_full_size_sampled_rows(lib, name, tol_out, tol_delta):
     print(f"[parity] {name} block: rel_l2(out)={e_out:.3e} rel_l2(update)={e_delta:.3e} max row {e_row:.3e} "
           f"max column {e_col:.3e}", flush=True)
     assert e_out <= tol_out and e_delta <= tol_delta, (e_out, e_delta)
-    assert e_row <= 1.5 * tol_out and e_col <= 1.5 * tol_out, (e_row, e_col)
+    assert e_row <= 1.5 * tol_out and e_col <= 5 * tol_out, (e_row, e_col)
     if w.linear_dtype == "fp8":
         emul = bf(o_dit.video_block_rows(x0, c0, ctx0, params, w.heads, rows, fp8_act=True))
         e_emul = o_dit.rel_l2(got - xr, emul - xr)

@@ -13,10 +13,12 @@ against the float64 oracle over every output element.
   compound: each block's update is of the size of the residual stream, and
   its quantisation error is fresh, about 4% of it), so this bound has about
   15% headroom and is not widened.
-* every row (token) and every column (feature) of the output is also held to
-  1.5 times the whole-tensor bound: a row's or a column's error is the same
-  statistic over 5120 or 256 elements, and a wrong row or column would show
-  an O(1) error there.
+* every row (token) of the output is also held to 1.5 times the whole-tensor
+  bound and every column (feature) to 5 times it: a wrong row or column shows
+  an error of order 1 there.  Rows are alike; a few columns carry 3-4 times
+  the whole tensor's error, because a linear's input column that a
+  per-column shift dominates rounds the same way in every row (the oracle
+  with emulated fp8 activations shows the same against the plain one).
 
 The oracle runs block by block beside the store's build, on the same drawn
 tensors (tests/gpu_util.build_with_oracle), so host memory holds the pinned
@@ -51,7 +53,7 @@ def _check(name, got, x0, want, tol_out, tol_delta):
           f"max row {e_row:.3e} max column {e_col:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert e_out <= tol_out and e_delta <= tol_delta, (e_out, e_delta)
-    assert e_row <= 1.5 * tol_out and e_col <= 1.5 * tol_out, (e_row, e_col)
+    assert e_row <= 1.5 * tol_out and e_col <= 5 * tol_out, (e_row, e_col)
 
 
 def test_video14b_t256_bf16_stack_streamed_prefix_resident(lib):
