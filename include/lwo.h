@@ -12,8 +12,8 @@
  *         table (prefetch next block on a copy stream, last block prefetches
  *         block 0, flattened pinned host tensors).
  *   [DLO] "Distributed Layerwise Offload": "Components and ownership",
- *         "Startup and runtime sequence" (two shared device slots sized for
- *         the largest streamed block, readiness events, prime the first
+ *         "Startup and runtime sequence" (a pair of device buffers as large
+ *         as the biggest streamed block, readiness events, prime the first
  *         block), "Registered runtime-cache transfer" (page-align, coalesce,
  *         budget check before mutation, read-only registration, all-or-
  *         nothing rollback, unregister before unmap), "Failure and lifecycle
@@ -84,7 +84,7 @@ typedef enum lwo_status {
     LWO_EROLLBACK = 6,   /* a rollback unregister failed: the process must not unmap the range */
     LWO_ESTATE = 7,      /* call not valid in the store's current state */
     LWO_ECHECKSUM = 8,   /* slot bytes differ from the host extent, or a cache entry from its digests */
-    LWO_ETIMEOUT = 9,    /* a bounded wait ran out (another writer holds a cache lock) */
+    LWO_ETIMEOUT = 9,    /* a wait with a time limit expired (another writer holds a cache lock) */
     LWO_EIO = 10         /* a file, lock or mapping operation failed (message names it) */
 } lwo_status;
 
@@ -337,13 +337,18 @@ lwo_status lwo_set_max_inflight(lwo_store* store, int32_t max_inflight);
 
 /* Validation mode (on != 0): before each streamed block the compute stream
  * checksums the slot on the device and compares it with the host extent's
- * sum taken at build; mismatches are counted in lwo_stats. */
+ * sum taken at build; mismatches are counted in lwo_stats.
+ * Source: [ARCH] "Cross-strategy invariants" (while a parameter is offloaded
+ * its host copy is the single authoritative one, so a slot must hold exactly
+ * those bytes); the checksum itself is a project addition (the pages name no
+ * check), a position-weighted SplitMix64 sum (lwo_extent_checksum). */
 lwo_status lwo_set_validation(lwo_store* store, int32_t on);
 
 /* Synchronise, copy block `block` into a slot (or use its resident copy),
  * checksum it on the device and compare with the host extent's checksum.
  * Writes both sums; LWO_ECHECKSUM if they differ.  Leaves the ring primed
- * as it was. */
+ * as it was.  Source: as lwo_set_validation ([ARCH] "Cross-strategy
+ * invariants"); a project addition for checking one block on demand. */
 lwo_status lwo_block_checksum(lwo_store* store, int32_t block, uint64_t* host_sum, uint64_t* slot_sum);
 
 /* Per-copy timing: when on, every block copy is bracketed by timing events on
@@ -371,7 +376,12 @@ typedef struct lwo_kernel_stat {
 lwo_status lwo_set_kernel_timing(lwo_store* store, int32_t on);
 lwo_status lwo_kernel_stats(lwo_store* store, lwo_kernel_stat* out, int32_t cap, int32_t* n);
 
-/* Synchronise the store's copy stream and snapshot its counters. */
+/* Synchronise the store's copy stream and snapshot its counters.  A project
+ * addition: the pages publish no figures ([DLO] "Validation status": hardware
+ * and performance claims need fresh measurements), and these counters (bytes
+ * copied per step, host and device residency, the host mode in effect after
+ * a registration fallback, [DLO] "Host backing and transfer composition")
+ * are what such measurements read. */
 lwo_status lwo_get_stats(lwo_store* store, lwo_stats* out);
 
 /* [DLO] "Failure and lifecycle boundaries": synchronise outstanding device
@@ -444,7 +454,10 @@ lwo_status lwo_op_rmsnorm_qk(int32_t dtype, void* qkv, int32_t M, int32_t D, con
 lwo_status lwo_probe_mfma(int32_t dtype, int32_t blocks, int32_t iters, float* sink, uint64_t sink_floats, void* stream,
                           double* flops);
 
-/* Thread-local description of the last failure ("" if none). */
+/* Thread-local description of the last failure ("" if none).  A project
+ * addition: [DLO] "Failure and lifecycle boundaries" and [ARCH] "Shared
+ * lifecycle" require failures to surface without partial state; the status
+ * code says which failure, this text says where. */
 const char* lwo_last_error(void);
 
 #ifdef __cplusplus

@@ -4,6 +4,7 @@ from __future__ import annotations
 import ctypes as C
 import dataclasses
 import os
+import weakref
 
 import numpy as np
 
@@ -429,21 +430,42 @@ def cache_publish(directory: str, desc: ModelDesc, extents=None, fill=None, wait
     return key.value.decode(), bool(created.value)
 
 
+class CacheExtents(list):
+    """Page-aligned extent addresses inside an open entry's mapping.  The list
+    holds its entry, so a store that keeps the list keeps the entry too."""
+
+    def __init__(self, addrs, entry):
+        super().__init__(addrs)
+        self.entry = entry
+
+
 class CacheEntry:
-    """An open, validated entry mapped read-only; extents() are page-aligned addresses in the mapping."""
+    """An open, validated entry mapped read-only; extents() are page-aligned addresses in the mapping.
+    close() refuses while a store built on those extents is alive (its copies read the mapping)."""
 
     def __init__(self, handle, n):
         self._h = handle
         self.n_blocks = n
+        self._borrowers = weakref.WeakSet()
 
-    def extents(self) -> list[int]:
+    def extents(self) -> CacheExtents:
+        if not self._h:
+            raise LwoError(7, "cache entry is closed")
         arr = (C.c_void_p * self.n_blocks)()
         n = C.c_int32()
         _check(_lib_cache_extents(self._h, arr, self.n_blocks, C.byref(n)))
-        return [int(arr[i]) for i in range(n.value)]
+        return CacheExtents([int(arr[i]) for i in range(n.value)], self)
+
+    def borrow(self, store) -> None:
+        """Record a store (anything with a `handle`, non-zero while it is alive) that reads the mapping."""
+        self._borrowers.add(store)
 
     def close(self) -> None:
         if self._h:
+            live = [s for s in self._borrowers if getattr(s, "handle", 0)]
+            if live:
+                raise LwoError(7, f"{len(live)} store(s) built on this entry's extents are still alive: "
+                                  "destroy them before closing the entry")
             _check(_lib_cache_close(self._h))
             self._h = None
 
@@ -468,7 +490,10 @@ def build_block_store(desc: ModelDesc, extents=None, fill=None, host_mode: int =
     src, keep = _source(extents, fill)
     h = C.c_void_p()
     _check(_lib_build(C.byref(desc._c()), C.byref(src), host_mode, register_budget, device, C.byref(h)))
-    return Store(h, desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)
+    store = Store(h, desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)
+    if isinstance(extents, CacheExtents) and host_mode in (HOST_REGISTER, HOST_STAGED):
+        extents.entry.borrow(store)
+    return store
 
 
 def build_mixed_store(types, block_type, extents=None, fill=None, host_mode: int = HOST_PIN_COPY,

@@ -7,7 +7,7 @@
 // entry per identity; publication into a same-filesystem temporary directory
 // that is flushed and atomically renamed; a manifest with SHA-256 digests;
 // kernel flock ownership, so a dead writer releases the lock; stale
-// temporary entries removed by the next lock owner; a bounded wait) and
+// temporary entries removed by the next lock owner; a lock wait with a time limit) and
 // "Registered runtime-cache transfer" (page-aligned ranges of one mapping).
 //
 // Entry <dir>/<key>/ holds

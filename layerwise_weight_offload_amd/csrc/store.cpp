@@ -7,16 +7,16 @@
 //    / How It Works": a dedicated copy stream prefetches block i+1 while
 //    block i computes, parameters are kept as flattened pinned host tensors,
 //    and the last block prefetches block 0 (execution-flow table).
-//  * "Distributed Layerwise Offload", "Startup and runtime sequence": two
-//    shared device slots sized for the largest streamed block, compute waits
-//    until the current slot is ready, the next block goes to the alternate
+//  * "Distributed Layerwise Offload", "Startup and runtime sequence": a pair
+//    of device buffers, each as large as the biggest block that streams;
+//    compute waits for the current buffer's readiness, the next block goes to the alternate
 //    slot, the first block is primed at enable; "Feature compatibility":
 //    resident leading layers; "Registered runtime-cache transfer" and
 //    "Failure and lifecycle boundaries": page-aligned, coalesced, budgeted,
 //    read-only, all-or-nothing host registration, and shutdown order
 //    (synchronise, unregister, then release).
-//  * "CPU Offloading", "Cross-strategy invariants": device storage is not
-//    reused until dependent compute or transfer work is complete; "Shared
+//  * "CPU Offloading", "Cross-strategy invariants": a device buffer is only
+//    reused once the kernels and copies that depend on it have finished; "Shared
 //    lifecycle": a failed enable leaves no partial state.
 //  * "Distributed Layerwise Offload", "Host backing and transfer
 //    composition" and "Runtime cache": with pageable (e.g. mmap) host

@@ -174,3 +174,36 @@ def test_held_lock_times_out_and_dead_writer_releases(lib, tmp_path):
     p.join(timeout=60)
     key2, created = lib.cache_publish(str(tmp_path), desc, extents=bufs, wait_ms=5000)
     assert key2 == key and created
+
+
+def test_close_refuses_while_a_borrowing_store_lives(lib, tmp_path):
+    """The extents list keeps its entry alive, and the entry cannot be unmapped
+    while a store that reads its extents is alive (a stand-in object with a
+    live handle plays the store here; the GPU test builds a real one)."""
+    import gc
+    desc, ext, bufs = _extents(lib, "dit_tiny_fp32")
+    key, _ = lib.cache_publish(str(tmp_path), desc, extents=bufs)
+    entry = lib.cache_open(str(tmp_path), key, desc, verify=True)
+    addrs = entry.extents()
+    assert addrs.entry is entry
+
+    class Borrower:
+        handle = 1
+
+    store = Borrower()
+    entry.borrow(store)
+    with pytest.raises(lib.LwoError) as e:
+        entry.close()
+    assert e.value.status == 7
+    assert ctypes.string_at(addrs[0], ext) == bufs[0].tobytes()   # still mapped
+    store.handle = 0                                               # destroyed
+    entry.close()
+    with pytest.raises(lib.LwoError):
+        entry.extents()
+    # a dropped store no longer blocks closing
+    entry = lib.cache_open(str(tmp_path), key, desc, verify=False)
+    s2 = Borrower()
+    entry.borrow(s2)
+    del s2
+    gc.collect()
+    entry.close()

@@ -120,6 +120,8 @@ def test_cache_backed_staged_store(lib, tmp_path):
         with lib.build_block_store(desc, extents=entry.extents(), host_mode=lib.HOST_STAGED) as st:
             x, c, cx = device_inputs(w)
             run_steps(st, x, c, cx, steps=2)
+            with pytest.raises(lib.LwoError):   # the store still reads the mapping
+                entry.close()
             for b in range(w.n_blocks):
                 hs, ss = st.block_checksum(b)
                 assert hs == ss == o_ck.extent_checksum(o_layout.pack_block(w, lwo_synth.block_tensors(w, b)))
