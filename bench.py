@@ -231,6 +231,9 @@ def main() -> int:
     ap.add_argument("--cache-dir", default=None,
                     help="with --host-mode staged: publish the stack as a flat-block file under this directory, "
                          "map it back (verified) and stream from the mapping")
+    ap.add_argument("--shard", default=None, metavar="G:R",
+                    help="one rank's share of an all-gather group of G: only shard R of every block is pinned and "
+                         "copied host -> device; the other shards stand in on the device")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of known size (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -282,8 +285,17 @@ def main() -> int:
         if b % 8 == 7 or b == L - 1:
             log(f"packed block {b + 1}/{L}")
 
+    shard = None
+    if args.shard:
+        if mixed is not None or args.host_mode != "pin_copy":
+            print("bench.py: --shard takes a one-type stack and no --host-mode", file=sys.stderr)
+            return 2
+        g, r = (int(v) for v in args.shard.split(":"))
+        shard = (g, r)
     t0 = time.perf_counter()
-    if args.host_mode == "staged":
+    if shard is not None:
+        store = lwo.build_shard_store(desc, shard[0], shard[1], fill=fill)
+    elif args.host_mode == "staged":
         pageable = []
         for b in range(L):
             buf = np.empty(ext, np.uint8)   # ordinary pageable host memory
@@ -354,8 +366,8 @@ def main() -> int:
     store.set_copy_timing(False)
     st = store.stats()
 
-    # ---- pinned H2D peak
-    peak_block = pinned_peak(torch, ext, s)
+    # ---- pinned H2D peak (copies of the size the ring issues: an extent, or a shard)
+    peak_block = pinned_peak(torch, st.shard_bytes if shard is not None else ext, s)
     peak_gib = pinned_peak(torch, 1 << 30, s, reps=5)
     peak = max(peak_block, peak_gib)
     log(f"pinned H2D peak: block-sized {peak_block:.1f} GB/s, 1 GiB {peak_gib:.1f} GB/s")
@@ -364,6 +376,8 @@ def main() -> int:
 
     m = L - k
     copies_per_step = m if m >= 3 else 0
+    if shard is not None:   # only the rank's shard crosses the host link
+        ext_of = [st.shard_bytes] * L
     bytes_per_step = sum(ext_of[k:]) if copies_per_step else 0
     h2d_gbps = bytes_per_step / (t_str * 1e-3) / 1e9 if bytes_per_step else 0.0
     t_copy = bytes_per_step / (peak_block * 1e9) * 1e3 if bytes_per_step else 0.0
@@ -438,6 +452,15 @@ def main() -> int:
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    if shard is not None:
+        cm = sorted(copy_ms)
+        out["config"]["host_mode"] = "shard"
+        out["shard"] = {"group": shard[0], "rank": shard[1], "shard_bytes": st.shard_bytes,
+                        "host_pinned_bytes": st.host_bytes, "h2d_bytes_per_step": bytes_per_step,
+                        "gather_bytes_per_step": copies_per_step * (st.slot_bytes - st.shard_bytes),
+                        "peer_device_bytes": st.peer_device_bytes,
+                        "shard_copy_ms_median": round(cm[len(cm) // 2], 4) if cm else None,
+                        "note": "the other ranks' shards come from a device region in place of the all-gather"}
     if mixed is not None:
         out["config"]["types"] = [{"heads": t.heads, "ffn": t.ffn, "linear_dtype": t.linear_dtype, "extent_bytes": e}
                                   for t, e in zip(mixed.types, text)]

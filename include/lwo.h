@@ -90,7 +90,10 @@ typedef enum lwo_status {
 
 typedef enum lwo_dtype { LWO_F32 = 0, LWO_BF16 = 1, LWO_FP8_E4M3 = 2 } lwo_dtype;
 typedef enum lwo_block_kind { LWO_KIND_DIT = 0, LWO_KIND_VIDEO = 1 } lwo_block_kind;
-typedef enum lwo_host_mode { LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1, LWO_HOST_STAGED = 2 } lwo_host_mode;
+typedef enum lwo_host_mode {
+    LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1, LWO_HOST_STAGED = 2,
+    LWO_HOST_SHARD = 3     /* one rank's share of an all-gather group (lwo_build_shard_store) */
+} lwo_host_mode;
 
 /* Shape of the block stack and of one denoise step's activations.
  * Constraints (LWO_EINVAL otherwise): n_blocks >= 1; hidden = heads * head
@@ -158,6 +161,11 @@ typedef struct lwo_stats {
     double pack_ms;              /* STAGED: host wall time spent packing (total) */
     int32_t pack_threads;        /* STAGED: threads that pack one extent */
     int32_t reserved;
+    int32_t group;               /* SHARD: all-gather group size (1 otherwise) */
+    int32_t rank;                /* SHARD: this store's rank in the group (0 otherwise) */
+    uint64_t shard_bytes;        /* SHARD: bytes of one block's shard (the extent padded to group * 4096, / group) */
+    uint64_t gather_bytes;       /* SHARD: bytes the gather stand-in copied into slots (total) */
+    uint64_t peer_device_bytes;  /* SHARD: device bytes of the region standing in for the other ranks' shards */
 } lwo_stats;
 
 /* --- layout and packing (host only, no GPU needed) ---------------------- */
@@ -296,6 +304,35 @@ lwo_status lwo_build_block_store(const lwo_model_desc* desc, const lwo_block_sou
 lwo_status lwo_build_mixed_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type,
                                  int32_t n_blocks, const lwo_block_source* src, int32_t host_mode,
                                  uint64_t register_budget, int32_t device, lwo_store** out);
+
+/* [DLO] "AllGather path" and "Host backing and transfer composition" (the
+ * row for ordinary runtime tensors with a group larger than one): one rank's
+ * share of the sharded ring, on one GPU.  Each block's extent is padded with
+ * zeros to a multiple of group * 4096 bytes (shard_bytes = padded / group;
+ * shards cut across tensor boundaries) and rank `rank` keeps only shard
+ * `rank` of every block in pinned host memory: about extent / group bytes
+ * per block.  The ring is lwo_build_block_store's, with one change per
+ * streamed block: the copy stream copies the rank's shard host -> device to
+ * its offset rank * shard_bytes of the slot, and a second (gather) stream
+ * waits for that copy and then completes the slot with the other group - 1
+ * shards, the all-gather's result.  On one GPU the shards the peers would
+ * send over the all-gather come from a device region holding them
+ * (peer_device_bytes = n_blocks * (padded - shard_bytes)), copied device to
+ * device; the compute stream waits for the gather's event exactly as it
+ * waits for a whole-block copy.  Host -> device bytes per step are thus
+ * n_streamed * shard_bytes (lwo_stats.h2d_bytes counts those only;
+ * gather_bytes the rest).  With group 1 the one shard is the whole extent and
+ * nothing is gathered.
+ *   src: the caller's extents (read during the call) or fill (called once per
+ *        block, in order, with a scratch extent of extent_bytes), as for
+ *        PIN_COPY; each extent is read once, checksummed for validation and
+ *        split.
+ *   LWO_EINVAL: group outside [1, 64], rank outside [0, group), or as
+ *   lwo_build_block_store.  Everything else (resident prefix, validation,
+ *   timing, stats, destroy) works as for the other host modes; copy timing
+ *   covers the shard's host -> device copy. */
+lwo_status lwo_build_shard_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t group,
+                                 int32_t rank, int32_t device, lwo_store** out);
 
 /* [DLO] "Feature compatibility" (resident leading layers): keep blocks
  * 0..k-1 in a device-resident region and stream blocks k..n_blocks-1

@@ -29,7 +29,7 @@ _lib = C.CDLL(LIB_PATH)
 # enums (include/lwo.h)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KIND_DIT, KIND_VIDEO = 0, 1
-HOST_PIN_COPY, HOST_REGISTER, HOST_STAGED = 0, 1, 2
+HOST_PIN_COPY, HOST_REGISTER, HOST_STAGED, HOST_SHARD = 0, 1, 2, 3
 STATUS = {0: "LWO_OK", 1: "LWO_EINVAL", 2: "LWO_ENOMEM", 3: "LWO_EHIP", 4: "LWO_EBUDGET",
           5: "LWO_EREGISTER", 6: "LWO_EROLLBACK", 7: "LWO_ESTATE", 8: "LWO_ECHECKSUM", 9: "LWO_ETIMEOUT",
           10: "LWO_EIO"}
@@ -69,7 +69,9 @@ class _Stats(C.Structure):
                                           "registered_ranges", "registered_bytes")] + \
                [(n, C.c_int32) for n in ("resident_prefix", "head_slot", "host_mode", "validation")] + \
                [("build_ms", C.c_double), ("staging_bytes", C.c_uint64), ("pack_bytes", C.c_uint64),
-                ("pack_ms", C.c_double), ("pack_threads", C.c_int32), ("reserved", C.c_int32)]
+                ("pack_ms", C.c_double), ("pack_threads", C.c_int32), ("reserved", C.c_int32),
+                ("group", C.c_int32), ("rank", C.c_int32), ("shard_bytes", C.c_uint64), ("gather_bytes", C.c_uint64),
+                ("peer_device_bytes", C.c_uint64)]
 
 
 class _KStat(C.Structure):
@@ -97,6 +99,8 @@ _lib_build = _sig("lwo_build_block_store", C.c_int, C.POINTER(_Desc), C.POINTER(
                   C.c_int32, C.POINTER(_P))
 _lib_build_mixed = _sig("lwo_build_mixed_store", C.c_int, C.POINTER(_Desc), C.c_int32, C.POINTER(C.c_int32), C.c_int32,
                         C.POINTER(_Source), C.c_int32, C.c_uint64, C.c_int32, C.POINTER(_P))
+_lib_build_shard = _sig("lwo_build_shard_store", C.c_int, C.POINTER(_Desc), C.POINTER(_Source), C.c_int32, C.c_int32,
+                        C.c_int32, C.POINTER(_P))
 _lib_set_prefix = _sig("lwo_set_resident_prefix", C.c_int, _P, C.c_int32)
 _lib_run = _sig("lwo_run_denoise_step", C.c_int, _P, _P, _P, _P, _P)
 _lib_set_validation = _sig("lwo_set_validation", C.c_int, _P, C.c_int32)
@@ -124,7 +128,7 @@ _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, 
 _lib_probe_mfma = _sig("lwo_probe_mfma", C.c_int, _I, _I, _I, _P, C.c_uint64, _P, C.POINTER(C.c_double))
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_tile_weight", "lwo_extent_checksum", "lwo_register_ranges",
-            "lwo_build_block_store", "lwo_build_mixed_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
+            "lwo_build_block_store", "lwo_build_mixed_store", "lwo_build_shard_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
             "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
@@ -297,6 +301,11 @@ class Stats:
     pack_ms: float
     pack_threads: int
     reserved: int
+    group: int
+    rank: int
+    shard_bytes: int
+    gather_bytes: int
+    peer_device_bytes: int
 
 
 class Store:
@@ -509,3 +518,13 @@ def build_mixed_store(types, block_type, extents=None, fill=None, host_mode: int
                             C.byref(h)))
     n_desc = dataclasses.replace(types[0], n_blocks=len(bt))
     return Store(h, n_desc, keepalive=keep if host_mode in (HOST_REGISTER, HOST_STAGED) else None)
+
+
+def build_shard_store(desc: ModelDesc, group: int, rank: int, extents=None, fill=None, device: int = 0) -> Store:
+    """One rank's share of an all-gather group (see lwo_build_shard_store): only shard `rank` of every block is
+    pinned on the host; the other shards stand in on the device for what the all-gather would bring."""
+    src, keep = _source(extents, fill)
+    h = C.c_void_p()
+    _check(_lib_build_shard(C.byref(desc._c()), C.byref(src), group, rank, device, C.byref(h)))
+    del keep
+    return Store(h, desc)

@@ -24,6 +24,15 @@
 //    two bounded pinned host staging slots and copied from there; a zero
 //    registration budget or a failed (rolled back) registration keeps that
 //    staging path.
+//  * "Distributed Layerwise Offload", "AllGather path" and "Host backing and
+//    transfer composition" (ordinary runtime tensors, group larger than one):
+//    each rank keeps about 1/group of every streamed block pinned, copies its
+//    shard of the next block to the device, and the group's all-gather on a
+//    communication stream completes the slot while the current block runs.
+//    SHARD mode is one rank's share of that on one GPU: the rank's shard is
+//    the only host memory and the only host -> device copy; the other shards,
+//    which the all-gather would bring from the peers, come from a device
+//    region that stands in for them (copied on a separate gather stream).
 #include <algorithm>
 #include <chrono>
 #include <condition_variable>
@@ -102,8 +111,16 @@ struct lwo_store {
     std::vector<Layout> tlay;             // per block type
     std::vector<int> btype;               // per block: its type
     std::vector<uint64_t> bext;           // per block: extent bytes of its type
-    std::vector<uint64_t> roff;           // per block: offset in the resident region (prefix sums of bext)
-    uint64_t max_ext = 0;                 // slot and staging size
+    std::vector<uint64_t> dext;           // per block: device bytes (bext, or the shard-padded extent)
+    std::vector<uint64_t> roff;           // per block: offset in the resident region (prefix sums of dext)
+    uint64_t max_ext = 0;                 // slot and staging size (largest dext)
+    // SHARD: this rank's share of an all-gather group
+    int group = 1, rank = 0;
+    uint64_t shard = 0;                   // bytes of one shard (dext / group)
+    char* peer = nullptr;                 // device: per block the group-1 other shards, back to back
+    hipStream_t gather = nullptr;         // stand-in for the communication stream
+    hipEvent_t shard_done[2] = {nullptr, nullptr};
+    uint64_t gather_bytes = 0;
     int device = 0;
     int host_mode = LWO_HOST_PIN_COPY;    // mode in effect
     std::vector<void*> host;              // per-block host extent
@@ -217,6 +234,7 @@ static void release(lwo_store* s) {
     if (!s) return;
     (void)hipSetDevice(s->device);
     if (s->copy) (void)hipStreamSynchronize(s->copy);
+    if (s->gather) (void)hipStreamSynchronize(s->gather);
     (void)hipDeviceSynchronize();   // compute that may still read a slot runs on caller streams
     if (s->host_mode == LWO_HOST_REGISTER) {
         for (size_t i = s->reg_base.size(); i-- > 0;) (void)hipHostUnregister((void*)(uintptr_t)s->reg_base[i]);
@@ -241,6 +259,10 @@ static void release(lwo_store* s) {
     for (hipEvent_t e : s->step_done)
         if (e) (void)hipEventDestroy(e);
     if (s->resident) (void)hipFree(s->resident);
+    if (s->peer) (void)hipFree(s->peer);
+    for (hipEvent_t e : s->shard_done)
+        if (e) (void)hipEventDestroy(e);
+    if (s->gather) (void)hipStreamDestroy(s->gather);
     s->kt.destroy();
     workspace_free(&s->ws);
     if (s->copy) (void)hipStreamDestroy(s->copy);
@@ -249,12 +271,16 @@ static void release(lwo_store* s) {
 
 // ------------------------------------------------------------------ helpers
 
-// Enqueue the host -> device copy of block b's extent into dst on the copy
-// stream (optional timing events around the device copy only).  STAGED: wait
-// until the device copy last issued from the next staging slot is done (the
-// host is about to overwrite it), pack the pageable extent into it, then copy.
-static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
-    const uint64_t ext = s->bext[b];
+// Enqueue the transfer of block b into dst (device, dext[b] bytes) and record
+// `done` on the stream that finishes it (optional timing events around the
+// host -> device copy only).  STAGED: wait until the device copy last issued
+// from the next staging slot is done (the host is about to overwrite it), pack
+// the pageable extent into it, then copy.  SHARD: copy this rank's pinned
+// shard to its offset of dst on the copy stream; the gather stream waits for
+// it and copies the other shards from the peer region around it.
+static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t done, hipEvent_t t0 = nullptr,
+                            hipEvent_t t1 = nullptr) {
+    const uint64_t ext = s->host_mode == LWO_HOST_SHARD ? s->shard : s->bext[b];
     const char* src = (const char*)s->host[b];
     int q = -1;
     if (s->host_mode == LWO_HOST_STAGED) {
@@ -267,8 +293,9 @@ static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t t0 = null
         s->pack_bytes += ext;
         src = s->stage[q];
     }
+    char* at = s->host_mode == LWO_HOST_SHARD ? dst + (uint64_t)s->rank * s->shard : dst;
     if (t0) LWO_HIP_TRY(hipEventRecord(t0, s->copy));
-    LWO_HIP_TRY(hipMemcpyAsync(dst, src, ext, hipMemcpyHostToDevice, s->copy));
+    LWO_HIP_TRY(hipMemcpyAsync(at, src, ext, hipMemcpyHostToDevice, s->copy));
     if (t1) LWO_HIP_TRY(hipEventRecord(t1, s->copy));
     if (q >= 0) {
         LWO_HIP_TRY(hipEventRecord(s->stage_done[q], s->copy));
@@ -276,6 +303,27 @@ static lwo_status h2d_block(lwo_store* s, char* dst, int b, hipEvent_t t0 = null
     }
     s->h2d_copies++;
     s->h2d_bytes += ext;
+    if (s->host_mode != LWO_HOST_SHARD || s->group == 1) {
+        if (done) LWO_HIP_TRY(hipEventRecord(done, s->copy));
+        return LWO_OK;
+    }
+    // The all-gather stand-in: shards [0, rank) and (rank, group) of block b.
+    const int sl = (dst == s->slot[1]) ? 1 : 0;
+    LWO_HIP_TRY(hipEventRecord(s->shard_done[sl], s->copy));
+    LWO_HIP_TRY(hipStreamWaitEvent(s->gather, s->shard_done[sl], 0));
+    const uint64_t below = (uint64_t)s->rank * s->shard, above = s->dext[b] - below - s->shard;
+    const char* pb = s->peer + (uint64_t)b * (s->dext[b] - s->shard);
+    if (below) LWO_HIP_TRY(hipMemcpyAsync(dst, pb, below, hipMemcpyDeviceToDevice, s->gather));
+    if (above) LWO_HIP_TRY(hipMemcpyAsync(dst + below + s->shard, pb + below, above, hipMemcpyDeviceToDevice, s->gather));
+    s->gather_bytes += below + above;
+    if (done) LWO_HIP_TRY(hipEventRecord(done, s->gather));
+    return LWO_OK;
+}
+
+// Wait on the host until every transfer stream of the store has drained.
+static lwo_status sync_transfers(lwo_store* s) {
+    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    if (s->gather) LWO_HIP_TRY(hipStreamSynchronize(s->gather));
     return LWO_OK;
 }
 
@@ -284,8 +332,7 @@ static lwo_status prime_head(lwo_store* s) {
     s->head_slot = 0;
     s->slot_block[0] = s->slot_block[1] = -1;
     if (s->k >= s->d.n_blocks) return LWO_OK;
-    LWO_TRY(h2d_block(s, s->slot[0], s->k));
-    LWO_HIP_TRY(hipEventRecord(s->copy_done[0], s->copy));
+    LWO_TRY(h2d_block(s, s->slot[0], s->k, s->copy_done[0]));
     s->slot_block[0] = s->k;
     return LWO_OK;
 }
@@ -313,6 +360,7 @@ static lwo_status check_store(lwo_store* s) {
 // ------------------------------------------------------------------ build
 
 static lwo_status build_staged(lwo_store* s, const lwo_block_source* src);
+static lwo_status build_shard(lwo_store* s, const lwo_block_source* src);
 static lwo_status build_device(lwo_store* s);
 
 static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uint64_t budget) {
@@ -337,6 +385,8 @@ static lwo_status build(lwo_store* s, const lwo_block_source* src, int mode, uin
                 return LWO_EINVAL;
             }
         }
+    } else if (mode == LWO_HOST_SHARD) {
+        return build_shard(s, src);
     } else if (mode == LWO_HOST_REGISTER && budget > 0) {
         if (!src->extents) { set_error("REGISTER mode needs caller extents"); return LWO_EINVAL; }
         const uint64_t page = 4096;
@@ -395,6 +445,59 @@ static lwo_status build_staged(lwo_store* s, const lwo_block_source* src) {
     return build_device(s);
 }
 
+// SHARD: read each block's whole extent once (from the caller's extents or the
+// fill callback, into a pinned scratch extent padded with zeros to the shard
+// multiple), checksum it, keep this rank's shard in pinned host memory and
+// place the other shards in the peer region on the device.
+static lwo_status build_shard(lwo_store* s, const lwo_block_source* src) {
+    const int n = s->d.n_blocks;
+    const uint64_t dx = s->dext[0], sh = s->shard, ext = s->bext[0];
+    s->host_owned = true;   // the shards allocated so far are released on failure
+    char* tmp = nullptr;
+    if (hipHostMalloc((void**)&tmp, dx, hipHostMallocDefault) != hipSuccess || !tmp) {
+        set_error("hipHostMalloc of the shard build's scratch extent failed");
+        return LWO_ENOMEM;
+    }
+    struct Free { char* p; ~Free() { if (p) (void)hipHostFree(p); } } guard{tmp};
+    if (s->group > 1) {
+        const uint64_t bytes = (uint64_t)n * (dx - sh);
+        if (hipMalloc(&s->peer, bytes) != hipSuccess) {
+            s->peer = nullptr;
+            set_error("hipMalloc of the peer-shard region (" + std::to_string(bytes) + " bytes) failed");
+            return LWO_ENOMEM;
+        }
+        LWO_HIP_TRY(hipStreamCreateWithFlags(&s->gather, hipStreamNonBlocking));
+        for (hipEvent_t& e : s->shard_done) LWO_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    }
+    s->host_sums.assign(n, 0);
+    for (int b = 0; b < n; ++b) {
+        if (src->extents) {
+            if (!src->extents[b]) { set_error("extent " + std::to_string(b) + " is NULL"); return LWO_EINVAL; }
+            std::memcpy(tmp, src->extents[b], ext);
+        } else if (src->fill(src->user, b, tmp, ext) != 0) {
+            set_error("fill callback failed for block " + std::to_string(b));
+            return LWO_EINVAL;
+        }
+        std::memset(tmp + ext, 0, dx - ext);
+        s->host_sums[b] = extent_checksum_host(tmp, ext);
+        void* p = nullptr;
+        if (hipHostMalloc(&p, sh, hipHostMallocDefault) != hipSuccess || !p) {
+            set_error("hipHostMalloc of shard " + std::to_string(b) + " (" + std::to_string(sh) + " bytes) failed");
+            return LWO_ENOMEM;
+        }
+        s->host[b] = p;
+        const uint64_t below = (uint64_t)s->rank * sh;
+        std::memcpy(p, tmp + below, sh);
+        if (s->group > 1) {
+            char* pb = s->peer + (uint64_t)b * (dx - sh);
+            if (below) LWO_HIP_TRY(hipMemcpy(pb, tmp, below, hipMemcpyHostToDevice));
+            if (dx - below - sh) LWO_HIP_TRY(hipMemcpy(pb + below, tmp + below + sh, dx - below - sh, hipMemcpyHostToDevice));
+        }
+    }
+    s->sums_ready = true;
+    return build_device(s);
+}
+
 // Device arena, workspace, copy stream and events; prime the head block.
 static lwo_status build_device(lwo_store* s) {
     const uint64_t ext = s->max_ext;
@@ -407,14 +510,14 @@ static lwo_status build_device(lwo_store* s) {
     LWO_HIP_TRY(hipStreamCreateWithFlags(&s->copy, hipStreamNonBlocking));
     for (hipEvent_t& e : s->step_done) LWO_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     LWO_TRY(prime_head(s));
-    LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+    LWO_TRY(sync_transfers(s));
     return LWO_OK;
 }
 
-// Shared by both build calls: block b has descriptor types[block_type[b]].
+// Shared by the build calls: block b has descriptor types[block_type[b]].
 static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, const int32_t* block_type, int32_t n_blocks,
                               const lwo_block_source* src, int32_t host_mode, uint64_t register_budget,
-                              int32_t device, lwo_store** out) {
+                              int32_t device, lwo_store** out, int32_t group = 1, int32_t rank = 0) {
     if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
     *out = nullptr;
     if (!types || n_types < 1 || !block_type || n_blocks < 1) { set_error("stack: types, block_type and n_blocks >= 1 required"); return LWO_EINVAL; }
@@ -433,8 +536,13 @@ static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, cons
     for (int b = 0; b < n_blocks; ++b)
         if (block_type[b] < 0 || block_type[b] >= n_types) { set_error("block_type[" + std::to_string(b) + "] out of range"); return LWO_EINVAL; }
     if (!src || (!src->extents && !src->fill)) { set_error("block source has neither extents nor fill"); return LWO_EINVAL; }
-    if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER && host_mode != LWO_HOST_STAGED) {
+    if (host_mode != LWO_HOST_PIN_COPY && host_mode != LWO_HOST_REGISTER && host_mode != LWO_HOST_STAGED &&
+        host_mode != LWO_HOST_SHARD) {
         set_error("host_mode");
+        return LWO_EINVAL;
+    }
+    if (host_mode == LWO_HOST_SHARD && (n_types != 1 || group < 1 || group > 64 || rank < 0 || rank >= group)) {
+        set_error("shard store: one block type, 1 <= group <= 64 and 0 <= rank < group required");
         return LWO_EINVAL;
     }
     int ndev = 0;
@@ -459,10 +567,16 @@ static lwo_status build_store(const lwo_model_desc* types, int32_t n_types, cons
         uint64_t off = 0;
         for (int b = 0; b < n_blocks; ++b) {
             s->bext.push_back(s->tlay[block_type[b]].extent_bytes);
+            // SHARD: the extent padded to group equal shards of whole pages
+            const uint64_t unit = (uint64_t)group * 4096;
+            s->dext.push_back(host_mode == LWO_HOST_SHARD ? (s->bext[b] + unit - 1) / unit * unit : s->bext[b]);
             s->roff.push_back(off);
-            off += s->bext[b];
-            s->max_ext = std::max(s->max_ext, s->bext[b]);
+            off += s->dext[b];
+            s->max_ext = std::max(s->max_ext, s->dext[b]);
         }
+        s->group = group;
+        s->rank = rank;
+        s->shard = s->dext[0] / group;
         s->device = device;
         s->host_mode = host_mode;
         st = build(s, src, host_mode, register_budget);
@@ -518,6 +632,24 @@ extern "C" lwo_status lwo_build_mixed_store(const lwo_model_desc* types, int32_t
     }
 }
 
+extern "C" lwo_status lwo_build_shard_store(const lwo_model_desc* desc, const lwo_block_source* src, int32_t group,
+                                            int32_t rank, int32_t device, lwo_store** out) {
+    try {
+        clear_error();
+        if (!out) { set_error("out is NULL"); return LWO_EINVAL; }
+        *out = nullptr;
+        LWO_TRY(validate_desc(desc));
+        std::vector<int32_t> bt(desc->n_blocks, 0);
+        return build_store(desc, 1, bt.data(), desc->n_blocks, src, LWO_HOST_SHARD, 0, device, out, group, rank);
+    } catch (const std::bad_alloc&) {
+        return fail_alloc("lwo_build_shard_store");
+    } catch (const std::exception& e) {
+        return fail_exception("lwo_build_shard_store", e.what());
+    } catch (...) {
+        return fail_exception("lwo_build_shard_store", "unknown exception");
+    }
+}
+
 extern "C" lwo_status lwo_destroy_block_store(lwo_store* s) {
     try {
         clear_error();
@@ -540,24 +672,24 @@ extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
         LWO_TRY(check_store(s));
         if (k < 0 || k > s->d.n_blocks) { set_error("resident prefix out of range"); return LWO_EINVAL; }
         LWO_HIP_TRY(hipSetDevice(s->device));
-        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        LWO_TRY(sync_transfers(s));
         LWO_HIP_TRY(hipDeviceSynchronize());
         char* region = nullptr;
         if (k > 0) {
-            const uint64_t bytes = s->roff[k - 1] + s->bext[k - 1];
+            const uint64_t bytes = s->roff[k - 1] + s->dext[k - 1];
             if (hipMalloc(&region, bytes) != hipSuccess) {
                 set_error("hipMalloc of the resident region (" + std::to_string(bytes) + " bytes) failed");
                 return LWO_ENOMEM;   // previous prefix stays in effect
             }
             for (int b = 0; b < k; ++b) {
-                if (h2d_block(s, region + s->roff[b], b) != LWO_OK) {
-                    (void)hipStreamSynchronize(s->copy);
+                if (h2d_block(s, region + s->roff[b], b, nullptr) != LWO_OK) {
+                    (void)sync_transfers(s);
                     (void)hipFree(region);
                     set_error("copy of resident block " + std::to_string(b) + " failed");
                     return LWO_EHIP;
                 }
             }
-            if (hipStreamSynchronize(s->copy) != hipSuccess) {
+            if (sync_transfers(s) != LWO_OK) {
                 (void)hipFree(region);
                 set_error("copy of the resident prefix failed");
                 return LWO_EHIP;
@@ -567,7 +699,7 @@ extern "C" lwo_status lwo_set_resident_prefix(lwo_store* s, int32_t k) {
         s->resident = region;
         s->k = k;
         LWO_TRY(prime_head(s));
-        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        LWO_TRY(sync_transfers(s));
         return LWO_OK;
     } catch (const std::bad_alloc&) {
         return fail_alloc("lwo_set_resident_prefix");
@@ -627,8 +759,7 @@ static lwo_status run_step(lwo_store* s, void* x, const void* cond, const void* 
                         s->tev.push_back(e1);
                         s->n_timed++;
                     }
-                    LWO_TRY(h2d_block(s, s->slot[nxt], nb, e0, e1));
-                    LWO_HIP_TRY(hipEventRecord(s->copy_done[nxt], s->copy));
+                    LWO_TRY(h2d_block(s, s->slot[nxt], nb, s->copy_done[nxt], e0, e1));
                     s->slot_block[nxt] = nb;
                 }
             }
@@ -719,7 +850,7 @@ extern "C" lwo_status lwo_copy_times(lwo_store* s, float* ms, int32_t cap, int32
         clear_error();
         LWO_TRY(check_store(s));
         LWO_HIP_TRY(hipSetDevice(s->device));
-        LWO_HIP_TRY(hipStreamSynchronize(s->copy));
+        LWO_TRY(sync_transfers(s));
         int cnt = s->n_timed;
         if (n) *n = cnt;
         for (int i = 0; i < cnt && i < cap && ms; ++i)
@@ -751,8 +882,8 @@ extern "C" lwo_status lwo_block_checksum(lwo_store* s, int32_t block, uint64_t* 
         } else {
             // borrow the slot the ring is not about to read
             int sl = 1 - s->head_slot;
-            LWO_TRY(h2d_block(s, s->slot[sl], block));
-            LWO_HIP_TRY(hipEventRecord(s->copy_done[sl], s->copy));
+            LWO_TRY(h2d_block(s, s->slot[sl], block, s->copy_done[sl]));
+            LWO_HIP_TRY(hipStreamWaitEvent(s->copy, s->copy_done[sl], 0));
             s->slot_block[sl] = block;
             base = s->slot[sl];
         }
@@ -833,9 +964,15 @@ extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
         for (uint64_t e : s->bext) all += e;
         o->extent_bytes = ext;
         o->slot_bytes = ext;
-        o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->bext[s->k - 1] : 0);
+        o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->dext[s->k - 1] : 0);
         o->workspace_bytes = s->ws.bytes;
-        o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0 : all;
+        o->host_bytes = s->host_mode == LWO_HOST_STAGED ? 0
+                        : s->host_mode == LWO_HOST_SHARD ? (uint64_t)s->d.n_blocks * s->shard : all;
+        o->group = s->group;
+        o->rank = s->rank;
+        o->shard_bytes = s->host_mode == LWO_HOST_SHARD ? s->shard : 0;
+        o->gather_bytes = s->gather_bytes;
+        o->peer_device_bytes = s->peer ? (uint64_t)s->d.n_blocks * (s->dext[0] - s->shard) : 0;
         o->staging_bytes = s->host_mode == LWO_HOST_STAGED ? 2 * ext : 0;
         o->pack_bytes = s->pack_bytes;
         o->pack_ms = s->pack_ms;

@@ -291,3 +291,20 @@ def test_build_rejects_scratch_in_asm_read_kernels():
     ])
     bad = b._scratch_users(text)
     assert len(bad) == 1 and "k_attn_tr" in bad[0] and "16 bytes" in bad[0]
+
+
+def test_shard_build_validation_before_device(lib):
+    """Shard stores: a group outside [1, 64] or a rank outside [0, group) fails
+    with LWO_EINVAL before any device call; valid arguments get as far as the
+    device check."""
+    w = lwo_synth.get("dit_tiny_fp32")
+    desc = lib.ModelDesc.from_workload(w)
+    src = [np.zeros(8, np.uint8)] * w.n_blocks
+    for g, r in [(0, 0), (65, 0), (2, 2), (3, -1)]:
+        with pytest.raises(lib.LwoError) as e:
+            lib.build_shard_store(desc, g, r, extents=src)
+        assert e.value.status == 1 and "shard" in str(e.value), (g, r, str(e.value))
+    if not os.path.exists("/dev/kfd"):
+        with pytest.raises(lib.LwoError) as e:
+            lib.build_shard_store(desc, 4, 3, extents=src)
+        assert "device" in str(e.value)
