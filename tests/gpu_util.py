@@ -117,12 +117,20 @@ def build_with_oracle(lwo, w, fp8_act: bool = False):
 
 
 def row_col_errors(got: np.ndarray, want: np.ndarray):
-    """Largest relative L2 error of any token row and of any feature column of
-    [..., D] outputs (rows = every leading index).  A wrong row or column
-    shows an O(1) error there even when the whole-tensor figure hides it."""
+    """Largest error of any token row and of any feature column of [..., D]
+    outputs (rows = every leading index), each relative to a typical row or
+    column: a row's L2 error over that row's own norm (rows are alike), and a
+    column's L2 error over the root-mean-square column norm of the whole
+    tensor.  Columns are not alike: the residual stream's columns carry a
+    value shared by every row (most of a column's norm deep in a stack), so
+    a column whose shared value is near zero has a small norm of its own and
+    a large error relative to it, while its error is ordinary.  A wrong row or
+    column shows an error of order 1 under either measure, even when the
+    whole-tensor figure hides it."""
     g = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
     r = np.asarray(want, np.float64).reshape(-1, want.shape[-1])
     d = g - r
     rows = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)
-    cols = np.linalg.norm(d, axis=0) / np.maximum(np.linalg.norm(r, axis=0), 1e-300)
+    col_rms = max(np.linalg.norm(r) / np.sqrt(r.shape[1]), 1e-300)
+    cols = np.linalg.norm(d, axis=0) / col_rms
     return float(rows.max()), float(cols.max())

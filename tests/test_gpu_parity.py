@@ -3,14 +3,16 @@ streamed == resident bit for bit, slot bytes == host bytes.
 
 Tolerances (relative L2 over the whole output, float64).  Every token row is
 also held to 1.5 times the output bound and every feature column to 5 times
-it, so that a wrong row or column, which the whole-tensor figure can hide,
-fails (its error is of order 1).  Rows are alike (the worst row measures
-1.1 times the whole tensor); columns are not: where a linear's input column is
-dominated by a per-column shift, it rounds the same way in every row and its
-error does not average out, so a few columns carry 3-4 times the whole
-tensor's error.  The oracle with emulated fp8 activations shows the same
-against the plain oracle (worst column 0.14-0.17 against 0.042 on a video
-block), so this is the arithmetic, not the kernels.
+it (a column's error relative to the tensor's root-mean-square column norm,
+tests/gpu_util.row_col_errors), so that a wrong row or column, which the
+whole-tensor figure can hide, fails (its error is of order 1).  Rows are alike
+(the worst row measures 1.1 times the whole tensor); columns are not: where a
+linear's input column is dominated by a per-column shift, it rounds the same
+way in every row and its error does not average out, so a few columns carry
+3-4 times the whole tensor's error.  The oracle with emulated fp8 activations
+shows the same against the plain oracle (worst column 0.155-0.183 against
+0.042-0.045 over 1-20 blocks of the 256-token video stack), so this is the
+arithmetic, not the kernels.
   * fp32 workloads: 1e-4 on x_out and on the block-stack update x_out - x_in
     (fp32 accumulation over K <= 4608 gives ~1e-6; the bound is the stated one);
   * bf16 workloads: 2e-2 on x_out (the stated bound) and 3e-2 on the update:
