@@ -960,9 +960,9 @@ extern "C" lwo_status lwo_get_stats(lwo_store* s, lwo_stats* o) {
         LWO_HIP_TRY(hipDeviceSynchronize());
         std::memset(o, 0, sizeof(*o));
         const uint64_t ext = s->max_ext;
-        uint64_t all = 0;
-        for (uint64_t e : s->bext) all += e;
-        o->extent_bytes = ext;
+        uint64_t all = 0, big = 0;
+        for (uint64_t e : s->bext) { all += e; big = std::max(big, e); }
+        o->extent_bytes = big;
         o->slot_bytes = ext;
         o->device_weight_bytes = 2 * ext + (s->k ? s->roff[s->k - 1] + s->dext[s->k - 1] : 0);
         o->workspace_bytes = s->ws.bytes;
