@@ -368,6 +368,28 @@ lwo_status lwo_set_resident_prefix(lwo_store* store, int32_t k);
 lwo_status lwo_run_denoise_step(lwo_store* store, void* x, const void* cond, const void* ctx,
                                 void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * denoise step over n_blocks device-resident block extents, with the same
+ * kernels, in the same order, as lwo_run_denoise_step with every block
+ * resident, and no allocation of any kind on the device.
+ *   blocks  n_blocks device pointers (256-byte aligned), block b's extent in
+ *           the layout of lwo_block_layout(desc) (e.g. lwo_pack_block's bytes
+ *           copied to the device); caller-owned, read only;
+ *   x, cond, ctx as for lwo_run_denoise_step (x updated in place);
+ *   hip_stream a non-null stream; the call runs on that stream's device.
+ * The step's activation workspace lives in a file-scope device array of
+ * LWO_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  Every call on one GPU uses that GPU's one array
+ * and leaves its contents behind: calls that overlap on one GPU (two streams,
+ * or two threads) race and corrupt each other's results; serialise them.
+ * LWO_EINVAL if the descriptor's workspace (it grows with batch * tokens *
+ * max(3 * hidden, ffn)) exceeds the array, for a bad pointer or a NULL
+ * stream, before anything is enqueued.  Nothing is synchronised. */
+#define LWO_NOALLOC_SCRATCH_BYTES (64ull << 20)
+lwo_status lwo_run_blocks_noalloc(const lwo_model_desc* desc, const void* const* blocks, int32_t n_blocks, void* x,
+                                  const void* cond, const void* ctx, void* hip_stream);
+
 /* Set the pacing depth of lwo_run_denoise_step (1..16, or 0 for no host
  * wait at all). */
 lwo_status lwo_set_max_inflight(lwo_store* store, int32_t max_inflight);

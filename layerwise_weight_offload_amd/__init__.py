@@ -16,5 +16,5 @@ from ._binding import (  # noqa: F401
     LwoError, ModelDesc, Stats, Store, block_layout, build_block_store, extent_checksum, last_error,
     pack_block, register_ranges, exported_symbols, op_attention, op_layernorm, op_linear, op_quantize_rows,
     op_rmsnorm_qk, probe_mfma, sha256, cache_publish, cache_open, CacheEntry, CacheExtents, build_mixed_store,
-    build_shard_store, tile_weight,
+    build_shard_store, tile_weight, run_blocks_noalloc, NOALLOC_SCRATCH_BYTES,
 )

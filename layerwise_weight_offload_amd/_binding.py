@@ -101,6 +101,8 @@ _lib_build_mixed = _sig("lwo_build_mixed_store", C.c_int, C.POINTER(_Desc), C.c_
                         C.POINTER(_Source), C.c_int32, C.c_uint64, C.c_int32, C.POINTER(_P))
 _lib_build_shard = _sig("lwo_build_shard_store", C.c_int, C.POINTER(_Desc), C.POINTER(_Source), C.c_int32, C.c_int32,
                         C.c_int32, C.POINTER(_P))
+_lib_run_noalloc = _sig("lwo_run_blocks_noalloc", C.c_int, C.POINTER(_Desc), C.POINTER(C.c_void_p), C.c_int32, _P, _P,
+                        _P, _P)
 _lib_set_prefix = _sig("lwo_set_resident_prefix", C.c_int, _P, C.c_int32)
 _lib_run = _sig("lwo_run_denoise_step", C.c_int, _P, _P, _P, _P, _P)
 _lib_set_validation = _sig("lwo_set_validation", C.c_int, _P, C.c_int32)
@@ -128,7 +130,7 @@ _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, 
 _lib_probe_mfma = _sig("lwo_probe_mfma", C.c_int, _I, _I, _I, _P, C.c_uint64, _P, C.POINTER(C.c_double))
 
 EXPORTED = ["lwo_block_layout", "lwo_pack_block", "lwo_tile_weight", "lwo_extent_checksum", "lwo_register_ranges",
-            "lwo_build_block_store", "lwo_build_mixed_store", "lwo_build_shard_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_set_max_inflight",
+            "lwo_build_block_store", "lwo_build_mixed_store", "lwo_build_shard_store", "lwo_set_resident_prefix", "lwo_run_denoise_step", "lwo_run_blocks_noalloc", "lwo_set_max_inflight",
             "lwo_set_validation",
             "lwo_block_checksum", "lwo_set_copy_timing", "lwo_copy_times", "lwo_set_kernel_timing",
             "lwo_kernel_stats", "lwo_get_stats", "lwo_op_linear", "lwo_op_attention", "lwo_op_layernorm",
@@ -528,3 +530,14 @@ def build_shard_store(desc: ModelDesc, group: int, rank: int, extents=None, fill
     _check(_lib_build_shard(C.byref(desc._c()), C.byref(src), group, rank, device, C.byref(h)))
     del keep
     return Store(h, desc)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def run_blocks_noalloc(desc: ModelDesc, blocks, x: int, cond: int, ctx: int | None, stream: int) -> None:
+    """One step over device-resident extents (device addresses) with no device allocation
+    (see lwo_run_blocks_noalloc)."""
+    arr = (C.c_void_p * max(len(blocks), 1))(*[int(b) for b in blocks])
+    _check(_lib_run_noalloc(C.byref(desc._c()), arr, len(blocks), C.c_void_p(x), C.c_void_p(cond),
+                            C.c_void_p(ctx) if ctx else None, C.c_void_p(stream)))

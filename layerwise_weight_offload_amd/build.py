@@ -23,7 +23,8 @@ OUT = os.path.join(HERE, "liblwo.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["layout.cpp", "store.cpp", "cache.cpp", "ops.cpp", "block.hip", "k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_probe.hip"]
+SOURCES = ["layout.cpp", "store.cpp", "cache.cpp", "ops.cpp", "block.hip", "k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_probe.hip",
+           "noalloc.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -18,7 +18,8 @@ namespace lwo {
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
+// Lay the workspace out from `base` (nullptr: only size it); returns its bytes.
+size_t workspace_carve(const lwo_model_desc& d, void* base, Workspace* ws) {
     const size_t M = (size_t)d.batch * d.tokens, D = d.hidden, F = d.ffn;
     const size_t Mc = (size_t)d.batch * d.ctx_tokens;
     const size_t ae = dtype_bytes(d.act_dtype);
@@ -32,11 +33,7 @@ lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
     const size_t o_q8 = fp8 ? take(M * std::max(D, F)) : 0, o_q8s = fp8 ? take(std::max(M, Mc) * 4) : 0;
     const size_t o_c8 = fp8 ? take(Mc * D) : 0, o_c8s = fp8 ? take(Mc * 4) : 0;
     const size_t o_sums = take(16);
-    void* base = nullptr;
-    if (hipMalloc(&base, off) != hipSuccess) {
-        set_error("hipMalloc of the activation workspace (" + std::to_string(off) + " bytes) failed");
-        return LWO_ENOMEM;
-    }
+    if (!base) return off;
     char* b = (char*)base;
     ws->base = base;
     ws->bytes = off;
@@ -53,6 +50,17 @@ lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
     ws->ctx8 = fp8 ? (uint8_t*)(b + o_c8) : nullptr;
     ws->ctx8_scale = fp8 ? (float*)(b + o_c8s) : nullptr;
     ws->sums = (uint64_t*)(b + o_sums);
+    return off;
+}
+
+lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws) {
+    const size_t bytes = workspace_carve(d, nullptr, nullptr);
+    void* base = nullptr;
+    if (hipMalloc(&base, bytes) != hipSuccess) {
+        set_error("hipMalloc of the activation workspace (" + std::to_string(bytes) + " bytes) failed");
+        return LWO_ENOMEM;
+    }
+    workspace_carve(d, base, ws);
     LWO_HIP_TRY(hipMemset(ws->sums, 0, 16));
     return LWO_OK;
 }

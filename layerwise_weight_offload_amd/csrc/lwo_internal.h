@@ -103,6 +103,9 @@ struct Workspace {
 };
 
 lwo_status workspace_alloc(const lwo_model_desc& d, Workspace* ws);
+// The workspace's layout from base (device); with base == nullptr it only
+// returns the bytes it needs.
+size_t workspace_carve(const lwo_model_desc& d, void* base, Workspace* ws);
 void workspace_free(Workspace* ws);
 
 // Optional per-kernel timing: events around each launch, aggregated per kernel symbol.
