@@ -268,16 +268,15 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
             m_i = m_new;
         }
         const float nm = -m_i;
-        float rs = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, nm));
-                s[t][r] = p;
-                rs += p;
-            }
-        l_i += swap_halves(rs, [](float u, float v) { return u + v; });
+            for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, nm));
+        // The row sum is taken from the bf16 probabilities the PV products use,
+        // two at a time with a dot product against (1, 1): 16 VALU operations
+        // per tile instead of 32 adds (0.6% faster at 32760 x 32760), and the
+        // denominator sums exactly the values that multiply V.
+        float rs = 0.0f;
 
         // ---- O^T += V^T P^T, one k-step (16 keys) at a time.  Keys 32..63's
         // fragments are read while keys 0..31's MFMAs run; every wait leaves at
@@ -286,6 +285,15 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
             bf16x8 pf;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
+            {
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16x2_t pp = {pf[2 * e], pf[2 * e + 1]};
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp, one, rs, false);
+                }
+            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 asm volatile("" : "+v"(vf[ks][nt][0]), "+v"(vf[ks][nt][1]));
@@ -302,6 +310,7 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
         pv(1, 0, vb);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         pv(1, 1, vb);
+        l_i += swap_halves(rs, [](float u, float v) { return u + v; });
 #undef VREAD
     };
 
@@ -431,7 +440,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
                 if (ksplit) LWO_KL((k_attn_tr<72, 4, 2>), dim3((a.Tq + 127) / 128, a.H, a.B), 512, 0, st, a);
                 else LWO_KL((k_attn_tr<72, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a);
                 break;
-            case 128: LWO_KL((k_attn_tr<128, 8>), dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st, a); break;
+            case 128:
+                // Few key tiles (cross-attention over a 512-token context): four
+                // wavefronts, two workgroups per CU, so one workgroup's prologue
+                // and epilogue overlap the other's tiles (32760 x 512: 0.55 ->
+                // 0.51 ms); long key ranges keep eight wavefronts per workgroup.
+                if (a.Tk <= 1024) LWO_KL((k_attn_tr<128, 4>), dim3((a.Tq + 127) / 128, a.H, a.B), 256, 0, st, a);
+                else LWO_KL((k_attn_tr<128, 8>), dim3((a.Tq + 255) / 256, a.H, a.B), 512, 0, st, a);
+                break;
             default: return hipErrorInvalidValue;
         }
     } else {
