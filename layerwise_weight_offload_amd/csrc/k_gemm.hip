@@ -1,9 +1,9 @@
 // Linear layers of the DiT block, Y = A W^T with a fused epilogue (bias,
 // GELU-tanh, gated or plain residual add into the fp32 residual stream).
 //
-// k_gemm_deep takes bf16 (v_mfma_f32_32x32x16_bf16) or OCP fp8 e4m3
-// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) operands and
-// accumulates in fp32.  Both operands are K-contiguous: [M,K] row-major
+// k_gemm_deep takes bf16 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_16x16x32_bf16
+// for the 256x256 tiles) or OCP fp8 e4m3 (v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit block scales) operands and accumulates in fp32.  Both operands are K-contiguous: [M,K] row-major
 // activations, and [N,K] weights tiled in 64-row x 64-byte tiles (the block
 // layout's tiled weights), so a stage of weight rows is one run of
 // consecutive memory and each lane's MFMA fragment is one or two 16-byte LDS
@@ -131,13 +131,17 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
-template <int BM, int BN, int SB, bool FP8, int EPI, int NWN = 2>
+template <int BM, int BN, int SB, bool FP8, int EPI, int NWN = 2, bool M16 = false>
 __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
-    // 2 x NWN wavefronts, each owning (BM/2) x (BN/NWN) outputs = TM x TN MFMA blocks.
+    // 2 x NWN wavefronts, each owning (BM/2) x (BN/NWN) outputs = TM x TN MFMA blocks of RB x RB
+    // (RB = 32: v_mfma_f32_32x32x16_bf16 / the fp8 32x32x64; RB = 16: v_mfma_f32_16x16x32_bf16).
+    static_assert(!(M16 && FP8), "16x16 blocks: bf16 only");
+    constexpr int RB = M16 ? 16 : 32;
     constexpr int NW = 2 * NWN;
-    constexpr int TM = BM / 64, TN = BN / (32 * NWN);
+    constexpr int TM = BM / (2 * RB), TN = BN / (RB * NWN);
+    constexpr int TS = BM / 64;                      // 32-row slices of a wavefront's block (epilogue)
     constexpr int DIST = 3;                          // prefetch distance (4 buffers); SB = stage bytes per row
-    constexpr int KS = FP8 ? SB / 64 : SB / 32;      // MFMA k-steps per stage
+    constexpr int KS = (FP8 || M16) ? SB / 64 : SB / 32;   // MFMA k-steps per stage
     constexpr int CPR = SB / 16, RPI = kWave / CPR;  // 16-byte chunks per row, rows per load instruction
     constexpr int LIA = BM / (NW * RPI), LIW = BN / (NW * RPI);   // load instructions per wavefront per operand
     constexpr int VM = 2 * (LIA + LIW);              // loads of the two stages after the one awaited
@@ -211,13 +215,15 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                                              16, 0, 0);
     };
 
-    floatx16 acc[TM][TN];
+    using AccT = std::conditional_t<M16, floatx4, floatx16>;
+    constexpr int NACC = M16 ? 4 : 16;
+    AccT acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.0f;
 
     // Fragments: bf16 one 16-byte read per operand block and k-step, fp8 two.
     constexpr int RP = FP8 ? 2 : 1;                  // reads per fragment
@@ -226,19 +232,19 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     auto reads = [&](int slot, const unsigned char* as, const unsigned char* ws, int ks) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * (BM / 2) + i * 32 + l32, sw = swz(row);
+            const int row = wm * (BM / 2) + i * RB + (M16 ? lane % 16 : l32), sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
-                const int c = FP8 ? ks * 4 + half * 2 + q : ks * 2 + half;
+                const int c = M16 ? ks * 4 + lane / 16 : (FP8 ? ks * 4 + half * 2 + q : ks * 2 + half);
                 fa[slot][i][q] = lds_read16(as + row * SB + ((c ^ sw) * 16));
             }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn * (BN / NWN) + j * 32 + l32, sw = swz(row);
+            const int row = wn * (BN / NWN) + j * RB + (M16 ? lane % 16 : l32), sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
-                const int c = FP8 ? ks * 4 + half * 2 + q : ks * 2 + half;
+                const int c = M16 ? ks * 4 + lane / 16 : (FP8 ? ks * 4 + half * 2 + q : ks * 2 + half);
                 fb[slot][j][q] = lds_read16(ws + row * SB + ((c ^ sw) * 16));
             }
         }
@@ -269,6 +275,10 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                     const intx8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
                     // formats 0/0: e4m3 x e4m3; scale exponents 127 = 2^0
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 127, 0, 127);
+                } else if constexpr (M16) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[slot][i][0]),
+                                                                        __builtin_bit_cast(bf16x8, fb[slot][j][0]),
+                                                                        acc[i][j], 0, 0, 0);
                 } else {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[slot][i][0]),
                                                                         __builtin_bit_cast(bf16x8, fb[slot][j][0]),
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // residual forms load the fp32 residual rows of slice i + 1 before slice
     // i's LDS round trip, so the slices' load latencies overlap, and read the
     // gate row once when the tile's rows all lie in one batch.
-    constexpr int CW = 32 * TN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
+    constexpr int CW = BN / NWN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
     constexpr bool RES = EPI >= EPI_GATED;
     static_assert((NW / 4) * 32 * CW * 4 <= AB, "epilogue staging fits the A buffers");
     float* lds = (float*)((wave % 4 == 0 ? A_0 : wave % 4 == 1 ? A_1 : wave % 4 == 2 ? A_2 : A_3) +
@@ -409,15 +419,25 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     }
     if constexpr (RES) load_x(0, xq[0]);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TS; ++i) {
         if constexpr (RES) {
-            if (i + 1 < TM) load_x(i + 1, xq[(i + 1) % 2]);
+            if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
         }
+        if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: lane holds column lane % 16, rows 4 (lane / 16) + r
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                lds[(8 * (r / 4) + 4 * half + (r % 4)) * CW + j * 32 + l32] = acc[i][j][r];
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        lds[(sb * 16 + 4 * (lane / 16) + r) * CW + j * 16 + lane % 16] = acc[2 * i + sb][j][r];
+        } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    lds[(8 * (r / 4) + 4 * half + (r % 4)) * CW + j * 32 + l32] = acc[i][j][r];
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
 #pragma unroll
         for (int h = 0; h < NP / PB; ++h) {
@@ -480,8 +500,11 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     // CU (LDS), 128x128 two (64-byte stages) or one (128-byte stages), 128x64 one.
     const int t256 = tiles(256, 256), t256x128 = tiles(256, 128), t128 = tiles(128, 128);
     if (rows256 && t256 >= 256) {   // eight wavefronts: two per SIMD
+        // bf16 on 16x16x32 MFMAs: half the accumulator traffic per flop of the
+        // 32x32x16 form, which these power-limited products turn into speed
+        // (32760-token products 1-4% faster, same results bit for bit).
         if (f8) LWO_KL((k_gemm_deep<256, 256, 64, true, EPI, 4>), t256, 512, 0, st, g);
-        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI, 4>), t256, 512, 0, st, g);
+        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI, 4, true>), t256, 512, 0, st, g);
     } else if (rows256 && t256x128 >= 192 && t256x128 <= 256) {
         if (f8) LWO_KL((k_gemm_deep<256, 128, 64, true, EPI>), t256x128, 256, 0, st, g);
         else LWO_KL((k_gemm_deep<256, 128, 64, false, EPI>), t256x128, 256, 0, st, g);
