@@ -114,12 +114,16 @@ __device__ __forceinline__ void tile_of(int pid, int nt_m, int nt_n, int& tm, in
 // wavefront's L loads per stage for the two later stages may still be in
 // flight) followed by a plain s_barrier: the workgroup barrier of the
 // language would also drain those later loads.  LDS rows are 64 bytes (four
-// 16-byte chunks); chunk c of row r sits at c ^ f(r) with f(r) = (r >> 2) & 3:
-// rows r, r + 4, r + 8, r + 12 of one fragment read would otherwise share
-// banks (measured on gfx950 with the LDS bank-conflict counter: this choice
-// gives none for the fragment reads, XOR with bits 1 or 0 of r leaves half
-// the LDS cycles in conflicts).
+// 16-byte chunks); chunk c of row r sits at c ^ f(r).  Which f keeps a
+// fragment read on distinct banks depends on the lanes' row/chunk pattern
+// (measured on gfx950 with the LDS bank-conflict counter and with a timing
+// probe of ds_read_b128 at eight wavefronts per CU):
+//  * 32x32 blocks (lane l: row l % 32, chunk l / 32): f(r) = (r >> 2) & 3 is
+//    conflict-free, (r >> 1) & 3 and r & 3 are not;
+//  * 16x16x32 blocks (lane l: row l % 16, chunk l / 16): (r >> 1) & 3 is
+//    conflict-free, (r >> 2) & 3 takes two cycles per read.
 __device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz64_m16(int r) { return (r >> 1) & 3; }
 
 // 16-byte LDS read issued as an instruction the compiler does not track: its
 // completion is awaited explicitly (lds_wait), so the compiler's own waits,
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     static_assert(4 * (AB + WB) <= 160 * 1024, "LDS");
     // Chunk c of row r sits at c ^ swz(r): 64-byte rows as described above;
     // 128-byte rows (r >> 1) & 7 (rows r and r + 1 are half the banks apart).
-    auto swz = [](int r) { return SB == 64 ? swz64(r) : (r >> 1) & 7; };
+    auto swz = [](int r) { return SB == 64 ? (M16 ? swz64_m16(r) : swz64(r)) : (r >> 1) & 7; };
     // Four buffers per operand as separate arrays, used with compile-time
     // indices (the k loop is unrolled by four): the compiler can then tell the
     // buffer a load fills from the one being read, and does not stall every
