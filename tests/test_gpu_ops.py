@@ -218,6 +218,12 @@ def _attn_case(lib, dtype, B, H, Tq, Tk, d, fused_qkv, n_rows, seed):
     (1, 3, 129, 128, 128, False, 129),        # d 128: two full key tiles (even tile count)
     (2, 2, 64, 64, 128, True, 64),            # d 128: one full key tile
     (1, 2, 520, 700, 128, False, 520),        # d 128: eleven key tiles, three query blocks
+    # d 128 beyond 1024 keys (eight-wavefront workgroups): odd and even tile counts, partial last tiles
+    (2, 2, 300, 1025, 128, False, 300),       # 17 key tiles, the last with one key
+    (2, 1, 130, 1057, 128, False, 130),       # 17 tiles, the last with 33 keys (its second half one key)
+    (1, 2, 1100, 1100, 128, True, 1100),      # 18 tiles, the last with 12 keys; ragged queries, every row
+    (1, 2, 200, 1120, 128, False, 200),       # 18 tiles, the last with 32 keys (its second half empty)
+    (1, 3, 513, 1152, 128, False, 513),       # 18 full tiles, three query blocks, one row in the last
     (2, 2, 100, 150, 72, False, 100),         # key tiles split over two groups: the second has one partial tile
     (1, 16, 2100, 300, 72, False, 48),        # d 72 with more query tiles than CUs: no key split
     (1, 64, 600, 200, 64, False, 48),         # d 64 with more query tiles than CUs: no key split
