@@ -290,6 +290,73 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                 }
             }
     };
+    // Single-k-step stages (KS = 1: the 16x16x32 tiles and fp8): the stage's
+    // reads go out as the B fragments, then the A fragments in NG groups of
+    // rows; the MFMAs of each group of rows start as soon as its fragments
+    // have landed, so only the first group's read latency is exposed.
+    constexpr int NG = (KS == 1 && TM % 4 == 0) ? 4 : 1, GR = TM / NG;   // groups, A rows per group
+    auto reads_grouped = [&](const unsigned char* as, const unsigned char* ws) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int row = wn * (BN / NWN) + j * RB + (M16 ? lane % 16 : l32), sw = swz(row);
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int c = M16 ? lane / 16 : (FP8 ? half * 2 + q : half);
+                fb[0][j][q] = lds_read16(ws + row * SB + ((c ^ sw) * 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * (BM / 2) + i * RB + (M16 ? lane % 16 : l32), sw = swz(row);
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int c = M16 ? lane / 16 : (FP8 ? half * 2 + q : half);
+                fa[0][i][q] = lds_read16(as + row * SB + ((c ^ sw) * 16));
+            }
+        }
+    };
+    // Wait until the fragments of row group gi have landed (the later groups'
+    // GR RP reads each may still be outstanding); the waited fragments pass
+    // through the wait so that the MFMAs using them stay below it.
+    auto wait_group = [&](int g) {   // g: a literal after inlining
+        if (g == 0) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"((NG - 1) * GR * RP) : "memory");
+        else if (g == 1) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(NG > 2 ? (NG - 2) * GR * RP : 0) : "memory");
+        else if (g == 2) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(NG > 3 ? (NG - 3) * GR * RP : 0) : "memory");
+        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (g == 0) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < RP; ++q) asm volatile("" : "+v"(fb[0][j][q]));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            if (i / GR == g)
+#pragma unroll
+                for (int q = 0; q < RP; ++q) asm volatile("" : "+v"(fa[0][i][q]));
+    };
+    auto mma_rows = [&](int g) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if (i / GR != g) continue;
+                if constexpr (FP8) {
+                    const intx4 a0 = fa[0][i][0], a1 = fa[0][i][1], b0 = fb[0][j][0], b1 = fb[0][j][1];
+                    const intx8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    const intx8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 127, 0, 127);
+                } else if constexpr (M16) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[0][i][0]),
+                                                                        __builtin_bit_cast(bf16x8, fb[0][j][0]),
+                                                                        acc[i][j], 0, 0, 0);
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][i][0]),
+                                                                        __builtin_bit_cast(bf16x8, fb[0][j][0]),
+                                                                        acc[i][j], 0, 0, 0);
+                }
+            }
+    };
 
     const int nk = (int)(rowA / SB);
     // Stages of four k-steps (bf16, 128-byte stages) read the next stage's
@@ -331,6 +398,16 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                     reads(sl ^ 1, abuf(Next{}), wbuf(Next{}), 0);
                 }
                 mma(sl);
+            }
+        } else if constexpr (NG > 1) {
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM) : "memory");
+            issue(std::integral_constant<int, (B + DIST) % 4>{}, min(kt + DIST, nk - 1) * SB);
+            reads_grouped(as, ws);
+            static_assert(NG == 4, "four row groups");
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                wait_group(g);
+                mma_rows(g);
             }
         } else {
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM) : "memory");
