@@ -377,7 +377,9 @@ lwo_status lwo_run_denoise_step(lwo_store* store, void* x, const void* cond, con
  *           the layout of lwo_block_layout(desc) (e.g. lwo_pack_block's bytes
  *           copied to the device); caller-owned, read only;
  *   x, cond, ctx as for lwo_run_denoise_step (x updated in place);
- *   hip_stream a non-null stream; the call runs on that stream's device.
+ *   hip_stream a non-null stream; the call runs on that stream's device
+ *           (made current during the call; the caller's current device is
+ *           restored before it returns).
  * The step's activation workspace lives in a file-scope device array of
  * LWO_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
  * until the process ends.  Every call on one GPU uses that GPU's one array

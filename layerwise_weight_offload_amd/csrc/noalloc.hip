@@ -65,9 +65,13 @@ extern "C" lwo_status lwo_run_blocks_noalloc(const lwo_model_desc* desc, const v
             return LWO_EINVAL;
         }
         hipStream_t st = (hipStream_t)hip_stream;
-        int dev = -1;
+        int dev = -1, prev = -1;
         LWO_HIP_TRY(hipStreamGetDevice(st, &dev));
         if (dev < 0 || dev >= kMaxDevices) { set_error("noalloc: device ordinal out of range"); return LWO_EINVAL; }
+        LWO_HIP_TRY(hipGetDevice(&prev));
+        // The stream's device is made current for the symbol lookup and the
+        // launches; the caller's current device is restored on every return.
+        struct Restore { int d; ~Restore() { if (d >= 0) (void)hipSetDevice(d); } } restore{prev};
         LWO_HIP_TRY(hipSetDevice(dev));
         void* base = nullptr;
         LWO_TRY(scratch_on(dev, &base));

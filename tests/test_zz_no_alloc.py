@@ -52,6 +52,7 @@ def test_noalloc_equals_resident_step_twice(lib, name, small_tokens):
         lib.run_blocks_noalloc(desc, [e.data_ptr() for e in exts], x.data_ptr(), c.data_ptr(),
                                cx.data_ptr() if cx is not None else None, s.cuda_stream)
         s.synchronize()
+        assert torch.cuda.current_device() == 0   # the caller's current device is left as it was
         got = _bits(w, x)
         assert np.array_equal(got, _resident_step_bits(lib, w)), (name, w.tokens)
 
