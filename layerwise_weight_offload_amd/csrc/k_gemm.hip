@@ -295,7 +295,8 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // rows; the MFMAs of each group of rows start as soon as its fragments
     // have landed, so only the first group's read latency is exposed.
     constexpr int NG = (KS == 1 && TM % 4 == 0) ? 4 : 1, GR = TM / NG;   // groups, A rows per group
-    auto reads_grouped = [&](const unsigned char* as, const unsigned char* ws) {
+    // Group 0 of a stage: the B fragments and A rows [0, GR); the rest: A rows [GR, TM).
+    auto reads_group0 = [&](const unsigned char* as, const unsigned char* ws) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int row = wn * (BN / NWN) + j * RB + (M16 ? lane % 16 : l32), sw = swz(row);
@@ -306,7 +307,18 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < GR; ++i) {
+            const int row = wm * (BM / 2) + i * RB + (M16 ? lane % 16 : l32), sw = swz(row);
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int c = M16 ? lane / 16 : (FP8 ? half * 2 + q : half);
+                fa[0][i][q] = lds_read16(as + row * SB + ((c ^ sw) * 16));
+            }
+        }
+    };
+    auto reads_rest = [&](const unsigned char* as) {
+#pragma unroll
+        for (int i = GR; i < TM; ++i) {
             const int row = wm * (BM / 2) + i * RB + (M16 ? lane % 16 : l32), sw = swz(row);
 #pragma unroll
             for (int q = 0; q < RP; ++q) {
@@ -365,7 +377,10 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // 256-row tiles ran 2-3% slower that way, and with one (fp8, 64-byte
     // stages) both fragment slots would be live at once, beyond the 256x256
     // tile's registers; those stages read at their own start.
-    constexpr bool LOOK = KS >= 4;
+    // Grouped look-ahead (below) for the fp8 single-k-step stages: 3-4% faster
+    // on the 32760-token fp8 products, 1-3% slower on the 16x16x32 bf16 ones,
+    // which read their groups at the stage start (same-box A/B, same bits).
+    constexpr bool LOOK = KS >= 4 || (NG > 1 && FP8);
     // Look-ahead stage: multiply the tiles in buffer B = kt % 4 while the next
     // k-step's fragments are read, the first of them having been read at the
     // end of the previous stage.  Before its last k-step: wait for this
@@ -383,7 +398,28 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         constexpr int B = decltype(b)::value;
         const unsigned char* as = abuf(b);
         const unsigned char* ws = wbuf(b);
-        if constexpr (LOOK) {
+        if constexpr (LOOK && NG > 1) {
+            // Grouped look-ahead (one k-step per stage): group 0 of this stage was
+            // read at the end of the previous one; read the other rows, multiply
+            // each group as it lands, and before the last group wait for stage
+            // kt + 1's loads and barrier (every wavefront is then done reading
+            // buffer B, which takes stage kt + 4); after the last group's MFMAs
+            // read group 0 of stage kt + 1 into the registers they freed.
+            using Next = std::integral_constant<int, (B + 1) % 4>;
+            reads_rest(as);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                wait_group(g);
+                if (g == NG - 1) {
+                    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM) : "memory");
+                    issue(b, min(kt + 4, nk - 1) * SB);
+                }
+                mma_rows(g);
+                __builtin_amdgcn_sched_barrier(0);   // group g's MFMAs stay between its wait and the next
+            }
+            __builtin_amdgcn_sched_barrier(0);   // the last MFMAs read B and A rows before the reads reuse them
+            reads_group0(abuf(Next{}), wbuf(Next{}));
+        } else if constexpr (LOOK) {
             using Next = std::integral_constant<int, (B + 1) % 4>;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -402,8 +438,8 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         } else if constexpr (NG > 1) {
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM) : "memory");
             issue(std::integral_constant<int, (B + DIST) % 4>{}, min(kt + DIST, nk - 1) * SB);
-            reads_grouped(as, ws);
-            static_assert(NG == 4, "four row groups");
+            reads_group0(as, ws);
+            reads_rest(as);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 wait_group(g);
@@ -437,7 +473,8 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     if constexpr (LOOK) {
         issue(std::integral_constant<int, 3>{}, min(3, nk - 1) * SB);
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(VM + LIA + LIW) : "memory");
-        reads(0, abuf(std::integral_constant<int, 0>{}), wbuf(std::integral_constant<int, 0>{}), 0);
+        if constexpr (NG > 1) reads_group0(abuf(std::integral_constant<int, 0>{}), wbuf(std::integral_constant<int, 0>{}));
+        else reads(0, abuf(std::integral_constant<int, 0>{}), wbuf(std::integral_constant<int, 0>{}), 0);
     }
     // Without TAIL the launcher guarantees nk % 4 == 0.
     int kt = 0;
@@ -459,6 +496,13 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing re-loads before the workgroup ends
     __syncthreads();                                    // every wavefront is done with the stage buffers
 
+    // Lane and wavefront indices derived again after the k loop, through an asm
+    // statement, so that the compiler does not keep the k loop's copies (and
+    // values computed from them) alive across it.
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int ewave = etid / kWave, elane = etid % kWave, ewm = ewave / NWN, ewn = ewave % NWN;
+    const int el32 = elane % 32, ehalf = elane / 32;
     // Epilogue through LDS.  Per 32-row slice of its block, a wavefront writes
     // the fp32 accumulators into its own buffer (row stride CW floats), reads
     // them back as row-contiguous float4s (CH lanes per row, RPP rows per
@@ -469,12 +513,12 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     constexpr int CW = BN / NWN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
     constexpr bool RES = EPI >= EPI_GATED;
     static_assert((NW / 4) * 32 * CW * 4 <= AB, "epilogue staging fits the A buffers");
-    float* lds = (float*)((wave % 4 == 0 ? A_0 : wave % 4 == 1 ? A_1 : wave % 4 == 2 ? A_2 : A_3) +
-                          (wave / 4) * 32 * CW * 4);
-    const int c4 = lane % CH, rr = lane / CH;           // float4 column chunk and row-in-pass of this lane
-    const int nb = n0 + wn * CW + 4 * c4;               // its first output column (CW = BN / NWN)
+    float* lds = (float*)((ewave % 4 == 0 ? A_0 : ewave % 4 == 1 ? A_1 : ewave % 4 == 2 ? A_2 : A_3) +
+                          (ewave / 4) * 32 * CW * 4);
+    const int c4 = elane % CH, rr = elane / CH;           // float4 column chunk and row-in-pass of this elane
+    const int nb = n0 + ewn * CW + 4 * c4;               // its first output column (CW = BN / NWN)
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
-    const int mw = m0 + wm * (BM / 2);                  // first row of this wavefront's block
+    const int mw = m0 + ewm * (BM / 2);                  // first row of this wavefront's block
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
     if (ncol && g.bias) {
         const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nb);
@@ -504,20 +548,20 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         if constexpr (RES) {
             if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
         }
-        if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: lane holds column lane % 16, rows 4 (lane / 16) + r
+        if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: elane holds column elane % 16, rows 4 (elane / 16) + r
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        lds[(sb * 16 + 4 * (lane / 16) + r) * CW + j * 16 + lane % 16] = acc[2 * i + sb][j][r];
+                        lds[(sb * 16 + 4 * (elane / 16) + r) * CW + j * 16 + elane % 16] = acc[2 * i + sb][j][r];
         } else {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    lds[(8 * (r / 4) + 4 * half + (r % 4)) * CW + j * 32 + l32] = acc[i][j][r];
+                    lds[(8 * (r / 4) + 4 * ehalf + (r % 4)) * CW + j * 32 + el32] = acc[i][j][r];
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
 #pragma unroll
