@@ -133,6 +133,7 @@ def test_linear_bf16_sampled(lib, M, N, K, epi):
 
 @pytest.mark.parametrize("M,N,K,seg", [(32760, 15360, 5120, 5120), (32760, 5120, 13824, 5120), (300, 1024, 256, 1024),
                                        (2048, 1152, 4608, 1152),    # 144 tiles of 128x128, one per CU
+                                       (2048, 3456, 1024, 1152),    # 216 tiles of 256x128 (grouped look-ahead)
                                        (2000, 1088, 640, 64)])      # ragged M and N (a half tile of weight rows)
 def test_linear_fp8_sampled(lib, M, N, K, seg):
     torch = _torch()
