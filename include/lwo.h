@@ -90,6 +90,17 @@ typedef enum lwo_status {
 
 typedef enum lwo_dtype { LWO_F32 = 0, LWO_BF16 = 1, LWO_FP8_E4M3 = 2 } lwo_dtype;
 typedef enum lwo_block_kind { LWO_KIND_DIT = 0, LWO_KIND_VIDEO = 1 } lwo_block_kind;
+/* Activation row layout of the single-kernel entry points (project addition,
+ * a storage order only: no value changes).  LWO_ROWS: row-major with the
+ * stated leading dimension.  LWO_KTILED: the tiled-weight order above applied
+ * to activation rows, with R = leading dimension * element bytes (a multiple
+ * of 64) and the rows rounded up to a multiple of 64: the byte at row m, row
+ * byte c sits at ((m / 64) * (R / 64) + c / 64) * 4096 + (m % 64) * 64 +
+ * c % 64.  The buffer spans ceil(M / 64) * 64 rows; the padding rows of the
+ * last band are never read or written.  A denoise step writes the
+ * activations that feed its bf16/fp8 linears in this order, so each
+ * 64-byte GEMM stage of them is 4 KB of consecutive memory. */
+typedef enum lwo_layout { LWO_ROWS = 0, LWO_KTILED = 1 } lwo_layout;
 typedef enum lwo_host_mode {
     LWO_HOST_PIN_COPY = 0, LWO_HOST_REGISTER = 1, LWO_HOST_STAGED = 2,
     LWO_HOST_SHARD = 3     /* one rank's share of an all-gather group (lwo_build_shard_store) */
@@ -469,31 +480,39 @@ lwo_status lwo_destroy_block_store(lwo_store* store);
  * a_scale[m] + bias with bias and out bf16.  xr and gate are float32.
  * K must be a multiple of 16 (F32), 64 (BF16) or 128 (FP8); lda = K.  W is
  * row-major (ldw = K) for F32 and tiled (the block layout's tiled weights,
- * lwo_tile_weight) for BF16 and FP8, with N a multiple of 64. */
+ * lwo_tile_weight) for BF16 and FP8, with N a multiple of 64.  a_layout: A
+ * in LWO_ROWS or (BF16, FP8) LWO_KTILED order; out_layout: `out` of
+ * epilogues 0 and 1 in LWO_ROWS or (BF16, FP8; ldo a multiple of 32)
+ * LWO_KTILED order. */
 lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void* a, const float* a_scale, const void* w,
                          const float* w_scale, int32_t w_seg, const void* bias, int32_t M, int32_t N, int32_t K,
                          void* out, int32_t ldo, float* xr, int32_t ldx, const float* gate, int32_t gate_ld,
-                         int32_t rows_per_gate, void* stream);
+                         int32_t rows_per_gate, int32_t a_layout, int32_t out_layout, void* stream);
 
 /* Softmax attention without a mask, per batch b and head h:
  * O[b, t, h*d:(h+1)*d] = softmax(Q_bh K_bh^T / sqrt(d)) V_bh, rows of Q/O at
  * b*Tq + t, rows of K/V at b*Tk + t, head h in columns [h*d, (h+1)*d).
- * dtype F32 or BF16 for q, k, v, o; head_dim 64, 72 or 128. */
+ * dtype F32 or BF16 for q, k, v, o; head_dim 64, 72 or 128.  o_layout:
+ * LWO_ROWS, or LWO_KTILED (BF16, ldo a multiple of 32; rows b*Tq + t). */
 lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq, const void* k, int32_t ldk, const void* v,
                             int32_t ldv, void* o, int32_t ldo, int32_t batch, int32_t heads, int32_t tq,
-                            int32_t tk, int32_t head_dim, void* stream);
+                            int32_t tk, int32_t head_dim, int32_t o_layout, void* stream);
 
 /* Row LayerNorm (eps 1e-6, no affine) of float32 x [M, D] (row stride D);
  * with mod ([B, 6, D] float32, b = row / rows_per_batch) the result is
  * LN(x)(1 + mod[b, scale_chunk]) + mod[b, shift_chunk].  out_dtype F32/BF16
  * writes out [M, D]; FP8_E4M3 writes e4m3 codes to out and per-row scales
- * amax/448 to out_scale (codes = e4m3(y * 448 / amax), float32 arithmetic). */
+ * amax/448 to out_scale (codes = e4m3(y * 448 / amax), float32 arithmetic).
+ * out_layout: LWO_ROWS, or LWO_KTILED for BF16/FP8 rows of a multiple of 64
+ * bytes (scales stay one float per row). */
 lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int32_t rows_per_batch, const float* mod,
                             int32_t shift_chunk, int32_t scale_chunk, void* out, int32_t out_dtype,
-                            float* out_scale, void* stream);
+                            float* out_scale, int32_t out_layout, void* stream);
 
-/* bf16 rows [M, N] -> e4m3 codes [M, N] and per-row scales (as above). */
-lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* codes, float* scales, void* stream);
+/* bf16 rows [M, N] (row-major) -> e4m3 codes [M, N] and per-row scales (as
+ * above); codes_layout LWO_ROWS, or LWO_KTILED with N a multiple of 64. */
+lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* codes, float* scales,
+                                int32_t codes_layout, void* stream);
 
 /* In place on rows of width 3D (q | k | v): q <- RMSNorm(q) * gq and
  * k <- RMSNorm(k) * gk over the D features (eps 1e-6); dtype F32 or BF16. */

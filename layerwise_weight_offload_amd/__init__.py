@@ -12,7 +12,7 @@ Importing fails loudly if the library has not been built: there is no
 fallback implementation.
 """
 from ._binding import (  # noqa: F401
-    BF16, F32, FP8_E4M3, HOST_PIN_COPY, HOST_REGISTER, HOST_SHARD, HOST_STAGED, KIND_DIT, KIND_VIDEO, LIB_PATH,
+    BF16, F32, FP8_E4M3, KTILED, ROWS, HOST_PIN_COPY, HOST_REGISTER, HOST_SHARD, HOST_STAGED, KIND_DIT, KIND_VIDEO, LIB_PATH,
     LwoError, ModelDesc, Stats, Store, block_layout, build_block_store, extent_checksum, last_error,
     pack_block, register_ranges, exported_symbols, op_attention, op_layernorm, op_linear, op_quantize_rows,
     op_rmsnorm_qk, probe_mfma, sha256, cache_publish, cache_open, CacheEntry, CacheExtents, build_mixed_store,

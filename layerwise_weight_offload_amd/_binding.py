@@ -28,6 +28,7 @@ _lib = C.CDLL(LIB_PATH)
 
 # enums (include/lwo.h)
 F32, BF16, FP8_E4M3 = 0, 1, 2
+ROWS, KTILED = 0, 1   # lwo_layout
 KIND_DIT, KIND_VIDEO = 0, 1
 HOST_PIN_COPY, HOST_REGISTER, HOST_STAGED, HOST_SHARD = 0, 1, 2, 3
 STATUS = {0: "LWO_OK", 1: "LWO_EINVAL", 2: "LWO_ENOMEM", 3: "LWO_EHIP", 4: "LWO_EBUDGET",
@@ -122,10 +123,11 @@ _lib_cache_open = _sig("lwo_cache_open", C.c_int, C.c_char_p, C.c_char_p, C.POIN
 _lib_cache_extents = _sig("lwo_cache_extents", C.c_int, _P, C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_int32))
 _lib_cache_close = _sig("lwo_cache_close", C.c_int, _P)
 _I = C.c_int32
-_lib_op_linear = _sig("lwo_op_linear", C.c_int, _I, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _I, _P)
-_lib_op_attention = _sig("lwo_op_attention", C.c_int, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P)
-_lib_op_layernorm = _sig("lwo_op_layernorm", C.c_int, _P, _I, _I, _I, _P, _I, _I, _P, _I, _P, _P)
-_lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P, _P)
+_lib_op_linear = _sig("lwo_op_linear", C.c_int, _I, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _I,
+                      _I, _I, _P)
+_lib_op_attention = _sig("lwo_op_attention", C.c_int, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P)
+_lib_op_layernorm = _sig("lwo_op_layernorm", C.c_int, _P, _I, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P)
+_lib_op_quantize_rows = _sig("lwo_op_quantize_rows", C.c_int, _P, _I, _I, _P, _P, _I, _P)
 _lib_op_rmsnorm_qk = _sig("lwo_op_rmsnorm_qk", C.c_int, _I, _P, _I, _I, _P, _P, _P)
 _lib_probe_mfma = _sig("lwo_probe_mfma", C.c_int, _I, _I, _I, _P, C.c_uint64, _P, C.POINTER(C.c_double))
 
@@ -148,25 +150,26 @@ def _v(p):
 
 
 def op_linear(dtype, epilogue, a, w, M, N, K, stream, *, a_scale=0, w_scale=0, w_seg=0, bias=0, out=0, ldo=0,
-              xr=0, ldx=0, gate=0, gate_ld=0, rows_per_gate=0):
+              xr=0, ldx=0, gate=0, gate_ld=0, rows_per_gate=0, a_layout=ROWS, out_layout=ROWS):
     """All pointers are device addresses (ints); see lwo_op_linear."""
     _check(_lib_op_linear(dtype, epilogue, _v(a), _v(a_scale), _v(w), _v(w_scale), w_seg, _v(bias), M, N, K,
-                          _v(out), ldo, _v(xr), ldx, _v(gate), gate_ld, rows_per_gate, _v(stream)))
+                          _v(out), ldo, _v(xr), ldx, _v(gate), gate_ld, rows_per_gate, a_layout, out_layout,
+                          _v(stream)))
 
 
-def op_attention(dtype, q, ldq, k, ldk, v, ldv, o, ldo, batch, heads, tq, tk, head_dim, stream):
+def op_attention(dtype, q, ldq, k, ldk, v, ldv, o, ldo, batch, heads, tq, tk, head_dim, stream, *, o_layout=ROWS):
     _check(_lib_op_attention(dtype, _v(q), ldq, _v(k), ldk, _v(v), ldv, _v(o), ldo, batch, heads, tq, tk, head_dim,
-                             _v(stream)))
+                             o_layout, _v(stream)))
 
 
 def op_layernorm(x, M, D, out, out_dtype, stream, *, mod=0, rows_per_batch=1, shift_chunk=0, scale_chunk=0,
-                 out_scale=0):
+                 out_scale=0, out_layout=ROWS):
     _check(_lib_op_layernorm(_v(x), M, D, rows_per_batch, _v(mod), shift_chunk, scale_chunk, _v(out), out_dtype,
-                             _v(out_scale), _v(stream)))
+                             _v(out_scale), out_layout, _v(stream)))
 
 
-def op_quantize_rows(inp, M, N, codes, scales, stream):
-    _check(_lib_op_quantize_rows(_v(inp), M, N, _v(codes), _v(scales), _v(stream)))
+def op_quantize_rows(inp, M, N, codes, scales, stream, *, codes_layout=ROWS):
+    _check(_lib_op_quantize_rows(_v(inp), M, N, _v(codes), _v(scales), codes_layout, _v(stream)))
 
 
 def op_rmsnorm_qk(dtype, qkv, M, D, gq, gk, stream):

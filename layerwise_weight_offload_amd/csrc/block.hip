@@ -21,16 +21,17 @@ static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // Lay the workspace out from `base` (nullptr: only size it); returns its bytes.
 size_t workspace_carve(const lwo_model_desc& d, void* base, Workspace* ws) {
     const size_t M = (size_t)d.batch * d.tokens, D = d.hidden, F = d.ffn;
+    const size_t Mp = (M + 63) / 64 * 64;   // buffers that may hold k-tiled rows span whole 64-row bands
     const size_t Mc = (size_t)d.batch * d.ctx_tokens;
     const size_t ae = dtype_bytes(d.act_dtype);
     const bool video = d.kind == LWO_KIND_VIDEO, fp8 = d.linear_dtype == LWO_FP8_E4M3;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    const size_t o_xr = take(M * D * 4), o_mod = take((size_t)d.batch * 6 * D * 4), o_h = take(M * D * ae);
+    const size_t o_xr = take(M * D * 4), o_mod = take((size_t)d.batch * 6 * D * 4), o_h = take(Mp * D * ae);
     const size_t o_silu = video ? 0 : take((size_t)d.batch * D * 4);
-    const size_t o_big = take(M * std::max(3 * D, F) * ae), o_attn = take(M * D * ae);
+    const size_t o_big = take(Mp * std::max(3 * D, F) * ae), o_attn = take(Mp * D * ae);
     const size_t o_cq = video ? take(M * D * ae) : 0, o_ckv = video ? take(Mc * 2 * D * ae) : 0;
-    const size_t o_q8 = fp8 ? take(M * std::max(D, F)) : 0, o_q8s = fp8 ? take(std::max(M, Mc) * 4) : 0;
+    const size_t o_q8 = fp8 ? take(Mp * std::max(D, F)) : 0, o_q8s = fp8 ? take(std::max(M, Mc) * 4) : 0;
     const size_t o_c8 = fp8 ? take(Mc * D) : 0, o_c8s = fp8 ? take(Mc * 4) : 0;
     const size_t o_sums = take(16);
     if (!base) return off;
@@ -142,7 +143,7 @@ lwo_status enqueue_step_begin(const lwo_model_desc& d, const Workspace& ws, cons
     if (d.kind == LWO_KIND_DIT)   // SiLU(cond) feeds the adaLN linear of every block: once per step
         LWO_LAUNCH(launch_silu(cond, d.act_dtype, ws.silu_cond, d.batch * d.hidden, st));
     if (d.linear_dtype == LWO_FP8_E4M3)   // the context feeds the cross K/V linears of every block: quantise once
-        LWO_LAUNCH(launch_quant_rows(ctx, d.batch * d.ctx_tokens, d.hidden, ws.ctx8, ws.ctx8_scale, st));
+        LWO_LAUNCH(launch_quant_rows(ctx, d.batch * d.ctx_tokens, d.hidden, ws.ctx8, ws.ctx8_scale, 0, st));
     return LWO_OK;
 }
 
@@ -161,6 +162,8 @@ static GemmArgs gemm_args(const lwo_model_desc& d, const void* a, const void* w,
     g.epi = epi;
     g.bias = bias;
     g.rows_per_batch = d.tokens;
+    // The block's own activations reach the MFMA linears k-tiled (the caller's context rows are the exception).
+    g.a_tiled = d.linear_dtype != LWO_F32;
     return g;
 }
 
@@ -170,6 +173,11 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     const int M = B * T, Mc = B * d.ctx_tokens;
     const int act = d.act_dtype, ae = dtype_bytes(act);
     const bool fp8 = d.linear_dtype == LWO_FP8_E4M3;
+    // Activations that feed an MFMA linear are written k-tiled by their producer:
+    // LayerNorm, and with bf16 linears the attention output and the GELU output
+    // (with fp8 linears those two stay row-major for the row quantiser, which
+    // writes the codes k-tiled).
+    const int tl = d.linear_dtype != LWO_F32, tl16 = tl && !fp8;
     const int h_dt = fp8 ? LWO_FP8_E4M3 : act;      // LayerNorm output dtype feeding a linear
     void* h_buf = fp8 ? (void*)ws.q8 : ws.h;
     char* big = (char*)ws.big;
@@ -210,7 +218,7 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     auto attn = [&](const char* site, const void* q, int ldq, const void* k, const void* v, int ldkv, int Tk) {
         AttnArgs a{};
         a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldkv; a.v = v; a.ldv = ldkv;
-        a.o = ws.attn; a.ldo = D;
+        a.o = ws.attn; a.ldo = D; a.o_tiled = tl16;
         a.B = B; a.H = H; a.Tq = T; a.Tk = Tk; a.dh = dh; a.dtype = act;
         char name[48];
         snprintf(name, sizeof(name), "attn_%s_%s_d%d", site, act == LWO_F32 ? "f32" : "bf16", dh);
@@ -221,11 +229,11 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     auto ln = [&](const float* m, int shc, int scc, void* out, int out_dt, float* osc) {
         const double bytes = (double)M * D * (4 + dtype_bytes(out_dt)) + (m ? 2.0 * B * D * 4 : 0.0);
         return timed(m ? "layernorm_mod" : "layernorm", 0.0, bytes,
-                     [&] { return launch_ln(ws.xr, M, D, T, m, shc, scc, out, out_dt, osc, st); });
+                     [&] { return launch_ln(ws.xr, M, D, T, m, shc, scc, out, out_dt, osc, tl, st); });
     };
     auto quant = [&](const void* in, int rows, int n, uint8_t* codes, float* sc) {
         return timed("quant_rows_fp8", 0.0, (double)rows * n * 3,
-                     [&] { return launch_quant_rows(in, rows, n, codes, sc, st); });
+                     [&] { return launch_quant_rows(in, rows, n, codes, sc, tl, st); });
     };
 
     if (d.kind == LWO_KIND_DIT) {
@@ -241,7 +249,7 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
         LWO_LAUNCH(gemm("o", g));
         LWO_LAUNCH(ln(mod, 3, 4, ws.h, act, nullptr));
         g = gemm_args(d, ws.h, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
-        g.out = big; g.ldo = F;
+        g.out = big; g.ldo = F; g.out_tiled = tl16;
         LWO_LAUNCH(gemm("fc1", g));
         g = gemm_args(d, big, p.fc2_w, M, D, F, EPI_GATED, p.fc2_b);
         g.xr = ws.xr; g.ldx = D; g.gate = mod + 5 * D; g.gate_ld = 6 * D;
@@ -274,7 +282,7 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     fp8_in(g, 4, ws.q8_scale, false);
     LWO_LAUNCH(gemm("cq", g));
     g = gemm_args(d, fp8 ? (const void*)ws.ctx8 : ctx, p.ck_w, Mc, 2 * D, D, EPI_STORE, p.ckv_b);
-    g.out = ws.ckv; g.ldo = 2 * D;
+    g.out = ws.ckv; g.ldo = 2 * D; g.a_tiled = 0;
     fp8_in(g, 5, ws.ctx8_scale, true);
     LWO_LAUNCH(gemm("ckv", g));
     const char* ckv = (const char*)ws.ckv;
@@ -289,7 +297,7 @@ lwo_status enqueue_block(const lwo_model_desc& d, const BlockPtrs& p, const Work
     // FFN
     LWO_LAUNCH(ln(mod, 3, 4, h_buf, h_dt, ws.q8_scale));
     g = gemm_args(d, h_buf, p.fc1_w, M, F, D, EPI_GELU, p.fc1_b);
-    g.out = big; g.ldo = F;
+    g.out = big; g.ldo = F; g.out_tiled = tl16;
     fp8_in(g, 8, ws.q8_scale, false);
     LWO_LAUNCH(gemm("fc1", g));
     a_in = big;

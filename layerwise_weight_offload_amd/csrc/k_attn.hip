@@ -361,7 +361,8 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
 
     if (qi >= Tq) return;
     const float inv = 1.0f / l_i;
-    bf16* O = (bf16*)a.o + (size_t)(b * Tq + qi) * a.ldo + h * DH;
+    const int orow = b * Tq + qi;
+    bf16* O = (bf16*)a.o + (size_t)orow * a.ldo + h * DH;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -371,7 +372,10 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
                 bf16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[nt][4 * g + e] * inv);
-                *(bf16x4*)(O + d0) = o;
+                // k-tiled output: 8 bytes at an 8-byte column offset stay inside one 64-byte tile row
+                bf16* dst = a.o_tiled ? (bf16*)((char*)a.o + ktiled_off(orow, (size_t)2 * (h * DH + d0), (size_t)2 * a.ldo))
+                                      : O + d0;
+                *(bf16x4*)dst = o;
             }
         }
 }

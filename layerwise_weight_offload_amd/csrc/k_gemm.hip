@@ -3,11 +3,13 @@
 //
 // k_gemm_deep takes bf16 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_16x16x32_bf16
 // for the 256x256 tiles) or OCP fp8 e4m3 (v_mfma_scale_f32_32x32x64_f8f6f4 with
-// unit block scales) operands and accumulates in fp32.  Both operands are K-contiguous: [M,K] row-major
-// activations, and [N,K] weights tiled in 64-row x 64-byte tiles (the block
-// layout's tiled weights), so a stage of weight rows is one run of
-// consecutive memory and each lane's MFMA fragment is one or two 16-byte LDS
-// reads from a row.  No split-K: every output is produced by one lane in a
+// unit block scales) operands and accumulates in fp32.  Both operands are K-contiguous: [M,K]
+// activations, row-major or k-tiled, and [N,K] weights tiled in 64-row x
+// 64-byte tiles (the block layout's tiled weights), so a stage of weight rows
+// (and of k-tiled activation rows, which the block's own producers write) is
+// one run of consecutive memory, loaded with 128-byte requests where a
+// row-major stage takes 64-byte ones; each lane's MFMA fragment is one or two
+// 16-byte LDS reads from a row.  No split-K: every output is produced by one lane in a
 // fixed order, so results are deterministic run to run.  Tiles of 256x256,
 // 256x128, 128x128 or 128x64 by problem size; direct-to-LDS loads three
 // stages ahead; LDS-staged vector epilogue (details at the kernel).
@@ -180,12 +182,17 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // of a 64-row band is 4 KB (64-byte stages) or 8 KB (128-byte) of
     // consecutive memory.  offW holds the part that does not move with kb; the
     // stage's own part is kb * 64.
+    // A is row-major, or k-tiled like W (g.a_tiled): then the band of m0 (a
+    // multiple of 64) starts at m0 * rowA as well, and a stage moves by kb * 64.
     uint32_t offA[LIA], offW[LIW];
 #pragma unroll
     for (int i = 0; i < LIA; ++i) {
         const int r = (wave * LIA + i) * RPI + lane / CPR;
-        offA[i] = (uint32_t)(min(r, g.M - 1 - m0) * rowA) + (uint32_t)(((lane % CPR) ^ swz(r)) * 16);
+        const int m = min(r, g.M - 1 - m0), ch = (lane % CPR) ^ swz(r);
+        offA[i] = g.a_tiled ? (uint32_t)((m >> 6) * rowA * 64) + (uint32_t)((ch >> 2) * 4096 + (m & 63) * 64 + (ch & 3) * 16)
+                            : (uint32_t)(m * rowA) + (uint32_t)(ch * 16);
     }
+    const int ash = g.a_tiled ? 6 : 0;
 #pragma unroll
     for (int i = 0; i < LIW; ++i) {
         const int r = (wave * LIW + i) * RPI + lane / CPR;
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         unsigned char* wd = wbuf(b);
 #pragma unroll
         for (int i = 0; i < LIA; ++i)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A0 + offA[i] + kb),
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A0 + offA[i] + (kb << ash)),
                                              (__attribute__((address_space(3))) void*)(ad + (wave * LIA + i) * RPI * SB),
                                              16, 0, 0);
 #pragma unroll
@@ -591,7 +598,9 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                     } else {
                         o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
                     }
-                    *(bf16x4*)((bf16*)g.out + (size_t)mrow[it] * g.ldo + nb) = o;
+                    bf16* dst = g.out_tiled ? (bf16*)((char*)g.out + ktiled_off(mrow[it], (size_t)2 * nb, (size_t)2 * g.ldo))
+                                            : (bf16*)g.out + (size_t)mrow[it] * g.ldo + nb;
+                    *(bf16x4*)dst = o;
                 } else {
                     const float4 x = xq[i % 2][h * PB + it];
                     float4 gg = g1;
@@ -652,6 +661,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const int kq = g.dtype == LWO_F32 ? 16 : (g.dtype == LWO_BF16 ? 64 : 128);
     if (g.N <= 0 || g.K <= 0 || g.K % kq) return hipErrorInvalidValue;
     if (g.dtype != LWO_F32 && g.act_dtype != LWO_BF16) return hipErrorInvalidValue;
+    if ((g.a_tiled || g.out_tiled) && g.dtype == LWO_F32) return hipErrorInvalidValue;   // fp32 tiles read rows
+    if (g.out_tiled && (g.epi > EPI_GELU || g.ldo % 32)) return hipErrorInvalidValue;    // whole 64-byte tile rows
     switch (g.epi) {
         case EPI_STORE: return launch_epi<EPI_STORE>(g, st);
         case EPI_GELU: return launch_epi<EPI_GELU>(g, st);

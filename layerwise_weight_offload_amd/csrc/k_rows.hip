@@ -180,7 +180,7 @@ hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* 
 template <int OUT, bool MOD, int NV4>
 __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M, int D, int T,
                                             const float* __restrict__ mod, int shc, int scc,
-                                            void* __restrict__ out, float* __restrict__ out_scale) {
+                                            void* __restrict__ out, float* __restrict__ out_scale, int tiled) {
     __shared__ float red[3][2][2];                      // [quantity][row of the workgroup][half]
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int rw = wave / 2, hf = wave % 2;             // row within the workgroup, half of the row
@@ -235,6 +235,7 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             v[i] = y;
         } else if (live && c < nh) {
             if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * cc4, y);
+            else if (tiled) store4((bf16*)((char*)out + ktiled_off(row, (size_t)8 * cc4, (size_t)2 * D)), y);
             else store4((bf16*)out + (size_t)row * D + 4 * cc4, y);
         }
     }
@@ -250,7 +251,8 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             const int c = lane + kWave * i;
             if (live && c < nh) {
                 uint32_t lo = pack2_e4m3(v[i].x * inv, v[i].y * inv), hi = pack2_e4m3(v[i].z * inv, v[i].w * inv);
-                *(uint32_t*)(o + 4 * (c0 + c)) = lo | (hi << 16);
+                uint8_t* dst = tiled ? (uint8_t*)out + ktiled_off(row, (size_t)4 * (c0 + c), (size_t)D) : o + 4 * (c0 + c);
+                *(uint32_t*)dst = lo | (hi << 16);
             }
         }
         if (live && lane == 0 && hf == 0) out_scale[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
@@ -259,12 +261,12 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
 
 template <int OUT, bool MOD>
 static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float* mod, int shc, int scc, void* out,
-                              float* out_scale, hipStream_t st) {
+                              float* out_scale, int tiled, hipStream_t st) {
     const int need = ((D / 4 + 1) / 2 + kWave - 1) / kWave;
     dim3 grid((M + 1) / 2);
 #define LWO_LN_CASE(NV)                                                                                     \
     if (need <= NV) {                                                                                       \
-        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, 0, st, xr, M, D, T, mod, shc, scc, out, out_scale);              \
+        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, 0, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled);       \
         return hipGetLastError();                                                                           \
     }
     LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(6) LWO_LN_CASE(8)
@@ -274,15 +276,16 @@ static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float*
 }
 
 hipError_t launch_ln(const float* xr, int M, int D, int T, const float* mod, int shift_chunk, int scale_chunk,
-                     void* out, int out_dt, float* out_scale, hipStream_t st) {
+                     void* out, int out_dt, float* out_scale, int out_tiled, hipStream_t st) {
     if (M <= 0) return hipSuccess;   // no rows: nothing to launch (a zero grid is an invalid launch)
     const bool m = mod != nullptr;
-    if (out_dt == LWO_F32) return m ? ln_dispatch<0, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
-                                    : ln_dispatch<0, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
-    if (out_dt == LWO_BF16) return m ? ln_dispatch<1, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
-                                     : ln_dispatch<1, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
-    return m ? ln_dispatch<2, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, st)
-             : ln_dispatch<2, false>(xr, M, D, T, mod, 0, 0, out, out_scale, st);
+    const int tl = out_dt == LWO_F32 ? 0 : out_tiled;
+    if (out_dt == LWO_F32) return m ? ln_dispatch<0, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, 0, st)
+                                    : ln_dispatch<0, false>(xr, M, D, T, mod, 0, 0, out, out_scale, 0, st);
+    if (out_dt == LWO_BF16) return m ? ln_dispatch<1, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, tl, st)
+                                     : ln_dispatch<1, false>(xr, M, D, T, mod, 0, 0, out, out_scale, tl, st);
+    return m ? ln_dispatch<2, true>(xr, M, D, T, mod, shift_chunk, scale_chunk, out, out_scale, tl, st)
+             : ln_dispatch<2, false>(xr, M, D, T, mod, 0, 0, out, out_scale, tl, st);
 }
 
 // ------------------------------------------------------------------ q/k RMSNorm
@@ -393,7 +396,7 @@ hipError_t launch_rmsnorm_qk(void* qkv, int dt, int M, int D, const void* gq, co
 
 // One wavefront per row: amax over the row, then codes = e4m3(x * (448 / amax)), scale = amax / 448.
 __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in, int M, int N,
-                                                    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                    uint8_t* __restrict__ codes, float* __restrict__ scales, int tiled) {
     const int row = blockIdx.x * 4 + threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     if (row >= M) return;
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
         bf16x8 v = *(const bf16x8*)(x + 8 * c);
         uint32_t w0 = pack2_e4m3((float)v[0] * inv, (float)v[1] * inv) | (pack2_e4m3((float)v[2] * inv, (float)v[3] * inv) << 16);
         uint32_t w1 = pack2_e4m3((float)v[4] * inv, (float)v[5] * inv) | (pack2_e4m3((float)v[6] * inv, (float)v[7] * inv) << 16);
-        *(uint2*)(o + 8 * c) = make_uint2(w0, w1);
+        *(uint2*)(tiled ? codes + ktiled_off(row, (size_t)8 * c, (size_t)N) : o + 8 * c) = make_uint2(w0, w1);
     }
     if (lane == 0) scales[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
 }
@@ -419,7 +422,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16* __restrict__ in,
 // The same with the row held in registers between the two passes (one HBM read).
 template <int NV8>
 __global__ __launch_bounds__(256) void k_quant_rows_reg(const bf16* __restrict__ in, int M, int N,
-                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                        int tiled) {
     const int row = blockIdx.x * 4 + threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     if (row >= M) return;
@@ -446,23 +450,25 @@ __global__ __launch_bounds__(256) void k_quant_rows_reg(const bf16* __restrict__
             const bf16x8 u = v[i];
             uint32_t w0 = pack2_e4m3((float)u[0] * inv, (float)u[1] * inv) | (pack2_e4m3((float)u[2] * inv, (float)u[3] * inv) << 16);
             uint32_t w1 = pack2_e4m3((float)u[4] * inv, (float)u[5] * inv) | (pack2_e4m3((float)u[6] * inv, (float)u[7] * inv) << 16);
-            *(uint2*)(o + 8 * c) = make_uint2(w0, w1);
+            *(uint2*)(tiled ? codes + ktiled_off(row, (size_t)8 * c, (size_t)N) : o + 8 * c) = make_uint2(w0, w1);
         }
     }
     if (lane == 0) scales[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
-hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st) {
+hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, int codes_tiled,
+                             hipStream_t st) {
     if (M <= 0) return hipSuccess;
     const int need = (N / 8 + kWave - 1) / kWave;
 #define LWO_Q_CASE(NV)                                                                                         \
     if (need <= NV) {                                                                                          \
-        LWO_KL((k_quant_rows_reg<NV>), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales);         \
+        LWO_KL((k_quant_rows_reg<NV>), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales,          \
+               codes_tiled);                                                                                   \
         return hipGetLastError();                                                                              \
     }
     LWO_Q_CASE(1) LWO_Q_CASE(2) LWO_Q_CASE(4) LWO_Q_CASE(8) LWO_Q_CASE(10) LWO_Q_CASE(16) LWO_Q_CASE(28)
 #undef LWO_Q_CASE
-    LWO_KL((k_quant_rows), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales);
+    LWO_KL((k_quant_rows), (M + 3) / 4, 256, 0, st, (const bf16*)in, M, N, codes, scales, codes_tiled);
     return hipGetLastError();
 }
 

@@ -17,6 +17,15 @@ namespace lwo {
 
 constexpr int kWave = 64;
 
+// k-tiled activation rows (the operand form of the tiled weights): a matrix of
+// M rows of R bytes (R a multiple of 64) stored as 64-row x 64-byte tiles, the
+// tiles of one 64-row band in column order, so that one 64-byte stage of a
+// 64-row band is 4 KB of consecutive memory.  Byte c of row m sits at the
+// offset below; the buffer spans whole bands (rows rounded up to 64).
+__host__ __device__ __forceinline__ size_t ktiled_off(int m, size_t c, size_t R) {
+    return (size_t)(m >> 6) * R * 64 + (c >> 6) * 4096 + (size_t)(m & 63) * 64 + (c & 63);
+}
+
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
 

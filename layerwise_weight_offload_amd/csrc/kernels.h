@@ -27,7 +27,7 @@ LaunchEvents& launch_events();   // per host thread
 enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_GATED = 2, EPI_RESID = 3 };
 
 struct GemmArgs {
-    const void* a;          // [M, K] row-major, lda = K
+    const void* a;          // [M, K], lda = K: row-major, or k-tiled when a_tiled (bf16/fp8)
     const void* w;          // [N, K] (a Linear weight [out, in]): row-major for fp32, 64x64-byte tiles for bf16/fp8
     int M, N, K;
     int dtype;              // lwo_dtype of A and W: F32, BF16, or FP8_E4M3 (A codes + per-row a_scale)
@@ -39,6 +39,8 @@ struct GemmArgs {
     const float* gate; int gate_ld; int rows_per_batch;
     const float* w_scale; int w_seg;   // fp8: per-segment weight scale (segment = w_seg output columns)
     const float* a_scale;              // fp8: per-row activation scale
+    int a_tiled;            // A in k-tiled rows (ktiled_off, R = K bytes)
+    int out_tiled;          // EPI_STORE / EPI_GELU: out in k-tiled rows (R = ldo bf16)
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
@@ -47,7 +49,8 @@ struct AttnArgs {
     const void* q; int ldq;     // row (b*Tq + t) holds head h at column h*dh
     const void* k; int ldk;     // row (b*Tk + t)
     const void* v; int ldv;
-    void* o; int ldo;           // row (b*Tq + t)
+    void* o; int ldo;           // row (b*Tq + t); k-tiled rows (R = ldo bf16) when o_tiled
+    int o_tiled;
     int B, H, Tq, Tk, dh;
     int dtype;                  // F32 or BF16 (q, k, v, o)
 };
@@ -64,12 +67,14 @@ hipError_t launch_mod_dit(const float* silu_cond, const void* w, const void* b, 
 hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* mod, int B, int D, hipStream_t st);
 // LayerNorm of the fp32 rows xr [M, D]; with mod, y = LN(x)(1 + mod[b, scale_chunk]) + mod[b, shift_chunk]
 // where b = row / T.  out_dt F32/BF16 writes `out`; FP8_E4M3 writes codes to `out` and row scales to out_scale.
+// out_tiled (BF16, FP8): `out` in k-tiled rows (ktiled_off, R = D elements).
 hipError_t launch_ln(const float* xr, int M, int D, int T, const float* mod, int shift_chunk, int scale_chunk,
-                     void* out, int out_dt, float* out_scale, hipStream_t st);
+                     void* out, int out_dt, float* out_scale, int out_tiled, hipStream_t st);
 // In-place RMSNorm of columns [0, D) (gain gq) and [D, 2D) (gain gk) of qkv rows (row stride 3D).
 hipError_t launch_rmsnorm_qk(void* qkv, int dt, int M, int D, const void* gq, const void* gk, hipStream_t st);
-// bf16 rows [M, N] -> e4m3 codes and per-row scales (dynamic amax / 448).
-hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, hipStream_t st);
+// bf16 rows [M, N] -> e4m3 codes and per-row scales (dynamic amax / 448); codes_tiled: codes in k-tiled rows.
+hipError_t launch_quant_rows(const void* in, int M, int N, uint8_t* codes, float* scales, int codes_tiled,
+                             hipStream_t st);
 hipError_t launch_checksum(const void* dev, uint64_t bytes, uint64_t* acc, hipStream_t st);
 hipError_t launch_checksum_compare(uint64_t* acc, uint64_t expect, hipStream_t st);
 hipError_t launch_zero_u64(uint64_t* p, int n, hipStream_t st);

@@ -27,7 +27,8 @@ lwo_status launched(hipError_t e, const char* what) {
 extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void* a, const float* a_scale,
                                     const void* w, const float* w_scale, int32_t w_seg, const void* bias, int32_t M,
                                     int32_t N, int32_t K, void* out, int32_t ldo, float* xr, int32_t ldx,
-                                    const float* gate, int32_t gate_ld, int32_t rows_per_gate, void* stream) {
+                                    const float* gate, int32_t gate_ld, int32_t rows_per_gate, int32_t a_layout,
+                                    int32_t out_layout, void* stream) {
     try {
         clear_error();
         if (dtype != LWO_F32 && dtype != LWO_BF16 && dtype != LWO_FP8_E4M3) return bad("linear: dtype");
@@ -47,6 +48,11 @@ extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void*
             if (epilogue == EPI_GATED && (!gate || gate_ld < N || gate_ld % 8 || rows_per_gate < 1 || !aligned16(gate)))
                 return bad("linear: gate (16-byte aligned), gate_ld >= N (a multiple of 8) and rows_per_gate required");
         }
+        if ((a_layout != LWO_ROWS && a_layout != LWO_KTILED) || (out_layout != LWO_ROWS && out_layout != LWO_KTILED))
+            return bad("linear: a_layout and out_layout must be LWO_ROWS or LWO_KTILED");
+        if (dtype == LWO_F32 && (a_layout || out_layout)) return bad("linear: k-tiled operands need BF16 or FP8");
+        if (out_layout && (epilogue > EPI_GELU || ldo % 32))
+            return bad("linear: a k-tiled out needs epilogue 0 or 1 and ldo a multiple of 32");
         if (!stream) return bad("linear: stream is NULL");
         GemmArgs g{};
         g.a = a; g.w = w; g.M = M; g.N = N; g.K = K; g.dtype = dtype;
@@ -54,6 +60,7 @@ extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void*
         g.epi = epilogue; g.bias = bias; g.out = out; g.ldo = ldo; g.xr = xr; g.ldx = ldx;
         g.gate = gate; g.gate_ld = gate_ld; g.rows_per_batch = rows_per_gate > 0 ? rows_per_gate : 1;
         g.w_scale = w_scale; g.w_seg = w_seg > 0 ? w_seg : 1; g.a_scale = a_scale;
+        g.a_tiled = a_layout; g.out_tiled = out_layout;
         return launched(launch_gemm(g, (hipStream_t)stream), "linear");
     } catch (const std::bad_alloc&) {
         return fail_alloc("lwo_op_linear");
@@ -66,7 +73,7 @@ extern "C" lwo_status lwo_op_linear(int32_t dtype, int32_t epilogue, const void*
 
 extern "C" lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq, const void* k, int32_t ldk,
                                        const void* v, int32_t ldv, void* o, int32_t ldo, int32_t batch, int32_t heads,
-                                       int32_t tq, int32_t tk, int32_t head_dim, void* stream) {
+                                       int32_t tq, int32_t tk, int32_t head_dim, int32_t o_layout, void* stream) {
     try {
         clear_error();
         if (dtype != LWO_F32 && dtype != LWO_BF16) return bad("attention: dtype must be F32 or BF16");
@@ -77,10 +84,12 @@ extern "C" lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq
         if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8) return bad("attention: leading dimensions must be multiples of 8");
         if (!q || !k || !v || !o || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
             return bad("attention: pointers must be 16-byte aligned device pointers");
+        if (o_layout != LWO_ROWS && o_layout != LWO_KTILED) return bad("attention: o_layout must be LWO_ROWS or LWO_KTILED");
+        if (o_layout && (dtype != LWO_BF16 || ldo % 32)) return bad("attention: a k-tiled o needs BF16 and ldo a multiple of 32");
         if (!stream) return bad("attention: stream is NULL");
         AttnArgs a{};
         a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv; a.o = o; a.ldo = ldo;
-        a.B = batch; a.H = heads; a.Tq = tq; a.Tk = tk; a.dh = head_dim; a.dtype = dtype;
+        a.B = batch; a.H = heads; a.Tq = tq; a.Tk = tk; a.dh = head_dim; a.dtype = dtype; a.o_tiled = o_layout;
         return launched(launch_attention(a, (hipStream_t)stream), "attention");
     } catch (const std::bad_alloc&) {
         return fail_alloc("lwo_op_attention");
@@ -93,7 +102,7 @@ extern "C" lwo_status lwo_op_attention(int32_t dtype, const void* q, int32_t ldq
 
 extern "C" lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int32_t rows_per_batch, const float* mod,
                                        int32_t shift_chunk, int32_t scale_chunk, void* out, int32_t out_dtype,
-                                       float* out_scale, void* stream) {
+                                       float* out_scale, int32_t out_layout, void* stream) {
     try {
         clear_error();
         if (M < 0 || D < 4 || D % 4 || D > 8192) return bad("layernorm: D must be a multiple of 4 and at most 8192");
@@ -102,9 +111,12 @@ extern "C" lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int
         if (mod && (rows_per_batch < 1 || shift_chunk < 0 || shift_chunk > 5 || scale_chunk < 0 || scale_chunk > 5 || !aligned16(mod)))
             return bad("layernorm: modulation arguments");
         if (out_dtype == LWO_FP8_E4M3 && !out_scale) return bad("layernorm: fp8 output needs out_scale");
+        if (out_layout != LWO_ROWS && out_layout != LWO_KTILED) return bad("layernorm: out_layout must be LWO_ROWS or LWO_KTILED");
+        if (out_layout && (out_dtype == LWO_F32 || (D * (out_dtype == LWO_BF16 ? 2 : 1)) % 64))
+            return bad("layernorm: a k-tiled out needs BF16 or FP8 rows of a multiple of 64 bytes");
         if (!stream) return bad("layernorm: stream is NULL");
         return launched(launch_ln(x, M, D, rows_per_batch > 0 ? rows_per_batch : 1, mod, shift_chunk, scale_chunk, out,
-                                  out_dtype, out_scale, (hipStream_t)stream), "layernorm");
+                                  out_dtype, out_scale, out_layout, (hipStream_t)stream), "layernorm");
     } catch (const std::bad_alloc&) {
         return fail_alloc("lwo_op_layernorm");
     } catch (const std::exception& e) {
@@ -115,13 +127,16 @@ extern "C" lwo_status lwo_op_layernorm(const float* x, int32_t M, int32_t D, int
 }
 
 extern "C" lwo_status lwo_op_quantize_rows(const void* in, int32_t M, int32_t N, uint8_t* codes, float* scales,
-                                           void* stream) {
+                                           int32_t codes_layout, void* stream) {
     try {
         clear_error();
         if (M < 0 || N < 8 || N % 8) return bad("quantize_rows: N must be a positive multiple of 8");
         if (!in || !codes || !scales || !aligned16(in) || ((uintptr_t)codes & 7u)) return bad("quantize_rows: pointers");
+        if (codes_layout != LWO_ROWS && codes_layout != LWO_KTILED)
+            return bad("quantize_rows: codes_layout must be LWO_ROWS or LWO_KTILED");
+        if (codes_layout && N % 64) return bad("quantize_rows: k-tiled codes need N a multiple of 64");
         if (!stream) return bad("quantize_rows: stream is NULL");
-        return launched(launch_quant_rows(in, M, N, codes, scales, (hipStream_t)stream), "quantize_rows");
+        return launched(launch_quant_rows(in, M, N, codes, scales, codes_layout, (hipStream_t)stream), "quantize_rows");
     } catch (const std::bad_alloc&) {
         return fail_alloc("lwo_op_quantize_rows");
     } catch (const std::exception& e) {
