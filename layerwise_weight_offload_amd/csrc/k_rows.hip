@@ -177,11 +177,16 @@ hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* 
 // which keeps the register count, and so the wavefronts per SIMD, where the
 // HBM stream needs them; their partial sums meet in LDS and are added in a fixed
 // order (first half + second half), so every output type sees the same floats.
+// k-tiled output (`tiled`): the workgroup's two rows (an even row and the next,
+// neighbours inside one 64-row tile) are staged in LDS (2 x D x out bytes of
+// dynamic LDS) and written as 128-byte runs, row 2b's 64 bytes of a tile
+// followed by row 2b + 1's, 16 bytes per lane.
 template <int OUT, bool MOD, int NV4>
 __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M, int D, int T,
                                             const float* __restrict__ mod, int shc, int scc,
                                             void* __restrict__ out, float* __restrict__ out_scale, int tiled) {
     __shared__ float red[3][2][2];                      // [quantity][row of the workgroup][half]
+    extern __shared__ __attribute__((aligned(16))) unsigned char ln_rows[];   // k-tiled output staging
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int rw = wave / 2, hf = wave % 2;             // row within the workgroup, half of the row
     const int row = blockIdx.x * 2 + rw;
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             v[i] = y;
         } else if (live && c < nh) {
             if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * cc4, y);
-            else if (tiled) store4((bf16*)((char*)out + ktiled_off(row, (size_t)8 * cc4, (size_t)2 * D)), y);
+            else if (tiled) store4((bf16*)(ln_rows + (size_t)rw * 2 * D) + 4 * cc4, y);
             else store4((bf16*)out + (size_t)row * D + 4 * cc4, y);
         }
     }
@@ -251,11 +256,23 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             const int c = lane + kWave * i;
             if (live && c < nh) {
                 uint32_t lo = pack2_e4m3(v[i].x * inv, v[i].y * inv), hi = pack2_e4m3(v[i].z * inv, v[i].w * inv);
-                uint8_t* dst = tiled ? (uint8_t*)out + ktiled_off(row, (size_t)4 * (c0 + c), (size_t)D) : o + 4 * (c0 + c);
+                uint8_t* dst = tiled ? ln_rows + (size_t)rw * D + 4 * (c0 + c) : o + 4 * (c0 + c);
                 *(uint32_t*)dst = lo | (hi << 16);
             }
         }
         if (live && lane == 0 && hf == 0) out_scale[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    if (OUT != 0 && tiled) {
+        __syncthreads();
+        const int R = OUT == 1 ? 2 * D : D, nq = (R / 64) * 8;   // 16-byte pieces of the two rows
+        const int r0 = blockIdx.x * 2;
+        const bool live1 = r0 + 1 < M;
+        unsigned char* g = (unsigned char*)out + ktiled_off(r0, 0, (size_t)R);   // row r0 + 1 follows at +64
+        for (int q = threadIdx.x; q < nq; q += blockDim.x) {
+            const int j = q >> 3, p = q & 7, rr = p >> 2;
+            if (rr && !live1) continue;
+            *(uint4*)(g + (size_t)j * 4096 + 16 * p) = *(const uint4*)(ln_rows + (size_t)rr * R + 64 * j + 16 * (p & 3));
+        }
     }
 }
 
@@ -264,9 +281,10 @@ static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float*
                               float* out_scale, int tiled, hipStream_t st) {
     const int need = ((D / 4 + 1) / 2 + kWave - 1) / kWave;
     dim3 grid((M + 1) / 2);
+    const size_t shm = tiled ? (size_t)2 * D * (OUT == 1 ? 2 : 1) : 0;   // two staged rows
 #define LWO_LN_CASE(NV)                                                                                     \
     if (need <= NV) {                                                                                       \
-        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, 0, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled);       \
+        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, shm, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled);     \
         return hipGetLastError();                                                                           \
     }
     LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(6) LWO_LN_CASE(8)
