@@ -48,10 +48,12 @@ namespace lwo {
 //    With lane 4y + c pointing at key K0 + y, columns d0 + 4c .. d0 + 4c + 3,
 //    lane j gets V[K0 .. K0 + 3][d0 + j]: four keys of one output column, in
 //    the key order of the probability operand.
-//  * The softmax reference point moves only when a score exceeds it by more
-//    than 2^8 (base-2 exponent 8); until then the probabilities and the row
-//    sum keep the older reference, which changes no result (both share it)
-//    and skips most rescales of the output accumulators.
+//  * The softmax reference point (the row max in base-2 exponent units) is
+//    set on a wavefront's first tile and then kept: the probabilities and the
+//    row sum share it, so any reference gives the same result up to rounding.
+//    A tile takes no row max unless its row sum passes 2^32 in some lane (a
+//    score far above the reference); such a tile recomputes its scores from
+//    LDS, moves the reference to the row max and rescales O and the row sum.
 
 // LDS reads issued as instructions the compiler does not track (their
 // completion is awaited with explicit lgkmcnt waits, so loads still in flight
@@ -174,58 +176,71 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
                         8 * (tc % 2);
     }
 
-    auto tile = [&](auto buf, int key0) {
+    // `first`: the wavefront's first tile (m_i = -inf in every lane).
+    auto tile = [&](auto buf, int key0, bool first) {
         constexpr int BO = decltype(buf)::value * TB;
         floatx16 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-        // ---- S^T = K Q^T for 64 keys
-        if constexpr (KS == 8) {
-            // four batches of four k-steps (batch u: 32-key half u / 2, k-steps
-            // 4 (u % 2) .. + 3); two batches in flight
-            intx4 kf[2][4];
-#define KREAD(u)                                                                  \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
-        LDS_RD128(kf[(u) % 2][i], kaddr[4 * ((u) % 2) + i], BO + ((u) / 2) * 32 * PITCH);
-            KREAD(0);
-            KREAD(1);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u < 3) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
-                else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    asm volatile("" : "+v"(kf[u % 2][i]));
-                    s[u / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[u % 2][i]),
-                                                                       __builtin_bit_cast(bf16x8, qf[4 * (u % 2) + i]),
-                                                                       s[u / 2], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);   // keep batch u's MFMAs ahead of the reads that reuse its registers
-                if (u == 0) { KREAD(2); }
-                if (u == 1) { KREAD(3); }
-            }
-#undef KREAD
-        } else {
-            // both 32-key halves in flight, then the MFMAs of each
-            intx4 kf[2][KS];
+        // ---- S^T = K Q^T for 64 keys (computed again from the same LDS tile
+        // on the rare path below); keys past Tk are masked to -inf
+        auto scores = [&]() {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int st = 0; st < KS; ++st) LDS_RD128(kf[t][st], kaddr[st], BO + t * 32 * PITCH);
-            asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(KS) : "memory");
+                for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+            if constexpr (KS == 8) {
+                // four batches of four k-steps (batch u: 32-key half u / 2, k-steps
+                // 4 (u % 2) .. + 3); two batches in flight
+                intx4 kf[2][4];
+#define KREAD(u)                                                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                         \
+        LDS_RD128(kf[(u) % 2][i], kaddr[4 * ((u) % 2) + i], BO + ((u) / 2) * 32 * PITCH);
+                KREAD(0);
+                KREAD(1);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                if (t == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                for (int u = 0; u < 4; ++u) {
+                    if (u < 3) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+                    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                for (int st = 0; st < KS; ++st) {
-                    asm volatile("" : "+v"(kf[t][st]));
-                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t][st]),
-                                                                   __builtin_bit_cast(bf16x8, qf[st]), s[t], 0, 0, 0);
+                    for (int i = 0; i < 4; ++i) {
+                        asm volatile("" : "+v"(kf[u % 2][i]));
+                        s[u / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[u % 2][i]),
+                                                                           __builtin_bit_cast(bf16x8, qf[4 * (u % 2) + i]),
+                                                                           s[u / 2], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // keep batch u's MFMAs ahead of the reads that reuse its registers
+                    if (u == 0) { KREAD(2); }
+                    if (u == 1) { KREAD(3); }
+                }
+#undef KREAD
+            } else {
+                // both 32-key halves in flight, then the MFMAs of each
+                intx4 kf[2][KS];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int st = 0; st < KS; ++st) LDS_RD128(kf[t][st], kaddr[st], BO + t * 32 * PITCH);
+                asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(KS) : "memory");
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if (t == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                    for (int st = 0; st < KS; ++st) {
+                        asm volatile("" : "+v"(kf[t][st]));
+                        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t][st]),
+                                                                       __builtin_bit_cast(bf16x8, qf[st]), s[t], 0, 0, 0);
+                    }
                 }
             }
-        }
+            // s[t][r]: key key0 + 32t + 8(r/4) + 4 half + r%4, query qi
+            if (key0 + BN > Tk) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (key0 + t * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= Tk) s[t][r] = -INFINITY;
+            }
+        };
+        scores();
         // V^T fragments of keys 0..31 (16 keys per k-step): read now, in flight
         // during the softmax below, whose two-half reductions use a lane swap
         // (VALU) rather than an LDS permute so that nothing waits for them early.
@@ -242,63 +257,76 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
             return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
         };
 
-        // s[t][r]: key key0 + 32t + 8(r/4) + 4 half + r%4, query qi
-        if (key0 + BN > Tk) {
+        // ---- Probabilities against the current reference point m_i (base-2
+        // exponent units) and their row sum, taken from the bf16 values the PV
+        // products use (two at a time, a dot product against (1, 1)).  The
+        // reference point does not follow the row max tile by tile: any m_i
+        // gives the same O and row sum up to rounding, as both share it, so the
+        // max is only taken when the probabilities would grow too large.  A tile
+        // whose row sum passes 2^32 in some lane (a score far above m_i, or the
+        // first tile, where m_i = -inf) recomputes its scores from the tile still
+        // in LDS, moves m_i to the row max, rescales O and the row sum, and
+        // recomputes the probabilities; the first tile goes straight to the max,
+        // and every other tile skips it.
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        bf16x8 pf[2][2];
+        float rs;
+        auto probs = [&]() {
+            const float nm = -m_i;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (key0 + t * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= Tk) s[t][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, nm));
+            const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+            float r0 = 0.0f, r1 = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pf[t][ks][e] = (bf16)s[t][ks * 8 + e];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bf16x2_t pp = {pf[t][ks][2 * e], pf[t][ks][2 * e + 1]};
+                        if (ks == 0) r0 = __builtin_amdgcn_fdot2_f32_bf16(pp, one, r0, false);
+                        else r1 = __builtin_amdgcn_fdot2_f32_bf16(pp, one, r1, false);
+                    }
+                }
+            rs = r0 + r1;
+        };
+        bool redo = first;
+        if (!first) {
+            probs();
+            redo = __ballot(!(rs <= 0x1p32f)) != 0;   // NaN-safe: a NaN sum takes this path too
+            if (redo) scores();
         }
-        float mx = s[0][0];
+        if (redo) {
+            float mx = s[0][0];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-        mx = swap_halves(mx, [](float u, float v) { return fmaxf(u, v); }) * sl2;
-        const bool need = mx > m_i + 8.0f;
-        if (__ballot(need)) {
-            const float m_new = need ? mx : m_i;
-            const float corr = __builtin_amdgcn_exp2f(m_i - m_new);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+            mx = swap_halves(mx, [](float u, float v) { return fmaxf(u, v); }) * sl2;
+            const float m_new = fmaxf(m_i, mx);
+            const float corr = __builtin_amdgcn_exp2f(m_i - m_new);   // 0 on the first tile, 1 where m_i stays
             l_i *= corr;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[nt][r] *= corr;
             m_i = m_new;
+            probs();
         }
-        const float nm = -m_i;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, nm));
-        // The row sum is taken from the bf16 probabilities the PV products use,
-        // two at a time with a dot product against (1, 1): 16 VALU operations
-        // per tile instead of 32 adds (0.6% faster at 32760 x 32760), and the
-        // denominator sums exactly the values that multiply V.
-        float rs = 0.0f;
 
         // ---- O^T += V^T P^T, one k-step (16 keys) at a time.  Keys 32..63's
         // fragments are read while keys 0..31's MFMAs run; every wait leaves at
         // most 2 NT reads outstanding (the counter holds 15).
         auto pv = [&](int t, int ks, intx2 (&vf)[2][NT][2]) {
-            bf16x8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[t][ks * 8 + e];
-            {
-                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-                const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bf16x2_t pp = {pf[2 * e], pf[2 * e + 1]};
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp, one, rs, false);
-                }
-            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 asm volatile("" : "+v"(vf[ks][nt][0]), "+v"(vf[ks][nt][1]));
                 const intx4 v4 = {vf[ks][nt][0][0], vf[ks][nt][0][1], vf[ks][nt][1][0], vf[ks][nt][1][1]};
-                oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pf, oacc[nt], 0, 0, 0);
+                oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v4), pf[t][ks], oacc[nt], 0, 0, 0);
             }
         };
         VREAD(1, 0, vb);
@@ -324,11 +352,11 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
         // barrier publishes every wavefront's loads and frees buffer 1 for tile j + 1.
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (t0 + j + 1 < tend) issue(std::integral_constant<int, 1>{}, (t0 + j + 1) * BN);
-        if (t0 + j < tend) tile(std::integral_constant<int, 0>{}, (t0 + j) * BN);
+        if (t0 + j < tend) tile(std::integral_constant<int, 0>{}, (t0 + j) * BN, j == 0);
         if (j + 1 >= nt0) break;
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (t0 + j + 2 < tend) issue(std::integral_constant<int, 0>{}, (t0 + j + 2) * BN);
-        if (t0 + j + 1 < tend) tile(std::integral_constant<int, 1>{}, (t0 + j + 1) * BN);
+        if (t0 + j + 1 < tend) tile(std::integral_constant<int, 1>{}, (t0 + j + 1) * BN, false);
     }
 
     if constexpr (KSP == 2) {

@@ -234,6 +234,43 @@ def test_attention_bf16(lib, B, H, Tq, Tk, d, fused, rows):
     _attn_case(lib, BF16, B, H, Tq, Tk, d, fused, rows, seed=Tq + Tk + d)
 
 
+@pytest.mark.parametrize("pattern,d,Tk", [("growing", 128, 1100), ("growing", 72, 1000), ("late_key", 128, 1100),
+                                          ("late_key", 64, 700)])
+def test_attention_bf16_reference_point_moves(lib, pattern, d, Tk):
+    """Scores that rise far above the first tiles' maximum: the kernel's
+    probabilities are taken against a reference point that it moves only when
+    a tile's row sum passes 2^32, so these inputs must take that path (key
+    norms growing 30x along the keys, or one key in the last tile scaled to
+    dominate about half of the queries) and still match the oracle."""
+    torch = _torch()
+    print(f"[attention bf16 reference] {pattern} d={d} Tk={Tk}", flush=True)
+    rng = np.random.default_rng(Tk + d + len(pattern))
+    B, H, Tq = 1, 2, 300
+    D = H * d
+    q32 = rng.standard_normal((B * Tq, D), dtype=np.float32)
+    k32 = rng.standard_normal((B * Tk, D), dtype=np.float32)
+    if pattern == "growing":
+        k32 *= (1.0 + 30.0 * np.arange(Tk, dtype=np.float32) / Tk)[:, None]
+    else:
+        k32[Tk - 3] = 2000.0 / np.sqrt(d)
+    v32 = rng.standard_normal((B * Tk, D), dtype=np.float32)
+    q, k, v = _bf16_dev(q32), _bf16_dev(k32), _bf16_dev(v32)
+    o = torch.empty((B * Tq, D), dtype=torch.bfloat16, device="cuda:0")
+    s = _stream()
+    lib.op_attention(BF16, q.data_ptr(), D, k.data_ptr(), D, v.data_ptr(), D, o.data_ptr(), D, B, H, Tq, Tk, d,
+                     s.cuda_stream)
+    s.synchronize()
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    ref = o_dit.attention_rows(Q, K, V, H)
+    mag = o_dit.attention_rows(Q, K, np.abs(V), H)
+    got = _f64(o)
+    tol = 2.0 ** -8 * (mag + np.abs(ref)) + 1e-5
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    print(f"[attention bf16 reference] max err/tol = {np.max(err / tol):.3f}", flush=True)
+    assert np.all(err <= tol), float(np.max(err / tol))
+
+
 @pytest.mark.parametrize("B,H,Tq,Tk,d", [(1, 4, 64, 64, 64), (2, 8, 200, 200, 72), (1, 2, 77, 40, 128)])
 def test_attention_f32(lib, B, H, Tq, Tk, d):
     _attn_case(lib, F32, B, H, Tq, Tk, d, Tq == Tk, Tq, seed=d + Tq)
