@@ -252,6 +252,7 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
         intx2 va[2][NT][2], vb[2][NT][2];
         VREAD(0, 0, va);
         VREAD(0, 1, va);
+        __builtin_amdgcn_sched_barrier(0);   // issue them before the softmax, not where PV needs them
         auto swap_halves = [](float x, auto op) {
             const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
             return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
