@@ -290,3 +290,37 @@ def test_ktiled_argument_validation(lib):
         with pytest.raises(lib.LwoError):
             print(f"[ktiled validation] case {i}", flush=True)
             call()
+
+
+@pytest.mark.parametrize("M", [1, 63, 65])
+def test_ktiled_band_edges(lib, M):
+    """One row, one row short of a band, one row past a band: every k-tiled producer and the
+    linear that reads its output give the row-major bits, and no padding byte is written."""
+    torch = _torch()
+    print(f"[ktiled edges] M={M}", flush=True)
+    rng = np.random.default_rng(M)
+    D, N = 256, 128
+    s = _stream()
+    x = torch.from_numpy(rng.standard_normal((M, D), dtype=np.float32)).to("cuda:0")
+    rows16 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda:0")
+    t16 = _tiled_out(M, 2 * D)
+    lib.op_layernorm(x.data_ptr(), M, D, rows16.data_ptr(), BF16, s.cuda_stream)
+    lib.op_layernorm(x.data_ptr(), M, D, t16.data_ptr(), BF16, s.cuda_stream, out_layout=KTILED)
+    codes = _tiled_out(M, D)
+    sc = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    lib.op_quantize_rows(rows16.data_ptr(), M, D, codes.data_ptr(), sc.data_ptr(), s.cuda_stream, codes_layout=KTILED)
+    w = torch.from_numpy(rng.standard_normal((N, D), dtype=np.float32) * 0.05).to(torch.bfloat16).to("cuda:0")
+    wt = torch.from_numpy(lib.tile_weight(BF16, _bytes(w).view(np.uint16))).to("cuda:0")
+    y_rows = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    y_t = _tiled_out(M, 2 * N)
+    lib.op_linear(BF16, 1, rows16.data_ptr(), wt.data_ptr(), M, N, D, s.cuda_stream, out=y_rows.data_ptr(), ldo=N)
+    lib.op_linear(BF16, 1, t16.data_ptr(), wt.data_ptr(), M, N, D, s.cuda_stream, out=y_t.data_ptr(), ldo=N,
+                  a_layout=KTILED, out_layout=KTILED)
+    s.synchronize()
+    g16, p16 = _untile(t16, M, 2 * D)
+    g8, p8 = _untile(codes, M, D)
+    gy, py = _untile(y_t, M, 2 * N)
+    assert np.array_equal(g16, _bytes(rows16)) and np.all(p16 == SENT)
+    ref_codes, ref_sc = codecs.quantize_rows_e4m3(rows16.float().cpu().numpy())
+    assert np.array_equal(g8, ref_codes) and np.array_equal(sc.cpu().numpy(), ref_sc) and np.all(p8 == SENT)
+    assert np.array_equal(gy, _bytes(y_rows)) and np.all(py == SENT)
