@@ -386,7 +386,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // tile's registers; those stages read at their own start.
     // Grouped look-ahead (below) for the fp8 single-k-step stages: 3-4% faster
     // on the 32760-token fp8 products, 1-3% slower on the 16x16x32 bf16 ones,
-    // which read their groups at the stage start (same-box A/B, same bits).
+    // which read their groups at the stage start (A/B on one machine, same output bits).
     constexpr bool LOOK = KS >= 4 || (NG > 1 && FP8);
     // Look-ahead stage: multiply the tiles in buffer B = kt % 4 while the next
     // k-step's fragments are read, the first of them having been read at the
