@@ -16,7 +16,7 @@
 // and the PV output to a multiple of 32 columns (72 -> 80 and 96); padded
 // columns are never stored.  Key and query tails are masked.
 //
-// k_attn_f32: one query per lane with fp32 FMA, for the fp32 workloads.
+// k_attn_f32: four lanes per query with fp32 FMA, for the fp32 workloads.
 #include <math.h>
 
 #include <type_traits>
@@ -409,20 +409,27 @@ __global__ __launch_bounds__(NW * KSP * 64, 2) void k_attn_tr(AttnArgs a) {
         }
 }
 
+// fp32: four lanes per query, each holding a quarter of the head's columns of
+// q and of the output; the score is the four partial dot products summed by
+// two lane exchanges (the same bits in all four lanes), then every lane runs
+// the same online softmax.  16 queries per 64-lane workgroup, 32-key tiles in
+// LDS shared by all of them.
 template <int DH>
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
+    constexpr int QL = 4, DS = DH / QL;   // lanes per query, columns per lane
+    static_assert(DH % QL == 0, "head dim");
     __shared__ float Ks[32][DH];
     __shared__ float Vs[32][DH];
     const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int qi = blockIdx.x * 64 + lane;
+    const int qi = blockIdx.x * (64 / QL) + lane / QL, d0 = (lane % QL) * DS;
     const float* Q = (const float*)a.q;
     const float* K = (const float*)a.k;
     const float* V = (const float*)a.v;
-    float q[DH], o[DH];
+    float q[DS], o[DS];
     const float scale = 1.0f / sqrtf((float)DH);
 #pragma unroll
-    for (int d = 0; d < DH; ++d) {
-        q[d] = qi < a.Tq ? Q[(size_t)(b * a.Tq + qi) * a.ldq + h * DH + d] * scale : 0.0f;
+    for (int d = 0; d < DS; ++d) {
+        q[d] = qi < a.Tq ? Q[(size_t)(b * a.Tq + qi) * a.ldq + h * DH + d0 + d] * scale : 0.0f;
         o[d] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
@@ -439,20 +446,22 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
         for (int j = 0; j < nk; ++j) {
             float s = 0.0f;
 #pragma unroll
-            for (int d = 0; d < DH; ++d) s += q[d] * Ks[j][d];
+            for (int d = 0; d < DS; ++d) s += q[d] * Ks[j][d0 + d];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
             const float mn = fmaxf(m, s);
             const float c = expf(m - mn), p = expf(s - mn);
             l = l * c + p;
 #pragma unroll
-            for (int d = 0; d < DH; ++d) o[d] = o[d] * c + p * Vs[j][d];
+            for (int d = 0; d < DS; ++d) o[d] = o[d] * c + p * Vs[j][d0 + d];
             m = mn;
         }
     }
     if (qi >= a.Tq) return;
-    float* O = (float*)a.o + (size_t)(b * a.Tq + qi) * a.ldo + h * DH;
+    float* O = (float*)a.o + (size_t)(b * a.Tq + qi) * a.ldo + h * DH + d0;
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) O[d] = o[d] * inv;
+    for (int d = 0; d < DS; ++d) O[d] = o[d] * inv;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
@@ -484,7 +493,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
             default: return hipErrorInvalidValue;
         }
     } else {
-        dim3 grid((a.Tq + 63) / 64, a.H, a.B);
+        dim3 grid((a.Tq + 15) / 16, a.H, a.B);   // 16 queries per workgroup
         switch (a.dh) {
             case 64: LWO_KL((k_attn_f32<64>), grid, 64, 0, st, a); break;
             case 72: LWO_KL((k_attn_f32<72>), grid, 64, 0, st, a); break;
