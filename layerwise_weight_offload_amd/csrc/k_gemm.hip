@@ -83,6 +83,73 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
         }
 }
 
+// A T x T tile (T = 32 or 64) with K split four ways inside a 1024-thread
+// workgroup, for grids too small to fill the chip with k_gemm_f32: group kg
+// (256 threads, (T / 16) x (T / 16) outputs each) sums k in [kg Kq, (kg + 1) Kq)
+// in k order, and group 0 adds the other groups' partial tiles in group order
+// (through LDS) before the epilogue, so the results do not depend on timing.
+template <int EPI, int T>
+__global__ __launch_bounds__(1024) void k_gemm_f32_splitk(GemmArgs g) {
+    constexpr int KG = 4, R = T / 16, LPR = 256 / T, LW = 16 / LPR;   // outputs per thread side; loaders per row; floats each
+    static_assert(T == 32 || T == 64, "tile");
+    __shared__ float As[KG][16][T + 4];
+    __shared__ float Ws[KG][16][T + 4];
+    __shared__ float red[KG - 1][T][T + 1];
+    const int kg = threadIdx.x / 256, tid = threadIdx.x % 256, tx = tid % 16, ty = tid / 16;
+    const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
+    const float* A = (const float*)g.a;
+    const float* W = (const float*)g.w;
+    const int lr = tid / LPR, lk = (tid % LPR) * LW;
+    const int Kq = (g.K / 16 + KG - 1) / KG * 16;   // every group runs Kq / 16 steps; columns past K read zeros
+    const int kb = kg * Kq;
+    float acc[R][R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[i][j] = 0.0f;
+    for (int k0 = kb; k0 < kb + Kq; k0 += 16) {
+        const bool kin = k0 < g.K;
+        float av[LW], wv[LW];
+#pragma unroll
+        for (int e = 0; e < LW; ++e) {
+            av[e] = (kin && m0 + lr < g.M) ? A[(size_t)(m0 + lr) * g.K + k0 + lk + e] : 0.0f;
+            wv[e] = (kin && n0 + lr < g.N) ? W[(size_t)(n0 + lr) * g.K + k0 + lk + e] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < LW; ++e) { As[kg][lk + e][lr] = av[e]; Ws[kg][lk + e][lr] = wv[e]; }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[R], b[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) { a[i] = As[kg][kk][ty * R + i]; b[i] = Ws[kg][kk][tx * R + i]; }
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int j = 0; j < R; ++j) acc[i][j] += a[i] * b[j];
+        }
+    }
+    if (kg > 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int j = 0; j < R; ++j) red[kg - 1][ty * R + i][tx * R + j] = acc[i][j];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            float v = acc[i][j];
+#pragma unroll
+            for (int r = 0; r < KG - 1; ++r) v += red[r][ty * R + i][tx * R + j];
+            const int m = m0 + ty * R + i, n = n0 + tx * R + j;
+            if (m < g.M && n < g.N) epilogue<EPI, float>(g, m, n, v);
+        }
+}
+
 // ------------------------------------------------------------------ MFMA tiles (bf16 / fp8)
 
 // Tile index -> (tile row, tile col).  Workgroups are handed to the 8 XCDs
@@ -621,7 +688,14 @@ template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     if (g.dtype == LWO_F32) {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
-        LWO_KL((k_gemm_f32<EPI>), grid, 256, 0, st, g);
+        // Under 64 tiles of 64x64 a few CUs would each run one wavefront per SIMD
+        // down the whole of K: 32x32 tiles (four times the workgroups), K split four ways.
+        if (grid.x * grid.y < 64 && g.K >= 64) {
+            dim3 g32((g.N + 31) / 32, (g.M + 31) / 32);
+            LWO_KL((k_gemm_f32_splitk<EPI, 32>), g32, 1024, 0, st, g);
+        } else {
+            LWO_KL((k_gemm_f32<EPI>), grid, 256, 0, st, g);
+        }
         return hipGetLastError();
     }
     // K rows are a multiple of 128 bytes (argument checks); the 256-row tiles
