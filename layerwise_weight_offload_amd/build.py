@@ -23,7 +23,7 @@ OUT = os.path.join(HERE, "liblwo.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["layout.cpp", "store.cpp", "cache.cpp", "ops.cpp", "block.hip", "k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_probe.hip",
+SOURCES = ["layout.cpp", "store.cpp", "cache.cpp", "ops.cpp", "block.hip", "k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_attn_f32.hip", "k_probe.hip",
            "noalloc.hip"]
 
 CFLAGS = [

@@ -56,6 +56,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t st);   // dtype F32 (launch_attention calls it)
 
 hipError_t launch_to_f32(const void* x, int dt, float* xr, size_t n, hipStream_t st);
 hipError_t launch_from_f32(const float* xr, void* x, int dt, size_t n, hipStream_t st);
