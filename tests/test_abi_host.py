@@ -308,3 +308,35 @@ def test_shard_build_validation_before_device(lib):
         with pytest.raises(lib.LwoError) as e:
             lib.build_shard_store(desc, 4, 3, extents=src)
         assert "device" in str(e.value)
+
+
+def test_op_layout_arguments_rejected_before_any_device_call(lib):
+    """The single-kernel entry points check their row-layout arguments (LWO_ROWS / LWO_KTILED) before
+    touching a device: every call below fails validation with LWO_EINVAL and a message, on a host with no
+    GPU.  The pointers are 16-byte aligned stand-ins that are never dereferenced."""
+    P, S = 0x100000, 0x200000   # stand-in device pointer and stream handle
+    F32, BF16, FP8, KT = 0, 1, 2, 1
+    bad = [
+        ("linear: k-tiled operands need BF16 or FP8",
+         lambda: lib.op_linear(F32, 0, P, P, 64, 64, 64, S, out=P, ldo=64, a_layout=KT)),
+        ("linear: a k-tiled out needs epilogue 0 or 1",
+         lambda: lib.op_linear(BF16, 2, P, P, 64, 64, 64, S, xr=P, ldx=64, gate=P, gate_ld=64, rows_per_gate=1,
+                               out_layout=KT)),
+        ("linear: a k-tiled out needs", lambda: lib.op_linear(BF16, 0, P, P, 64, 64, 64, S, out=P, ldo=72,
+                                                              out_layout=KT)),
+        ("linear: a_layout and out_layout", lambda: lib.op_linear(BF16, 0, P, P, 64, 64, 64, S, out=P, ldo=64,
+                                                                  a_layout=2)),
+        ("attention: a k-tiled o needs BF16",
+         lambda: lib.op_attention(F32, P, 64, P, 64, P, 64, P, 64, 1, 1, 4, 4, 64, S, o_layout=KT)),
+        ("attention: o_layout", lambda: lib.op_attention(BF16, P, 64, P, 64, P, 64, P, 64, 1, 1, 4, 4, 64, S,
+                                                         o_layout=-1)),
+        ("layernorm: a k-tiled out needs", lambda: lib.op_layernorm(P, 4, 64, P, F32, S, out_layout=KT)),
+        ("layernorm: a k-tiled out needs", lambda: lib.op_layernorm(P, 4, 48, P, FP8, S, out_scale=P,
+                                                                    out_layout=KT)),
+        ("quantize_rows: k-tiled codes need N a multiple of 64",
+         lambda: lib.op_quantize_rows(P, 4, 72, P, P, S, codes_layout=KT)),
+    ]
+    for msg, call in bad:
+        with pytest.raises(lib.LwoError) as e:
+            call()
+        assert e.value.status == 1 and msg in str(e.value), (msg, str(e.value))
