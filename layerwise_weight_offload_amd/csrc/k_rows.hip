@@ -5,8 +5,8 @@
 // The row kernels keep their row in registers, so LayerNorm takes its mean
 // and variance in two exact passes and the quantiser its amax and codes
 // without re-reading HBM: one 64-lane wavefront per row (q/k RMSNorm, fp8
-// quantisation) or two per row, each with half of it (LayerNorm); four
-// wavefronts share a 256-thread workgroup.
+// quantisation, LayerNorm up to 2048 wide) or two per row, each with half of
+// it (wider LayerNorm); four wavefronts share a 256-thread workgroup.
 #include "../../include/lwo.h"
 #include "kcommon.h"
 #include "kernels.h"
@@ -69,43 +69,54 @@ __global__ void k_silu(const T* __restrict__ in, float* __restrict__ out, int n)
 
 // A GEMV over the [6D, D] weight, bound by reading it once: 16 lanes own one
 // row, a workgroup of NT threads owns NT / 16 rows (512: the DiT-XL matrix in
-// one round of workgroups, one per CU).  K goes in windows of 16 16-byte loads per
-// lane.  Each thread first loads its share of the window's SiLU(cond)
-// (computed once per step, up to four batches) into registers, then issues
-// the weight loads, then stages the SiLU values into LDS: both sets of loads
-// are in flight together, so the window costs one memory round trip.
-template <typename T, int NT>
-__global__ __launch_bounds__(NT) void k_mod_dit(const float* __restrict__ sc_in, const T* __restrict__ w,
+// one round of workgroups, one per CU).  K goes in windows of CL 16-byte loads
+// per lane, CL sized to the row (the DiT-XL row is 9 loads).  Each thread first
+// loads its share of the window's SiLU(cond) (computed once per step, up to
+// four batches), then issues the weight loads, then stages the SiLU values
+// into LDS: both sets of loads are in flight together, so the window costs one
+// memory round trip, and the products of a load start as soon as it lands.
+// For that every load is unconditional (a lane past the row end re-reads the
+// row's last 16 bytes, a SiLU value past the window end goes to a spare LDS
+// slot), so the compiler's wait counts are exact instead of draining all loads
+// at the first use; the scheduling barrier and the weight pointer without
+// __restrict__ keep the weight loads ahead of the workgroup barrier (loads
+// through a restrict pointer are free to sink to their use).  The bias is read
+// with the rest, once.  ONE: a single window and at most four batches, so the
+// kernel is straight-line code (a loop would make its head wait for every
+// load still in flight, the bias's included).
+template <typename T, int NT, int CL, bool ONE>
+__global__ __launch_bounds__(NT) void k_mod_dit(const float* __restrict__ sc_in, const T* w,
                                                  const T* __restrict__ bias, float* __restrict__ mod, int B, int D) {
     constexpr int EV = 16 / sizeof(T);                  // elements per 16-byte load (8 bf16, 4 f32)
-    constexpr int CL = 16, WIN = CL * 16 * EV;          // loads per lane per window, window elements
-    __shared__ float sc[4][WIN];
-    static_assert(WIN % NT == 0 && NT % 16 == 0, "workgroup size");
+    constexpr int WIN = CL * 16 * EV;                   // window elements
+    constexpr int SPT = (4 * WIN + NT - 1) / NT;        // SiLU values per thread and window (four batches)
+    __shared__ __attribute__((aligned(16))) float scf[4 * WIN + kWave];
+    float (*sc)[WIN] = (float (*)[WIN])scf;
     const int n = blockIdx.x * (NT / 16) + threadIdx.x / 16, l16 = threadIdx.x % 16;
-    const T* wr = w + (size_t)min(n, 6 * D - 1) * D;
-    for (int b0 = 0; b0 < B; b0 += 4) {
-        const int nb = min(4, B - b0);
+    const int nr = min(n, 6 * D - 1);
+    const T* wr = w + (size_t)nr * D;
+    const T bq = bias[nr];
+    const int nbb = ONE ? 1 : (B + 3) / 4, nwin = ONE ? 1 : (D + WIN - 1) / WIN;
+    for (int bb = 0; bb < nbb; ++bb) {
+        const int b0 = bb * 4, nb = min(4, B - b0);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < D; k0 += WIN) {
-            const int wn = min(WIN, D - k0);
-            constexpr int SPT = 4 * WIN / NT;           // SiLU values per thread and window (four batches)
+        for (int wi = 0; wi < nwin; ++wi) {
+            const int k0 = wi * WIN, wn = min(WIN, D - k0);
             float sv[SPT];
 #pragma unroll
             for (int t = 0; t < SPT; ++t) {
-                const int j = t / (WIN / NT), kk = (t % (WIN / NT)) * NT + threadIdx.x;
-                sv[t] = (j < nb && kk < wn) ? sc_in[(size_t)(b0 + j) * D + k0 + kk] : 0.0f;
+                const int q = t * NT + threadIdx.x, j = q / WIN, kk = q % WIN;
+                sv[t] = sc_in[j < nb && kk < wn ? (size_t)(b0 + j) * D + k0 + kk : 0];
             }
             intx4 raw[CL];
 #pragma unroll
-            for (int i = 0; i < CL; ++i) {
-                const int k = k0 + (i * 16 + l16) * EV;
-                raw[i] = k < D ? *(const intx4*)(wr + k) : intx4{0, 0, 0, 0};
-            }
+            for (int i = 0; i < CL; ++i) raw[i] = *(const intx4*)(wr + min(k0 + (i * 16 + l16) * EV, D - EV));
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();                            // the previous window's reads are done
 #pragma unroll
             for (int t = 0; t < SPT; ++t) {
-                const int j = t / (WIN / NT), kk = (t % (WIN / NT)) * NT + threadIdx.x;
-                if (j < nb && kk < wn) sc[j][kk] = sv[t];
+                const int q = t * NT + threadIdx.x, j = q / WIN, kk = q % WIN;
+                scf[j < nb && kk < wn ? j * WIN + kk : 4 * WIN + threadIdx.x % kWave] = sv[t];
             }
             __syncthreads();
 #pragma unroll
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(NT) void k_mod_dit(const float* __restrict__ sc_in,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float v = row16_reduce(acc[j], [](float a, float b) { return a + b; });
-            if (l16 == 0 && n < 6 * D && j < nb) mod[(size_t)(b0 + j) * 6 * D + n] = v + to_f(bias[n]);
+            if (l16 == 0 && n < 6 * D && j < nb) mod[(size_t)(b0 + j) * 6 * D + n] = v + to_f(bq);
         }
     }
 }
@@ -153,13 +164,28 @@ hipError_t launch_silu(const void* in, int dt, float* out, int n, hipStream_t st
     return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t mod_dit_dispatch(const float* silu_cond, const T* w, const T* b, float* mod, int B, int D,
+                                   hipStream_t st) {
+    constexpr int EV = 16 / sizeof(T);
+    const int nch = (D + 16 * EV - 1) / (16 * EV);      // 16-byte loads per lane for one row
+    const dim3 grid((6 * D + 31) / 32);
+#define LWO_MOD_CASE(C)                                                                                     \
+    if (B <= 4 && nch <= C) {                                                                               \
+        LWO_KL((k_mod_dit<T, 512, C, true>), grid, 512, 0, st, silu_cond, w, b, mod, B, D);                  \
+        return hipGetLastError();                                                                           \
+    }
+    LWO_MOD_CASE(2) LWO_MOD_CASE(4) LWO_MOD_CASE(5) LWO_MOD_CASE(9) LWO_MOD_CASE(16)
+#undef LWO_MOD_CASE
+    LWO_KL((k_mod_dit<T, 512, 16, false>), grid, 512, 0, st, silu_cond, w, b, mod, B, D);
+    return hipGetLastError();
+}
+
 hipError_t launch_mod_dit(const float* silu_cond, const void* w, const void* b, int dt, float* mod, int B, int D,
                           hipStream_t st) {
     if (D < 8 || D % 8) return hipErrorInvalidValue;
-    const dim3 grid((6 * D + 31) / 32);
-    if (dt == LWO_F32) LWO_KL((k_mod_dit<float, 512>), grid, 512, 0, st, silu_cond, (const float*)w, (const float*)b, mod, B, D);
-    else LWO_KL((k_mod_dit<bf16, 512>), grid, 512, 0, st, silu_cond, (const bf16*)w, (const bf16*)b, mod, B, D);
-    return hipGetLastError();
+    if (dt == LWO_F32) return mod_dit_dispatch(silu_cond, (const float*)w, (const float*)b, mod, B, D, st);
+    return mod_dit_dispatch(silu_cond, (const bf16*)w, (const bf16*)b, mod, B, D, st);
 }
 
 hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* mod, int B, int D, hipStream_t st) {
@@ -171,41 +197,56 @@ hipError_t launch_mod_video(const void* cond, const void* table, int dt, float* 
 
 // ------------------------------------------------------------------ LayerNorm (+ modulation, + fp8)
 
-// OUT: 0 float, 1 bf16, 2 fp8 codes + row scale.  Two wavefronts share a row,
-// each holding half of it in registers (the first half has the odd float4 chunk,
-// NV4 chunks per lane, >= ceil(D / 8) / 64),
+// OUT: 0 float, 1 bf16, 2 fp8 codes + row scale.  WPR wavefronts share a row.
+// WPR 2 (wide rows): each wavefront holds half of the row in registers (the
+// first half has the odd float4 chunk, NV4 chunks per lane, >= ceil(D / 8) / 64),
 // which keeps the register count, and so the wavefronts per SIMD, where the
 // HBM stream needs them; their partial sums meet in LDS and are added in a fixed
-// order (first half + second half), so every output type sees the same floats.
-// k-tiled output (`tiled`): the workgroup's two rows (an even row and the next,
-// neighbours inside one 64-row tile) are staged in LDS (2 x D x out bytes of
-// dynamic LDS) and written as 128-byte runs, row 2b's 64 bytes of a tile
-// followed by row 2b + 1's, 16 bytes per lane.
-template <int OUT, bool MOD, int NV4>
+// order (first half + second half).  WPR 1 (rows up to 2048 wide): one
+// wavefront holds the whole row, so the statistics need no LDS exchange and no
+// barrier, and the modulation's scale and shift are loaded with the row
+// instead of after the statistics.  The choice depends on D only, so every
+// output type and layout of one width sees the same floats.
+// k-tiled output (`tiled`): the workgroup's RPW rows (consecutive rows inside one
+// 64-row tile) are staged in LDS (RPW x D x out bytes of dynamic LDS) and
+// written as runs of RPW x 64 bytes, 16 bytes per lane.
+template <int OUT, bool MOD, int NV4, int WPR>
 __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M, int D, int T,
                                             const float* __restrict__ mod, int shc, int scc,
                                             void* __restrict__ out, float* __restrict__ out_scale, int tiled) {
-    __shared__ float red[3][2][2];                      // [quantity][row of the workgroup][half]
+    constexpr int RPW = 4 / WPR;                        // rows per workgroup
+    constexpr bool PF = MOD && WPR == 1;                // scale and shift loaded with the row
+    __shared__ float red[3][RPW][WPR];                  // [quantity][row of the workgroup][half]
     extern __shared__ __attribute__((aligned(16))) unsigned char ln_rows[];   // k-tiled output staging
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int rw = wave / 2, hf = wave % 2;             // row within the workgroup, half of the row
-    const int row = blockIdx.x * 2 + rw;
+    const int rw = wave / WPR, hf = wave % WPR;         // row within the workgroup, half of the row
+    const int row = blockIdx.x * RPW + rw;
     const bool live = row < M;
-    const int n4 = D / 4, nh0 = (n4 + 1) / 2;
+    const int n4 = D / 4, nh0 = WPR == 2 ? (n4 + 1) / 2 : n4;
     const int nh = hf ? n4 - nh0 : nh0, c0 = hf ? nh0 : 0;   // float4 chunks of this half, first chunk
     const float* x = xr + (size_t)(live ? row : 0) * D;
-    float4 v[NV4];
+    const int bi = (live ? row : 0) / T;
+    const float* shift = MOD ? mod + ((size_t)bi * 6 + shc) * D : nullptr;
+    const float* scale = MOD ? mod + ((size_t)bi * 6 + scc) * D : nullptr;
+    float4 v[NV4], scv[PF ? NV4 : 1], shv[PF ? NV4 : 1];
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
         const int c = lane + kWave * i;
         v[i] = live && c < nh ? load4(x + 4 * (c0 + c)) : make_float4(0.f, 0.f, 0.f, 0.f);
-        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        if constexpr (PF) {
+            if (c < nh) { scv[i] = load4(scale + 4 * (c0 + c)); shv[i] = load4(shift + 4 * (c0 + c)); }
+        }
     }
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     s = wave_sum(s);
-    if (lane == 0) red[0][rw][hf] = s;
-    __syncthreads();
-    const float mean = (red[0][rw][0] + red[0][rw][1]) / (float)D;
+    if constexpr (WPR == 2) {
+        if (lane == 0) red[0][rw][hf] = s;
+        __syncthreads();
+        s = red[0][rw][0] + red[0][rw][1];
+    }
+    const float mean = s / (float)D;
     float s2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
@@ -216,12 +257,14 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
         }
     }
     s2 = wave_sum(s2);
-    if (lane == 0) red[1][rw][hf] = s2;
-    __syncthreads();
-    const float rstd = 1.0f / sqrtf((red[1][rw][0] + red[1][rw][1]) / (float)D + 1e-6f);
-    const int bi = (live ? row : 0) / T;
-    const float* shift = MOD ? mod + ((size_t)bi * 6 + shc) * D : nullptr;
-    const float* scale = MOD ? mod + ((size_t)bi * 6 + scc) * D : nullptr;
+    if constexpr (WPR == 2) {
+        if (lane == 0) red[1][rw][hf] = s2;
+        __syncthreads();
+        s2 = red[1][rw][0] + red[1][rw][1];
+    }
+    const float rstd = 1.0f / sqrtf(s2 / (float)D + 1e-6f);
+    constexpr int OB = OUT == 0 ? 4 : OUT == 1 ? 2 : 1; // output bytes per element
+    unsigned char* stage = ln_rows + (size_t)rw * D * OB;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
@@ -229,7 +272,9 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
         float4 y = make_float4((v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd,
                                (v[i].w - mean) * rstd);
         if (MOD && c < nh) {
-            const float4 sc = load4(scale + 4 * cc4), sh = load4(shift + 4 * cc4);
+            float4 sc, sh;
+            if constexpr (PF) { sc = scv[i]; sh = shv[i]; }
+            else { sc = load4(scale + 4 * cc4); sh = load4(shift + 4 * cc4); }
             y.x = y.x * (1.0f + sc.x) + sh.x;
             y.y = y.y * (1.0f + sc.y) + sh.y;
             y.z = y.z * (1.0f + sc.z) + sh.z;
@@ -240,15 +285,17 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             v[i] = y;
         } else if (live && c < nh) {
             if (OUT == 0) store4((float*)out + (size_t)row * D + 4 * cc4, y);
-            else if (tiled) store4((bf16*)(ln_rows + (size_t)rw * 2 * D) + 4 * cc4, y);
+            else if (tiled) store4((bf16*)stage + 4 * cc4, y);
             else store4((bf16*)out + (size_t)row * D + 4 * cc4, y);
         }
     }
     if (OUT == 2) {
         amax = wave_max(amax);
-        if (lane == 0) red[2][rw][hf] = amax;
-        __syncthreads();
-        amax = fmaxf(red[2][rw][0], red[2][rw][1]);
+        if constexpr (WPR == 2) {
+            if (lane == 0) red[2][rw][hf] = amax;
+            __syncthreads();
+            amax = fmaxf(red[2][rw][0], red[2][rw][1]);
+        }
         const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
         uint8_t* o = (uint8_t*)out + (size_t)row * D;
 #pragma unroll
@@ -256,7 +303,7 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
             const int c = lane + kWave * i;
             if (live && c < nh) {
                 uint32_t lo = pack2_e4m3(v[i].x * inv, v[i].y * inv), hi = pack2_e4m3(v[i].z * inv, v[i].w * inv);
-                uint8_t* dst = tiled ? ln_rows + (size_t)rw * D + 4 * (c0 + c) : o + 4 * (c0 + c);
+                uint8_t* dst = tiled ? stage + 4 * (c0 + c) : o + 4 * (c0 + c);
                 *(uint32_t*)dst = lo | (hi << 16);
             }
         }
@@ -264,13 +311,12 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
     }
     if (OUT != 0 && tiled) {
         __syncthreads();
-        const int R = OUT == 1 ? 2 * D : D, nq = (R / 64) * 8;   // 16-byte pieces of the two rows
-        const int r0 = blockIdx.x * 2;
-        const bool live1 = r0 + 1 < M;
-        unsigned char* g = (unsigned char*)out + ktiled_off(r0, 0, (size_t)R);   // row r0 + 1 follows at +64
+        const int R = D * OB, nq = (R / 64) * 4 * RPW;  // 16-byte pieces of the staged rows
+        const int r0 = blockIdx.x * RPW;
+        unsigned char* g = (unsigned char*)out + ktiled_off(r0, 0, (size_t)R);   // row r0 + k follows at +64 k
         for (int q = threadIdx.x; q < nq; q += blockDim.x) {
-            const int j = q >> 3, p = q & 7, rr = p >> 2;
-            if (rr && !live1) continue;
+            const int j = q / (4 * RPW), p = q % (4 * RPW), rr = p >> 2;
+            if (r0 + rr >= M) continue;
             *(uint4*)(g + (size_t)j * 4096 + 16 * p) = *(const uint4*)(ln_rows + (size_t)rr * R + 64 * j + 16 * (p & 3));
         }
     }
@@ -279,15 +325,23 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ xr, int M,
 template <int OUT, bool MOD>
 static hipError_t ln_dispatch(const float* xr, int M, int D, int T, const float* mod, int shc, int scc, void* out,
                               float* out_scale, int tiled, hipStream_t st) {
-    const int need = ((D / 4 + 1) / 2 + kWave - 1) / kWave;
-    dim3 grid((M + 1) / 2);
-    const size_t shm = tiled ? (size_t)2 * D * (OUT == 1 ? 2 : 1) : 0;   // two staged rows
+    const bool one = D <= 2048;                         // one wavefront per row
+    const int rpw = one ? 4 : 2;
+    const int need = one ? (D / 4 + kWave - 1) / kWave : ((D / 4 + 1) / 2 + kWave - 1) / kWave;
+    dim3 grid((M + rpw - 1) / rpw);
+    const size_t shm = tiled ? (size_t)rpw * D * (OUT == 1 ? 2 : 1) : 0;   // staged rows
 #define LWO_LN_CASE(NV)                                                                                     \
     if (need <= NV) {                                                                                       \
-        LWO_KL((k_ln<OUT, MOD, NV>), grid, 256, shm, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled);     \
+        if constexpr (NV <= 8) {                        /* one wavefront per row: need <= 8 */              \
+            if (one) {                                                                                      \
+                LWO_KL((k_ln<OUT, MOD, NV, 1>), grid, 256, shm, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled); \
+                return hipGetLastError();                                                                   \
+            }                                                                                               \
+        }                                                                                                   \
+        LWO_KL((k_ln<OUT, MOD, NV, 2>), grid, 256, shm, st, xr, M, D, T, mod, shc, scc, out, out_scale, tiled);     \
         return hipGetLastError();                                                                           \
     }
-    LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(6) LWO_LN_CASE(8)
+    LWO_LN_CASE(1) LWO_LN_CASE(2) LWO_LN_CASE(3) LWO_LN_CASE(4) LWO_LN_CASE(5) LWO_LN_CASE(6) LWO_LN_CASE(8)
     LWO_LN_CASE(10) LWO_LN_CASE(12) LWO_LN_CASE(16)
 #undef LWO_LN_CASE
     return hipErrorInvalidValue;
