@@ -204,6 +204,13 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
+// The gated epilogue in two forms: EPI_GATED reads one gate row per tile and
+// serves shapes where no tile spans two batches (one batch, or rows per batch
+// a multiple of the tile height); EPI_GATED_ROWS reads the gate row of each
+// output row.  Kept apart so that the common form has no per-row load behind a
+// branch: the compiler's wait after such a branch drains every load in flight.
+constexpr int EPI_GATED_ROWS = 4;
+
 template <int BM, int BN, int SB, bool FP8, int EPI, int NWN = 2, bool M16 = false>
 __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // 2 x NWN wavefronts, each owning (BM/2) x (BN/NWN) outputs = TM x TN MFMA blocks of RB x RB
@@ -583,7 +590,12 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // pass) and applies the epilogue with 8- or 16-byte global accesses.  The
     // residual forms load the fp32 residual rows of slice i + 1 before slice
     // i's LDS round trip, so the slices' load latencies overlap, and read the
-    // gate row once when the tile's rows all lie in one batch.
+    // gate row once when the tile's rows all lie in one batch.  Every load is
+    // unconditional (rows past M and columns past N read row M - 1 and column
+    // 0, and only the stores are masked), so the compiler's wait counts are
+    // exact: a load under a lane condition makes the waits that follow it drain
+    // every load in flight, which had put each residual load of the prefetch
+    // one round trip behind the previous one.
     constexpr int CW = BN / NWN, CH = CW / 4, RPP = kWave / CH, NP = 32 / RPP, PB = NP < 8 ? NP : 8;
     constexpr bool RES = EPI >= EPI_GATED;
     static_assert((NW / 4) * 32 * CW * 4 <= AB, "epilogue staging fits the A buffers");
@@ -592,97 +604,106 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     const int c4 = elane % CH, rr = elane / CH;           // float4 column chunk and row-in-pass of this elane
     const int nb = n0 + ewn * CW + 4 * c4;               // its first output column (CW = BN / NWN)
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
+    const int nbl = ncol ? nb : 0;                      // the column its loads read
     const int mw = m0 + ewm * (BM / 2);                  // first row of this wavefront's block
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (ncol && g.bias) {
-        const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nb);
+    if (g.bias) {
+        const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nbl);
         bias4 = make_float4((float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]);
     }
-    if (FP8 && ncol)
-        ws4 = make_float4(g.w_scale[nb / g.w_seg], g.w_scale[(nb + 1) / g.w_seg], g.w_scale[(nb + 2) / g.w_seg],
-                          g.w_scale[(nb + 3) / g.w_seg]);
+    if (FP8)
+        ws4 = make_float4(g.w_scale[nbl / g.w_seg], g.w_scale[(nbl + 1) / g.w_seg], g.w_scale[(nbl + 2) / g.w_seg],
+                          g.w_scale[(nbl + 3) / g.w_seg]);
     float4 xq[2][NP];                                   // residual rows of two slices (residual forms)
     auto load_x = [&](int i, float4 (&dst)[NP]) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int m = mw + i * 32 + p * RPP + rr;
-            if (ncol && m < g.M) dst[p] = *(const float4*)(g.xr + (size_t)m * g.ldx + nb);
+            const int m = min(mw + i * 32 + p * RPP + rr, g.M - 1);
+            dst[p] = *(const float4*)(g.xr + (size_t)m * g.ldx + nbl);
         }
     };
-    bool one_batch = false;
-    float4 g1 = make_float4(1.f, 1.f, 1.f, 1.f);
-    if constexpr (EPI == EPI_GATED) {
-        const int bfirst = m0 / g.rows_per_batch, blast = (min(m0 + BM, g.M) - 1) / g.rows_per_batch;
-        one_batch = bfirst == blast;
-        if (one_batch && ncol) g1 = *(const float4*)(g.gate + (size_t)bfirst * g.gate_ld + nb);
-    }
-    if constexpr (RES) load_x(0, xq[0]);
+    float4 g1 = make_float4(1.f, 1.f, 1.f, 1.f);     // the tile's gate row (EPI_GATED)
+    if constexpr (EPI == EPI_GATED) g1 = *(const float4*)(g.gate + (size_t)(m0 / g.rows_per_batch) * g.gate_ld + nbl);
+    {
+        if constexpr (RES) load_x(0, xq[0]);
 #pragma unroll
-    for (int i = 0; i < TS; ++i) {
-        if constexpr (RES) {
-            if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
-        }
-        if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: elane holds column elane % 16, rows 4 (elane / 16) + r
+        for (int i = 0; i < TS; ++i) {
+            if constexpr (RES) {
+                if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
+            }
+            if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: elane holds column elane % 16, rows 4 (elane / 16) + r
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            lds[(sb * 16 + 4 * (elane / 16) + r) * CW + j * 16 + elane % 16] = acc[2 * i + sb][j][r];
+            } else {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        lds[(sb * 16 + 4 * (elane / 16) + r) * CW + j * 16 + elane % 16] = acc[2 * i + sb][j][r];
-        } else {
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    lds[(8 * (r / 4) + 4 * ehalf + (r % 4)) * CW + j * 32 + el32] = acc[i][j][r];
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
-#pragma unroll
-        for (int h = 0; h < NP / PB; ++h) {
-            float4 v[PB];
-            int mrow[PB];
-#pragma unroll
-            for (int it = 0; it < PB; ++it) {
-                const int row = (h * PB + it) * RPP + rr;
-                mrow[it] = mw + i * 32 + row;
-                float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
-                if (FP8) {
-                    const float as = mrow[it] < g.M ? g.a_scale[mrow[it]] : 0.0f;
-                    a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
-                }
-                v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
+                    for (int r = 0; r < 16; ++r)
+                        lds[(8 * (r / 4) + 4 * ehalf + (r % 4)) * CW + j * 32 + el32] = acc[i][j][r];
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
 #pragma unroll
-            for (int it = 0; it < PB; ++it) {
-                if (!ncol || mrow[it] >= g.M) continue;
-                const float4 y = v[it];
-                if constexpr (EPI <= EPI_GELU) {
-                    bf16x4 o;
-                    if (EPI == EPI_GELU) {
-                        o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
-                        o[2] = (bf16)gelu_tanh(y.z); o[3] = (bf16)gelu_tanh(y.w);
-                    } else {
-                        o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
+            for (int h = 0; h < NP / PB; ++h) {
+                float4 v[PB];
+                int mrow[PB];
+#pragma unroll
+                for (int it = 0; it < PB; ++it) {
+                    const int row = (h * PB + it) * RPP + rr;
+                    mrow[it] = mw + i * 32 + row;
+                    float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
+                    if (FP8) {
+                        const float as = g.a_scale[min(mrow[it], g.M - 1)];
+                        a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
                     }
-                    bf16* dst = g.out_tiled ? (bf16*)((char*)g.out + ktiled_off(mrow[it], (size_t)2 * nb, (size_t)2 * g.ldo))
-                                            : (bf16*)g.out + (size_t)mrow[it] * g.ldo + nb;
-                    *(bf16x4*)dst = o;
-                } else {
-                    const float4 x = xq[i % 2][h * PB + it];
-                    float4 gg = g1;
-                    if (EPI == EPI_GATED && !one_batch)
-                        gg = *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb);
-                    *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
-                        make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
+                    v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
+                }
+#pragma unroll
+                for (int it = 0; it < PB; ++it) {
+                    if (!ncol || mrow[it] >= g.M) continue;
+                    const float4 y = v[it];
+                    if constexpr (EPI <= EPI_GELU) {
+                        bf16x4 o;
+                        if (EPI == EPI_GELU) {
+                            o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
+                            o[2] = (bf16)gelu_tanh(y.z); o[3] = (bf16)gelu_tanh(y.w);
+                        } else {
+                            o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
+                        }
+                        bf16* dst = g.out_tiled ? (bf16*)((char*)g.out + ktiled_off(mrow[it], (size_t)2 * nb, (size_t)2 * g.ldo))
+                                                : (bf16*)g.out + (size_t)mrow[it] * g.ldo + nb;
+                        *(bf16x4*)dst = o;
+                    } else {
+                        const float4 x = xq[i % 2][h * PB + it];
+                        float4 gg = g1;
+                        if constexpr (EPI == EPI_GATED_ROWS)
+                            gg = *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb);
+                        *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
+                            make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
+                    }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next slice overwrites
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next slice overwrites
     }
 }
 
 // ------------------------------------------------------------------ launch
+
+template <int EPI, int BM, int BN, int SB, bool F8, int NWN = 2, bool M16 = false>
+static void launch_deep(const GemmArgs& g, int grid, int threads, hipStream_t st) {
+    if constexpr (EPI == EPI_GATED) {
+        if (g.rows_per_batch < g.M && g.rows_per_batch % BM) {   // a batch boundary inside some tile
+            LWO_KL((k_gemm_deep<BM, BN, SB, F8, EPI_GATED_ROWS, NWN, M16>), grid, threads, 0, st, g);
+            return;
+        }
+    }
+    LWO_KL((k_gemm_deep<BM, BN, SB, F8, EPI, NWN, M16>), grid, threads, 0, st, g);
+}
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
@@ -711,21 +732,21 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
         // bf16 on 16x16x32 MFMAs: half the accumulator traffic per flop of the
         // 32x32x16 form, which these power-limited products turn into speed
         // (32760-token products 1-4% faster, same results bit for bit).
-        if (f8) LWO_KL((k_gemm_deep<256, 256, 64, true, EPI, 4>), t256, 512, 0, st, g);
-        else LWO_KL((k_gemm_deep<256, 256, 64, false, EPI, 4, true>), t256, 512, 0, st, g);
+        if (f8) launch_deep<EPI, 256, 256, 64, true, 4>(g, t256, 512, st);
+        else launch_deep<EPI, 256, 256, 64, false, 4, true>(g, t256, 512, st);
     } else if (rows256 && t256x128 >= 192 && t256x128 <= 256) {
-        if (f8) LWO_KL((k_gemm_deep<256, 128, 64, true, EPI>), t256x128, 256, 0, st, g);
-        else LWO_KL((k_gemm_deep<256, 128, 64, false, EPI>), t256x128, 256, 0, st, g);
+        if (f8) launch_deep<EPI, 256, 128, 64, true>(g, t256x128, 256, st);
+        else launch_deep<EPI, 256, 128, 64, false>(g, t256x128, 256, st);
     } else if (t128 > 256) {   // two 64 KB workgroups per CU
-        if (f8) LWO_KL((k_gemm_deep<128, 128, 64, true, EPI>), t128, 256, 0, st, g);
-        else LWO_KL((k_gemm_deep<128, 128, 64, false, EPI>), t128, 256, 0, st, g);
+        if (f8) launch_deep<EPI, 128, 128, 64, true>(g, t128, 256, st);
+        else launch_deep<EPI, 128, 128, 64, false>(g, t128, 256, st);
     } else if (t128 >= 128) {  // one workgroup per CU: 128-byte stages keep more bytes in flight
-        if (f8) LWO_KL((k_gemm_deep<128, 128, 128, true, EPI, 4>), t128, 512, 0, st, g);
-        else LWO_KL((k_gemm_deep<128, 128, 128, false, EPI, 4>), t128, 512, 0, st, g);
+        if (f8) launch_deep<EPI, 128, 128, 128, true, 4>(g, t128, 512, st);
+        else launch_deep<EPI, 128, 128, 128, false, 4>(g, t128, 512, st);
     } else {
         const int t = tiles(128, 64);
-        if (f8) LWO_KL((k_gemm_deep<128, 64, 128, true, EPI>), t, 256, 0, st, g);
-        else LWO_KL((k_gemm_deep<128, 64, 128, false, EPI>), t, 256, 0, st, g);
+        if (f8) launch_deep<EPI, 128, 64, 128, true>(g, t, 256, st);
+        else launch_deep<EPI, 128, 64, 128, false>(g, t, 256, st);
     }
     return hipGetLastError();
 }
