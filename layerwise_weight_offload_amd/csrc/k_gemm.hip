@@ -204,6 +204,7 @@ __device__ __forceinline__ intx4 lds_read16(const unsigned char* p) {
     return v;
 }
 
+
 // The gated epilogue in two forms: EPI_GATED reads one gate row per tile and
 // serves shapes where no tile spans two batches (one batch, or rows per batch
 // a multiple of the tile height); EPI_GATED_ROWS reads the gate row of each
@@ -548,6 +549,21 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // buffer; the values are not used).  Look-ahead: stages 0..3 in flight,
     // stage 0 visible to every wavefront and its first fragments read before
     // the loop.  Plain: stages 0..2 in flight.
+    // The epilogue's per-row and per-column operands (bias, fp8 row and weight
+    // scales) are loaded here, ahead of the first stages, held in registers
+    // through the k loop and put in LDS after it, so the epilogue reads no
+    // global memory but the residual.  Every thread loads (clamped indices), so
+    // no branch disturbs the compiler's wait counts.
+    __shared__ __attribute__((aligned(16))) float ep_as[FP8 ? BM : 1], ep_ws[FP8 ? BN : 1];
+    __shared__ __attribute__((aligned(16))) bf16 ep_bias[BN];
+    const bf16* bsrc = g.bias ? (const bf16*)g.bias : (const bf16*)g.w;   // W: any 8 readable bytes
+    const bf16x4 ep_bv = *(const bf16x4*)(bsrc + min(n0 + 4 * min(tid, BN / 4 - 1), g.N - 4));
+    float ep_asv = 0.0f, ep_wsv = 0.0f;
+    if constexpr (FP8) {
+        ep_asv = g.a_scale[min(m0 + min(tid, BM - 1), g.M - 1)];
+        ep_wsv = g.w_scale[min(n0 + min(tid, BN - 1), g.N - 1) / g.w_seg];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, min(1, nk - 1) * SB);
     issue(std::integral_constant<int, 2>{}, min(2, nk - 1) * SB);
@@ -575,6 +591,11 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
         lds_wait(1, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing re-loads before the workgroup ends
+    if (tid < BN / 4) *(bf16x4*)&ep_bias[4 * tid] = g.bias ? ep_bv : bf16x4{0, 0, 0, 0};
+    if constexpr (FP8) {
+        if (tid < BM) ep_as[tid] = ep_asv;
+        if (tid < BN) ep_ws[tid] = ep_wsv;
+    }
     __syncthreads();                                    // every wavefront is done with the stage buffers
 
     // Lane and wavefront indices derived again after the k loop, through an asm
@@ -606,14 +627,11 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     const bool ncol = nb < g.N;                         // N % 8 == 0: all four columns valid
     const int nbl = ncol ? nb : 0;                      // the column its loads read
     const int mw = m0 + ewm * (BM / 2);                  // first row of this wavefront's block
-    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (g.bias) {
-        const bf16x4 bb = *(const bf16x4*)((const bf16*)g.bias + nbl);
-        bias4 = make_float4((float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]);
-    }
-    if (FP8)
-        ws4 = make_float4(g.w_scale[nbl / g.w_seg], g.w_scale[(nbl + 1) / g.w_seg], g.w_scale[(nbl + 2) / g.w_seg],
-                          g.w_scale[(nbl + 3) / g.w_seg]);
+    const int nl = nb - n0;                             // its first column within the tile (< BN)
+    const bf16x4 bb = *(const bf16x4*)&ep_bias[nl];
+    const float4 bias4 = make_float4((float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]);
+    float4 ws4 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (FP8) ws4 = *(const float4*)&ep_ws[nl];
     float4 xq[2][NP];                                   // residual rows of two slices (residual forms)
     auto load_x = [&](int i, float4 (&dst)[NP]) {
 #pragma unroll
@@ -657,7 +675,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
                     mrow[it] = mw + i * 32 + row;
                     float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
                     if (FP8) {
-                        const float as = g.a_scale[min(mrow[it], g.M - 1)];
+                        const float as = ep_as[mrow[it] - m0];
                         a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
                     }
                     v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
