@@ -81,6 +81,7 @@ def _sample(rng, M, N, n):
     (200, 576, 2304, 1),         # ragged M and N
     (2000, 1088, 576, 2),        # gated, 128x128 tiles with ragged M and N and a stage tail
     (2048, 1152, 128, 3),        # residual, 128x128 tiles with fewer stages than the loads in flight
+    (4096, 5120, 1024, 2),       # gated, 256x256 tiles, two batches split on a tile boundary (one gate row a tile)
 ])
 def test_linear_bf16_sampled(lib, M, N, K, epi):
     torch = _torch()

@@ -35,8 +35,8 @@ from .gpu_util import device_inputs, make_store, oracle_out, row_col_errors, run
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
-def _parity(lwo, name, tol_out, tol_delta, k=0, steps=1):
-    w = lwo_synth.get(name)
+def _parity(lwo, name, tol_out, tol_delta, k=0, steps=1, w=None):
+    w = w or lwo_synth.get(name)
     print(f"[parity] {name} k={k} steps={steps}", flush=True)
     x0, want = oracle_out(w, steps=steps)
     with make_store(lwo, w, k=k) as st:
@@ -61,6 +61,18 @@ def test_dit_xl_full_step(lib):
     """The DiT-XL stack at its full size (28 blocks, hidden 1152, 2 x 1024 tokens), streamed from
     block 0 as the bench runs it, against the float64 oracle over every output element."""
     _parity(lib, "dit_xl_bf16", 2e-2, 3e-2)
+
+
+@pytest.mark.parametrize("base,change,tol_out,tol_delta", [
+    ("dit_t64_bf16", dict(batch=5, tokens=64, n_blocks=2), 2e-2, 3e-2),                      # two batch groups
+    ("dit_t_fp32", dict(hidden=1152, heads=9, ffn=4608, tokens=96, n_blocks=1), 1e-4, 1e-4),  # two windows
+])
+def test_dit_modulation_looping_form(lib, base, change, tol_out, tol_delta):
+    """DiT shapes whose adaLN GEMV runs its looping form: more than four batches (the SiLU values staged
+    in groups of four), and a row longer than sixteen 16-byte loads per lane (fp32 at 1152 wide: two
+    windows).  The DiT-XL, tiny and 200-token shapes take the single-window form."""
+    w = lwo_synth.get(base).with_(**change)
+    _parity(lib, f"{base} {change}", tol_out, tol_delta, w=w)
 
 
 @pytest.mark.parametrize("name,tol_out,tol_delta", [("video14b_bf16", 2e-2, 3e-2), ("video14b_fp8", 5e-2, 5e-2)])
