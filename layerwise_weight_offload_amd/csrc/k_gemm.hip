@@ -554,6 +554,7 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     // through the k loop and put in LDS after it, so the epilogue reads no
     // global memory but the residual.  Every thread loads (clamped indices), so
     // no branch disturbs the compiler's wait counts.
+    static_assert(128 * NWN >= BM && 128 * NWN >= BN, "a thread per epilogue row and column");
     __shared__ __attribute__((aligned(16))) float ep_as[FP8 ? BM : 1], ep_ws[FP8 ? BN : 1];
     __shared__ __attribute__((aligned(16))) bf16 ep_bias[BN];
     const bf16* bsrc = g.bias ? (const bf16*)g.bias : (const bf16*)g.w;   // W: any 8 readable bytes
@@ -642,71 +643,69 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm_deep(GemmArgs g) {
     };
     float4 g1 = make_float4(1.f, 1.f, 1.f, 1.f);     // the tile's gate row (EPI_GATED)
     if constexpr (EPI == EPI_GATED) g1 = *(const float4*)(g.gate + (size_t)(m0 / g.rows_per_batch) * g.gate_ld + nbl);
-    {
-        if constexpr (RES) load_x(0, xq[0]);
+    if constexpr (RES) load_x(0, xq[0]);
 #pragma unroll
-        for (int i = 0; i < TS; ++i) {
-            if constexpr (RES) {
-                if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
-            }
-            if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: elane holds column elane % 16, rows 4 (elane / 16) + r
+    for (int i = 0; i < TS; ++i) {
+        if constexpr (RES) {
+            if (i + 1 < TS) load_x(i + 1, xq[(i + 1) % 2]);
+        }
+        if constexpr (M16) {   // 16x16 blocks 2i, 2i + 1: elane holds column elane % 16, rows 4 (elane / 16) + r
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            lds[(sb * 16 + 4 * (elane / 16) + r) * CW + j * 16 + elane % 16] = acc[2 * i + sb][j][r];
-            } else {
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        lds[(8 * (r / 4) + 4 * ehalf + (r % 4)) * CW + j * 32 + el32] = acc[i][j][r];
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
+                    for (int r = 0; r < 4; ++r)
+                        lds[(sb * 16 + 4 * (elane / 16) + r) * CW + j * 16 + elane % 16] = acc[2 * i + sb][j][r];
+        } else {
 #pragma unroll
-            for (int h = 0; h < NP / PB; ++h) {
-                float4 v[PB];
-                int mrow[PB];
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int it = 0; it < PB; ++it) {
-                    const int row = (h * PB + it) * RPP + rr;
-                    mrow[it] = mw + i * 32 + row;
-                    float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
-                    if (FP8) {
-                        const float as = ep_as[mrow[it] - m0];
-                        a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
-                    }
-                    v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
-                }
-#pragma unroll
-                for (int it = 0; it < PB; ++it) {
-                    if (!ncol || mrow[it] >= g.M) continue;
-                    const float4 y = v[it];
-                    if constexpr (EPI <= EPI_GELU) {
-                        bf16x4 o;
-                        if (EPI == EPI_GELU) {
-                            o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
-                            o[2] = (bf16)gelu_tanh(y.z); o[3] = (bf16)gelu_tanh(y.w);
-                        } else {
-                            o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
-                        }
-                        bf16* dst = g.out_tiled ? (bf16*)((char*)g.out + ktiled_off(mrow[it], (size_t)2 * nb, (size_t)2 * g.ldo))
-                                                : (bf16*)g.out + (size_t)mrow[it] * g.ldo + nb;
-                        *(bf16x4*)dst = o;
-                    } else {
-                        const float4 x = xq[i % 2][h * PB + it];
-                        float4 gg = g1;
-                        if constexpr (EPI == EPI_GATED_ROWS)
-                            gg = *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb);
-                        *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
-                            make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
-                    }
-                }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next slice overwrites
+                for (int r = 0; r < 16; ++r)
+                    lds[(8 * (r / 4) + 4 * ehalf + (r % 4)) * CW + j * 32 + el32] = acc[i][j][r];
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own slice only: no cross-wavefront sync
+#pragma unroll
+        for (int h = 0; h < NP / PB; ++h) {
+            float4 v[PB];
+            int mrow[PB];
+#pragma unroll
+            for (int it = 0; it < PB; ++it) {
+                const int row = (h * PB + it) * RPP + rr;
+                mrow[it] = mw + i * 32 + row;
+                float4 a4 = *(const float4*)&lds[row * CW + 4 * c4];
+                if (FP8) {
+                    const float as = ep_as[mrow[it] - m0];
+                    a4 = make_float4(a4.x * ws4.x * as, a4.y * ws4.y * as, a4.z * ws4.z * as, a4.w * ws4.w * as);
+                }
+                v[it] = make_float4(a4.x + bias4.x, a4.y + bias4.y, a4.z + bias4.z, a4.w + bias4.w);
+            }
+#pragma unroll
+            for (int it = 0; it < PB; ++it) {
+                if (!ncol || mrow[it] >= g.M) continue;
+                const float4 y = v[it];
+                if constexpr (EPI <= EPI_GELU) {
+                    bf16x4 o;
+                    if (EPI == EPI_GELU) {
+                        o[0] = (bf16)gelu_tanh(y.x); o[1] = (bf16)gelu_tanh(y.y);
+                        o[2] = (bf16)gelu_tanh(y.z); o[3] = (bf16)gelu_tanh(y.w);
+                    } else {
+                        o[0] = (bf16)y.x; o[1] = (bf16)y.y; o[2] = (bf16)y.z; o[3] = (bf16)y.w;
+                    }
+                    bf16* dst = g.out_tiled ? (bf16*)((char*)g.out + ktiled_off(mrow[it], (size_t)2 * nb, (size_t)2 * g.ldo))
+                                            : (bf16*)g.out + (size_t)mrow[it] * g.ldo + nb;
+                    *(bf16x4*)dst = o;
+                } else {
+                    const float4 x = xq[i % 2][h * PB + it];
+                    float4 gg = g1;
+                    if constexpr (EPI == EPI_GATED_ROWS)
+                        gg = *(const float4*)(g.gate + (size_t)(mrow[it] / g.rows_per_batch) * g.gate_ld + nb);
+                    *(float4*)(g.xr + (size_t)mrow[it] * g.ldx + nb) =
+                        make_float4(x.x + gg.x * y.x, x.y + gg.y * y.y, x.z + gg.z * y.z, x.w + gg.w * y.w);
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next slice overwrites
     }
 }
 
