@@ -215,7 +215,9 @@ def test_attention_ktiled_output(lib, B, H, Tq, Tk, d, fused):
 
 # ------------------------------------------------------------------ row kernels
 
-@pytest.mark.parametrize("M,D", [(32760, 5120), (2048, 1152), (333, 256)])
+@pytest.mark.parametrize("M,D", [(32760, 5120), (2048, 1152), (333, 256),
+                                 (203, 2048),    # the widest rows of one wavefront each, a 4-row workgroup short of rows
+                                 (131, 2112)])   # the narrowest of two wavefronts per row (five float4 chunks a lane)
 def test_layernorm_ktiled(lib, M, D):
     torch = _torch()
     print(f"[ktiled layernorm] M={M} D={D}", flush=True)

@@ -279,7 +279,9 @@ def test_attention_f32(lib, B, H, Tq, Tk, d):
 
 # ------------------------------------------------------------------ row kernels
 
-@pytest.mark.parametrize("M,D", [(32760, 5120), (2048, 1152), (333, 256)])
+@pytest.mark.parametrize("M,D", [(32760, 5120), (2048, 1152), (333, 256),
+                                 (203, 2048),    # the widest rows of one wavefront each, a 4-row workgroup short of rows
+                                 (131, 2112)])   # the narrowest of two wavefronts per row (five float4 chunks a lane)
 def test_layernorm_modulated_and_fp8(lib, M, D):
     torch = _torch()
     print(f"[layernorm] M={M} D={D}", flush=True)
